@@ -1,0 +1,186 @@
+"""KIVI-style asymmetric quantisation of the KV cache, and its stored layout.
+
+The pages name KIVI as one of the lossy compressors that VeriCache turns into
+a drafter (VeriCache summary, "Architecture support": one compressor
+interface over token dropping and quantisation) but give no formulas. The
+scheme written out here is the plain min/max one:
+
+* keys are quantised per channel over groups of 32 consecutive tokens,
+  values per token over groups of 32 consecutive channels;
+* for each group: mn, mx = min, max; scale = fp16(round-nearest-even of
+  (mx - mn) / (2**b - 1)); zero = fp16(mn); code = clamp(rint((x - zero) /
+  scale), 0, 2**b - 1) computed in fp64 with the fp16-rounded scale and
+  zero (code 0 when scale == 0); dequantised value = code * scale + zero;
+* b is 2 or 4.
+
+The layout functions at the bottom define how codes and per-group
+parameters are stored for the GPU. They are pure index arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+
+
+def fp16_round(x) -> np.ndarray:
+    """Round fp64 to the nearest fp16 (ties to even), returned as fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _quantize_groups(x, bits: int, axis: int):
+    """Quantise along ``axis`` (the group axis). Returns codes, scale, zero
+    (scale and zero keep the reduced axis with length 1)."""
+    qmax = float((1 << bits) - 1)
+    x = np.asarray(x, dtype=np.float64)
+    mn = x.min(axis=axis, keepdims=True)
+    mx = x.max(axis=axis, keepdims=True)
+    scale = fp16_round((mx - mn) / qmax)
+    zero = fp16_round(mn)
+    safe = np.where(scale == 0.0, 1.0, scale)
+    codes = np.clip(np.rint((x - zero) / safe), 0.0, qmax)
+    codes = np.where(scale == 0.0, 0.0, codes)
+    return codes.astype(np.int64), scale, zero
+
+
+def quantize_keys(K, bits: int):
+    """K: [T][D] with T a multiple of 32. Per-channel groups of 32 tokens.
+
+    Returns codes int [T][D], scale [T/32][D], zero [T/32][D] (fp16 values).
+    """
+    K = np.asarray(K, dtype=np.float64)
+    T, D = K.shape
+    if T % GROUP:
+        raise ValueError("key token count must be a multiple of 32")
+    g = K.reshape(T // GROUP, GROUP, D)
+    codes, scale, zero = _quantize_groups(g, bits, axis=1)
+    return codes.reshape(T, D), scale[:, 0, :], zero[:, 0, :]
+
+
+def quantize_values(V, bits: int):
+    """V: [T][D] with D a multiple of 32. Per-token groups of 32 channels.
+
+    Returns codes int [T][D], scale [T][D/32], zero [T][D/32].
+    """
+    V = np.asarray(V, dtype=np.float64)
+    T, D = V.shape
+    g = V.reshape(T, D // GROUP, GROUP)
+    codes, scale, zero = _quantize_groups(g, bits, axis=2)
+    return codes.reshape(T, D), scale[:, :, 0], zero[:, :, 0]
+
+
+def dequantize_keys(codes, scale, zero) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.float64)
+    rep = np.repeat(np.asarray(scale), GROUP, axis=0)
+    zrep = np.repeat(np.asarray(zero), GROUP, axis=0)
+    return codes * rep + zrep
+
+
+def dequantize_values(codes, scale, zero) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.float64)
+    rep = np.repeat(np.asarray(scale), GROUP, axis=1)
+    zrep = np.repeat(np.asarray(zero), GROUP, axis=1)
+    return codes * rep + zrep
+
+
+# ----------------------------------------------------------------------------
+# Stored layout (the format the GPU library reads; declared in include/vc.h)
+# ----------------------------------------------------------------------------
+#
+# Key codes, per (sequence, KV head): uint32 [T][D*b/32], token-major; channel
+# d of a token sits in word floor(d*b/32) at bit (d*b) mod 32 (LSB first).
+# Key scale / zero: fp16 [T/32][D].
+#
+# Value codes, per (sequence, KV head): uint32 [T/32][64][D*b/64]. Each
+# 32-token block is split over 64 "lanes" L = 16*q + c (q in 0..3,
+# c in 0..15). Lane L holds, for every channel 16*m + c (m in 0..D/16-1),
+# the codes of the 8 tokens tau(q, s) = 16*(s // 4) + 4*q + (s % 4),
+# s in 0..7, of the block. Inside the lane's words, the code of
+# (m, s) sits in word (m*b) // 4 at bit 16*(s % 2) + b*f with
+# f = s // 2 + 4*(m % (4 // b)).
+# Value scale / zero: fp16 [T/32][D/32][32]; entry 8*q + s of group j is the
+# parameter of token tau(q, s) of the block, channel group j.
+
+
+def value_slot_token(q: int, s: int) -> int:
+    """Token (within a 32-token block) stored in value slot s of lane group q."""
+    return 16 * (s // 4) + 4 * q + (s % 4)
+
+
+def pack_key_codes(codes, bits: int) -> np.ndarray:
+    """codes int [T][D] -> uint32 [T][D*bits/32]."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    T, D = codes.shape
+    per = 32 // bits
+    c = codes.reshape(T, D // per, per)
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))[None, None, :]
+    return np.bitwise_or.reduce(c << shifts, axis=2).astype(np.uint32)
+
+
+def unpack_key_codes(words, bits: int, D: int) -> np.ndarray:
+    w = np.asarray(words, dtype=np.uint64)
+    per = 32 // bits
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))[None, None, :]
+    c = (w[:, :, None] >> shifts) & np.uint64((1 << bits) - 1)
+    return c.reshape(w.shape[0], D).astype(np.int64)
+
+
+def _value_positions(bits: int, D: int):
+    """For every (token-in-block t, channel d): (lane, word, bit)."""
+    lane = np.zeros((GROUP, D), dtype=np.int64)
+    word = np.zeros((GROUP, D), dtype=np.int64)
+    bit = np.zeros((GROUP, D), dtype=np.int64)
+    for q in range(4):
+        for s in range(8):
+            t = value_slot_token(q, s)
+            for d in range(D):
+                m, c = d // 16, d % 16
+                f = s // 2 + 4 * (m % (4 // bits))
+                lane[t, d] = 16 * q + c
+                word[t, d] = (m * bits) // 4
+                bit[t, d] = 16 * (s % 2) + bits * f
+    return lane, word, bit
+
+
+def pack_value_codes(codes, bits: int) -> np.ndarray:
+    """codes int [T][D] (T multiple of 32) -> uint32 [T/32][64][D*bits/64]."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    T, D = codes.shape
+    nw = D * bits // 64
+    lane, word, bit = _value_positions(bits, D)
+    out = np.zeros((T // GROUP, 64, nw), dtype=np.uint64)
+    blocks = codes.reshape(T // GROUP, GROUP, D)
+    for t in range(GROUP):
+        for d in range(D):
+            out[:, lane[t, d], word[t, d]] |= blocks[:, t, d] << np.uint64(bit[t, d])
+    return out.astype(np.uint32)
+
+
+def unpack_value_codes(words, bits: int, D: int) -> np.ndarray:
+    w = np.asarray(words, dtype=np.uint64)
+    nb = w.shape[0]
+    lane, word, bit = _value_positions(bits, D)
+    out = np.zeros((nb, GROUP, D), dtype=np.int64)
+    mask = np.uint64((1 << bits) - 1)
+    for t in range(GROUP):
+        for d in range(D):
+            out[:, t, d] = ((w[:, lane[t, d], word[t, d]] >> np.uint64(bit[t, d])) & mask).astype(np.int64)
+    return out.reshape(nb * GROUP, D)
+
+
+def pack_value_side(param) -> np.ndarray:
+    """Per-token value scale or zero [T][D/32] -> [T/32][D/32][32] (slot order)."""
+    p = np.asarray(param)
+    T, G = p.shape
+    blocks = p.reshape(T // GROUP, GROUP, G)
+    order = [value_slot_token(e // 8, e % 8) for e in range(GROUP)]
+    return np.ascontiguousarray(blocks[:, order, :].transpose(0, 2, 1))
+
+
+def unpack_value_side(packed) -> np.ndarray:
+    p = np.asarray(packed)
+    nb, G, _ = p.shape
+    out = np.empty((nb, GROUP, G), dtype=p.dtype)
+    for e in range(GROUP):
+        out[:, value_slot_token(e // 8, e % 8), :] = p[:, :, e]
+    return out.reshape(nb * GROUP, G)

@@ -1,0 +1,130 @@
+"""Pins for the KIVI-style quantiser, its stored layout, and the token dropper."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (dequantize_keys, dequantize_values, fp16_round, pack_key_codes,
+                    pack_value_codes, pack_value_side, quantize_keys, quantize_values,
+                    select_kept, unpack_key_codes, unpack_value_codes, unpack_value_side)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_fp16_round_ties_and_range():
+    assert fp16_round(1 + 2 ** -11) == 1.0                     # halfway -> even
+    assert fp16_round(1 + 2 ** -11 + 2 ** -30) == 1 + 2 ** -10  # just above halfway
+    assert fp16_round(1 + 3 * 2 ** -11) == 1 + 2 ** -9          # halfway -> even (up)
+    assert fp16_round(2 ** -25) == 0.0                          # below half the smallest subnormal
+    assert fp16_round(3 * 2 ** -26) == 2 ** -24                 # above it
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_codes_nearest_level_brute_force(bits):
+    """Each code is the level c*scale + zero nearest to x (ties: even c),
+    clamped to [0, 2^b-1]: checked by enumerating every level."""
+    rng = np.random.default_rng(bits)
+    K = rng.standard_normal((64, 8)) * 2
+    codes, scale, zero = quantize_keys(K, bits)
+    qmax = (1 << bits) - 1
+    for t in range(64):
+        for d in range(8):
+            s, z = scale[t // 32, d], zero[t // 32, d]
+            u = (K[t, d] - z) / s
+            dist = [abs(u - c) for c in range(qmax + 1)]
+            best = min(range(qmax + 1), key=lambda c: (dist[c], c % 2))
+            assert codes[t, d] == best
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group_extremes_and_error_bound(bits):
+    rng = np.random.default_rng(10 + bits)
+    V = rng.standard_normal((96, 64)) * 3
+    codes, scale, zero = quantize_values(V, bits)
+    qmax = (1 << bits) - 1
+    assert codes.min() >= 0 and codes.max() <= qmax
+    g = V.reshape(96, 2, 32)
+    c = codes.reshape(96, 2, 32)
+    assert (c[np.arange(96)[:, None], np.arange(2)[None], g.argmin(axis=2)] == 0).all()
+    assert (c[np.arange(96)[:, None], np.arange(2)[None], g.argmax(axis=2)] == qmax).all()
+    xh = dequantize_values(codes, scale, zero)
+    mn, mx = g.min(axis=2), g.max(axis=2)
+    s_exact = (mx - mn) / qmax
+    slack = np.abs(zero - mn) + qmax * np.abs(scale - s_exact)
+    bound = np.repeat(scale / 2 + slack, 32, axis=1) + 1e-12
+    assert (np.abs(V - xh) <= bound).all()
+
+
+def test_key_grouping_is_per_channel_over_32_tokens():
+    K = np.zeros((64, 4))
+    K[:32, 1] = np.linspace(0, 3, 32)      # channel 1, first group: range 3
+    K[32:, 1] = 100.0                      # second group constant
+    codes, scale, zero = quantize_keys(K, 2)
+    assert scale.shape == (2, 4) and scale[0, 1] == 1.0 and zero[0, 1] == 0.0
+    assert scale[1, 1] == 0.0 and (codes[32:, 1] == 0).all()
+    np.testing.assert_array_equal(dequantize_keys(codes, scale, zero)[32:, 1], 100.0)
+
+
+def test_constant_group_is_exact():
+    V = np.full((32, 32), -1.5)
+    codes, scale, zero = quantize_values(V, 4)
+    assert (codes == 0).all() and (scale == 0).all()
+    np.testing.assert_array_equal(dequantize_values(codes, scale, zero), V)
+
+
+@pytest.mark.parametrize("bits,D", [(2, 64), (2, 128), (4, 64), (4, 128)])
+def test_layout_roundtrip(bits, D):
+    rng = np.random.default_rng(bits * D)
+    c = rng.integers(0, 1 << bits, size=(96, D))
+    assert np.array_equal(unpack_key_codes(pack_key_codes(c, bits), bits, D), c)
+    assert np.array_equal(unpack_value_codes(pack_value_codes(c, bits), bits, D), c)
+    p = rng.standard_normal((96, D // 32))
+    assert np.array_equal(unpack_value_side(pack_value_side(p)), p)
+
+
+def test_layout_golden_positions():
+    """Hand-worked positions of single codes (tests/golden/kivi_layout.json)."""
+    with open(os.path.join(GOLDEN, "kivi_layout.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        bits, D, t, d = case["bits"], case["D"], case["token"], case["channel"]
+        codes = np.zeros((32, D), dtype=np.int64)
+        codes[t, d] = (1 << bits) - 1
+        kw = pack_key_codes(codes, bits)
+        nz = np.argwhere(kw)
+        assert nz.tolist() == [[t, case["key_word"]]]
+        assert int(kw[t, case["key_word"]]) == ((1 << bits) - 1) << case["key_bit"]
+        vw = pack_value_codes(codes, bits)
+        nz = np.argwhere(vw)
+        assert nz.tolist() == [[0, case["value_lane"], case["value_word"]]]
+        assert int(vw[0, case["value_lane"], case["value_word"]]) == ((1 << bits) - 1) << case["value_bit"]
+
+
+def _kept_by_rank(scores, n_keep):
+    """Independent definition: token i is kept iff fewer than n_keep tokens
+    beat it (higher score, or equal score and lower index)."""
+    T = len(scores)
+    kept = []
+    for i in range(T):
+        beats = sum(1 for j in range(T) if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+        if beats < n_keep:
+            kept.append(i)
+    return kept
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_dropper_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 40))
+    s = rng.integers(0, 6, size=T).astype(np.float32)   # many ties
+    rho = float(rng.choice([0.1, 0.25, 0.5, 0.9]))
+    n_keep = int(np.ceil(rho * T))
+    kept = select_kept(s, rho)
+    assert kept.tolist() == _kept_by_rank(s.tolist(), n_keep)
+    assert len(kept) == n_keep and (np.diff(kept) > 0).all()
+
+
+def test_dropper_keep_all_is_identity():
+    s = np.random.default_rng(0).random(77).astype(np.float32)
+    assert select_kept(s, 1.0).tolist() == list(range(77))

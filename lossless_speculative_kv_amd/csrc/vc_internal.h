@@ -1,0 +1,116 @@
+// Internal helpers shared by the gfx950 kernels of libvc (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vc.h"
+
+namespace vc {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------- MFMA ----
+// v_mfma_f32_16x16x32_{f16,bf16}. Lane l holds A row (l % 16) and B column
+// (l % 16), each with 8 contraction slots selected by l / 16 (the same slot
+// mapping for A and B); the result lane l holds column l % 16, rows
+// 4 * (l / 16) + r, r = 0..3.
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) return mfma_bf16(a, b, c);
+  else return mfma_f16(a, b, c);
+}
+
+// ------------------------------------------------------- conversions ----
+// Round-to-nearest-even packs (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v;
+  v.x = (_Float16)lo;
+  v.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (BF16) return pack_bf16(lo, hi);
+  else return pack_f16(lo, hi);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
+}
+// fp32 -> bf16 bits, nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------ cross-lane ops ----
+// DPP quad permutations: xor 1 ([1,0,3,2]) and xor 2 ([2,3,0,1]).
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+// Sum / max over the four lanes {l, l^16, l^32, l^48}; every lane gets the
+// bitwise-identical result (the swap pairs operands in lane-independent order).
+__device__ __forceinline__ float sum_q(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_q(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// Sum over the NG adjacent lanes of a column group (NG in {1, 2, 4}).
+template <int NG>
+__device__ __forceinline__ float sum_group(float x) {
+  if constexpr (NG >= 2) x = x + dpp_xor1(x);
+  if constexpr (NG >= 4) x = x + dpp_xor2(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ loads ----
+template <typename T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+// ---------------------------------------------------- host-side errors ----
+void set_error(const char* fmt, ...);
+vc_status fail(vc_status code, const char* fmt, ...);
+vc_status check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace vc

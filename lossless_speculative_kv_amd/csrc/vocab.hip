@@ -1,0 +1,360 @@
+// Vocabulary projection with a fused greedy argmax (VeriCache summary, "Core
+// algorithm" and "Experimental results": drafting and verification both pick
+// tokens greedily; "P1": drafting also streams the model weights from HBM).
+//
+// logits[m][n] = sum_k bf16(h[m][k]) * W[n][k], fp32 accumulation on
+// v_mfma_f32_16x16x32_bf16 with A = 16 vocabulary rows of W and B = 16 hidden
+// rows. Contraction slots are permuted so that each lane reads 64 contiguous
+// bytes of a W row per 128-wide k step: lane group qg takes k = k0 + 32*qg
+// + 8*kk + s in K-step kk (the B operand uses the same permutation).
+//
+// Two kernels share the epilogue:
+//  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
+//    rows; W goes straight from HBM to registers, h (bf16, tiny) from L2.
+//  * vocab_staged: any M. Each wave owns 32 vocab rows and all M rows; the
+//    hidden chunk [M][64] is staged in LDS (double-buffered) and shared by
+//    the 8 waves of the workgroup, so W is read from HBM exactly once.
+// Argmax: each workgroup reduces (logit, index) to one 64-bit key per row,
+// key = ordered(logit) << 32 | ~index, whose maximum is the largest logit with
+// the lowest index (-0 is folded to +0); a second kernel takes the max over
+// workgroups. The result does not depend on scheduling.
+#include "vc_internal.h"
+
+namespace vc {
+
+namespace {
+
+struct VocabParams {
+  const float* h;     // fp32 [M][K]
+  uint16_t* hb;       // bf16 [Mp][K] (workspace)
+  const uint16_t* w;  // bf16 [V][K]
+  uint64_t* keys;     // [nwg][M] (workspace)
+  int32_t* argmax;    // [M]
+  float* max_logit;   // [M] or null
+  float* logits;      // [M][V] or null
+  int M, Mp, K, V, nwg;
+};
+
+__device__ __forceinline__ uint64_t make_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0) u = 0;  // -0 -> +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)(~(uint32_t)k); }
+
+__device__ __forceinline__ uint64_t max_q_u64(uint64_t x) {
+  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  uint64_t k0 = ((uint64_t)b[0] << 32) | a[0], k1 = ((uint64_t)b[1] << 32) | a[1];
+  x = k0 > k1 ? k0 : k1;
+  lo = (uint32_t)x;
+  hi = (uint32_t)(x >> 32);
+  a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  k0 = ((uint64_t)b[0] << 32) | a[0];
+  k1 = ((uint64_t)b[1] << 32) | a[1];
+  return k0 > k1 ? k0 : k1;
+}
+
+// h fp32 -> bf16 (nearest even), rows M..Mp-1 zero.
+__global__ __launch_bounds__(256) void hidden_to_bf16_kernel(const VocabParams P) {
+  const size_t n = (size_t)P.Mp * P.K;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t m = i / P.K;
+    P.hb[i] = (m < (size_t)P.M) ? (uint16_t)f32_to_bf16_bits(P.h[i]) : (uint16_t)0;
+  }
+}
+
+// Reduce the per-wave candidates (vocab tile a, m-tile mt) into keys per row
+// and write the optional logits. acc[a][mt][r]: logit of vocab row
+// vbase + 16*a + 4*qg + r and hidden row 16*mt_row + n.
+template <int NA, int NMT>
+__device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc)[NA][NMT], int vbase,
+                                         const int (&mrow)[NMT], int lane, uint64_t (&best)[NMT]) {
+  const int n = lane & 15, qg = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int m = mrow[mt] + n;
+    uint64_t bk = 0;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = vbase + 16 * a + 4 * qg + r;
+        if (v < P.V) {
+          const uint64_t k = make_key(acc[a][mt][r], v);
+          bk = k > bk ? k : bk;
+        }
+      }
+    best[mt] = max_q_u64(bk);
+    if (P.logits != nullptr && m < P.M) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const int v0 = vbase + 16 * a + 4 * qg;
+        float* dst = P.logits + (size_t)m * P.V + v0;
+        if (v0 + 3 < P.V && (P.V & 3) == 0) {
+          *reinterpret_cast<f32x4*>(dst) = acc[a][mt];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (v0 + r < P.V) dst[r] = acc[a][mt][r];
+        }
+      }
+    }
+  }
+}
+
+template <int MS>
+__global__ __launch_bounds__(256) void vocab_stream_kernel(const VocabParams P) {
+  constexpr int NA = 4;  // vocab tiles per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, qg = lane >> 4;
+  const int vbase = (blockIdx.x * 4 + wave) * 64;
+  f32x4 acc[NA][MS];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < MS; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wrow[NA];
+  bool wok[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int v = vbase + 16 * a + n;
+    wok[a] = v < P.V;
+    wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K + 32 * qg;
+  }
+  const uint16_t* hrow[MS];
+#pragma unroll
+  for (int t = 0; t < MS; ++t) hrow[t] = P.hb + (size_t)(16 * t + n) * P.K + 32 * qg;
+
+  for (int k0 = 0; k0 < P.K; k0 += 128) {
+    u32x4 A[NA][4];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      u32x4 B[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) B[kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 8 * kk);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B[kk], acc[a][t]);
+    }
+  }
+  int mrow[MS];
+#pragma unroll
+  for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
+  uint64_t best[MS];
+  epilogue<NA, MS>(P, acc, vbase, mrow, lane, best);
+  __shared__ uint64_t red[4][16 * MS];
+#pragma unroll
+  for (int t = 0; t < MS; ++t)
+    if (qg == 0) red[wave][16 * t + n] = best[t];
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 256) {
+    uint64_t k = red[0][m];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) k = red[w][m] > k ? red[w][m] : k;
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+  }
+}
+
+// Staged kernel: 8 waves x 32 vocab rows; all m-tiles (NMT >= ceil(M/16)).
+constexpr int kStagedWaves = 8;
+constexpr int kKC = 64;  // k per LDS stage
+
+template <int NMT>
+__global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) {
+  constexpr int NA = 2, HSTR = kKC + 8;  // halfs per staged hidden row (16-byte aligned, skewed)
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  uint16_t* hs = reinterpret_cast<uint16_t*>(smem_raw);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, qg = lane >> 4;
+  const int mtiles = P.Mp / 16;
+  const int vbase = (blockIdx.x * kStagedWaves + wave) * 32;
+  f32x4 acc[NA][NMT];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wrow[NA];
+  bool wok[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int v = vbase + 16 * a + n;
+    wok[a] = v < P.V;
+    wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K;
+  }
+  const int stage_halfs = P.Mp * HSTR;
+  // cooperative copy of hidden chunk [Mp][kKC] into LDS buffer `buf`
+  auto stage = [&](int k0, int buf) {
+    uint16_t* dst = hs + buf * stage_halfs;
+    const int chunks = P.Mp * (kKC / 8);
+    for (int c = threadIdx.x; c < chunks; c += 64 * kStagedWaves) {
+      const int m = c / (kKC / 8), x = c % (kKC / 8);
+      *reinterpret_cast<u32x4*>(dst + m * HSTR + 8 * x) =
+          *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x);
+    }
+  };
+  stage(0, 0);
+  __syncthreads();
+  const int nk = P.K / kKC;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int k0 = kc * kKC;
+    // W for this chunk: 2 K-steps; lane group qg reads k0 + 16*qg + 8*kk (32 contiguous bytes)
+    u32x4 A[NA][2];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 16 * qg + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+    if (kc + 1 < nk) stage(k0 + kKC, (kc + 1) & 1);
+    const uint16_t* cur = hs + (kc & 1) * stage_halfs;
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) {
+      if (t < mtiles) {
+        const uint16_t* hr = cur + (16 * t + n) * HSTR + 16 * qg;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 B = *reinterpret_cast<const u32x4*>(hr + 8 * kk);
+#pragma unroll
+          for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B, acc[a][t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  int mrow[NMT];
+#pragma unroll
+  for (int t = 0; t < NMT; ++t) mrow[t] = 16 * t;
+  uint64_t best[NMT];
+  epilogue<NA, NMT>(P, acc, vbase, mrow, lane, best);
+  // cross-wave reduction through LDS (reuses the staging area)
+  uint64_t* red = reinterpret_cast<uint64_t*>(smem_raw);
+#pragma unroll
+  for (int t = 0; t < NMT; ++t)
+    if (qg == 0 && t < mtiles) red[wave * P.Mp + 16 * t + n] = best[t];
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 64 * kStagedWaves) {
+    uint64_t k = red[m];
+    for (int w = 1; w < kStagedWaves; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+  }
+}
+
+__global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
+  const int m = blockIdx.x;
+  uint64_t k = 0;
+  for (int i = threadIdx.x; i < P.nwg; i += 256) {
+    const uint64_t x = P.keys[(size_t)i * P.M + m];
+    k = x > k ? x : k;
+  }
+  __shared__ uint64_t red[256];
+  red[threadIdx.x] = k;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x + s] > red[threadIdx.x] ? red[threadIdx.x + s] : red[threadIdx.x];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    P.argmax[m] = key_index(red[0]);
+    if (P.max_logit) P.max_logit[m] = key_value(red[0]);
+  }
+}
+
+template <int NMT>
+void launch_staged(const VocabParams& P, hipStream_t s) {
+  const size_t lds = (size_t)2 * P.Mp * (kKC + 8) * 2;
+  const size_t red = (size_t)kStagedWaves * P.Mp * 8;
+  const size_t bytes = lds > red ? lds : red;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&vocab_staged_kernel<NMT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  hipLaunchKernelGGL((vocab_staged_kernel<NMT>), dim3(P.nwg), dim3(64 * kStagedWaves), bytes, s, P);
+}
+
+}  // namespace
+
+struct VocabPlan {
+  bool stream;
+  int ms;  // stream: m-tiles
+  int nmt; // staged: m-tiles template bound
+  int nwg;
+  int Mp;
+};
+
+VocabPlan vocab_plan(int M, int K, int V) {
+  (void)K;
+  VocabPlan p{};
+  p.Mp = (M + 15) / 16 * 16;
+  const int mt = p.Mp / 16;
+  if (mt <= 2) {
+    p.stream = true;
+    p.ms = mt;
+    p.nwg = (V + 255) / 256;
+  } else {
+    p.stream = false;
+    p.nmt = mt <= 4 ? 4 : mt <= 8 ? 8 : mt <= 12 ? 12 : mt <= 18 ? 18 : mt <= 24 ? 24 : 28;
+    p.nwg = (V + 32 * kStagedWaves - 1) / (32 * kStagedWaves);
+  }
+  return p;
+}
+
+int vocab_max_rows() { return 28 * 16; }
+
+size_t vocab_ws_bytes(int M, int K, int V) {
+  const VocabPlan p = vocab_plan(M, K, V);
+  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256);
+}
+
+vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32_t* argmax, float* max_logit,
+                       float* logits, void* ws, hipStream_t stream) {
+  const VocabPlan plan = vocab_plan(M, K, V);
+  VocabParams P{};
+  P.h = h;
+  P.hb = static_cast<uint16_t*>(ws);
+  P.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256));
+  P.w = static_cast<const uint16_t*>(w);
+  P.argmax = argmax;
+  P.max_logit = max_logit;
+  P.logits = logits;
+  P.M = M;
+  P.Mp = plan.Mp;
+  P.K = K;
+  P.V = V;
+  P.nwg = plan.nwg;
+  {
+    const size_t n = (size_t)plan.Mp * K;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, P);
+  }
+  if (plan.stream) {
+    if (plan.ms == 1) hipLaunchKernelGGL((vocab_stream_kernel<1>), dim3(plan.nwg), dim3(256), 0, stream, P);
+    else hipLaunchKernelGGL((vocab_stream_kernel<2>), dim3(plan.nwg), dim3(256), 0, stream, P);
+  } else {
+    switch (plan.nmt) {
+      case 4: launch_staged<4>(P, stream); break;
+      case 8: launch_staged<8>(P, stream); break;
+      case 12: launch_staged<12>(P, stream); break;
+      case 18: launch_staged<18>(P, stream); break;
+      case 24: launch_staged<24>(P, stream); break;
+      default: launch_staged<28>(P, stream); break;
+    }
+  }
+  vc_status st = check_launch("vocab projection");
+  if (st != VC_OK) return st;
+  hipLaunchKernelGGL(vocab_reduce_kernel, dim3(M), dim3(256), 0, stream, P);
+  return check_launch("vocab argmax reduce");
+}
+
+}  // namespace vc

@@ -1,0 +1,309 @@
+"""Round driver: device buffers from PyTorch, every step in libvc kernels.
+
+One VeriCache round (VeriCache summary, "Core algorithm"), all launches on
+the current stream with no host synchronisation:
+
+  for j in 0..k-1:   embed(x_j) -> q, append k/v to the draft tail
+                     vc_draft_decode_attn   (compressed cache)
+                     vc_vocab_logits(M=B)   -> x_{j+1}
+  embed(x_0..x_k)    -> verify queries and block keys/values
+  vc_verify_attn     (full cache; staged from pinned host memory in chunks on
+                      a side stream when the cache lives on the host)
+  vc_vocab_logits(M=(k+1)B) -> y_1..y_{k+1}
+  vc_greedy_accept   -> m, next token (written into row 0 of the token array)
+  vc_commit_round    -> full cache grows by m+1 rows; tail / body updated
+
+The synthetic model below attention (embedding of a token, vocab matrix) is
+drawn by the device copy of the seeded generator in synth/.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+import synth
+import synth.dev as sdev
+
+from . import _lib as L
+from .configs import RoundConfig
+
+KIND = {"dense": L.VC_DRAFT_DENSE, "kivi": L.VC_DRAFT_KIVI, "tokdrop": L.VC_DRAFT_TOKDROP}
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _round32(x: int) -> int:
+    return (x + 31) // 32 * 32
+
+
+class Engine:
+    """Owns the caches and round buffers of one batch of sequences."""
+
+    def __init__(self, cfg: RoundConfig, rounds_cap: int = 4, device: str = "cuda"):
+        self.cfg = c = cfg
+        self.dev = torch.device(device)
+        self.stream = torch.cuda.current_stream(self.dev)
+        sh = self.shape = L.vc_attn_shape(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim)
+        B, Hq, Hkv, D, k = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.k
+        self.rounds_cap = rounds_cap
+        self.round_idx = 0
+        s = self.stream.cuda_stream
+        bf = torch.bfloat16
+
+        # synthetic model
+        km = synth.outlier_multiplier(c.seed, Hkv, D, c.outliers)
+        self.key_mult = torch.from_numpy(km).to(self.dev) if c.outliers else None
+        self.W = torch.empty((c.vocab, c.hidden), dtype=bf, device=self.dev)
+        sdev.fill_w(c.seed, c.vocab, c.hidden, self.W.data_ptr(), s)
+
+        # full cache (context + room for committed rows)
+        self.full_cap = _round32(c.context + rounds_cap * (k + 1))
+        self.ctx_len = torch.full((B,), c.context, dtype=torch.int32, device=self.dev)
+        if c.staged:
+            self._init_staged()
+        else:
+            self.full_k = torch.empty((B, Hkv, self.full_cap, D), dtype=bf, device=self.dev)
+            self.full_v = torch.empty_like(self.full_k)
+            self._fill_context(self.full_k, self.full_v, self.full_cap)
+
+        # draft cache
+        self.tail_cap = _round32(max(c.residual, 0) + rounds_cap * (k + 1) + 32)
+        self.body_len = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.tail_len = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.kv = L.vc_draft_kv()
+        self.kv.kind = KIND[c.kind]
+        self.kv.tail_cap = self.tail_cap
+        self.kv.body_len = self.body_len.data_ptr()
+        self.kv.tail_len = self.tail_len.data_ptr()
+        tail_dtype = torch.float16 if c.kind == "kivi" else bf
+        self.tail_k = torch.zeros((B, Hkv, self.tail_cap, D), dtype=tail_dtype, device=self.dev)
+        self.tail_v = torch.zeros_like(self.tail_k)
+        self.kv.tail_k = self.tail_k.data_ptr()
+        self.kv.tail_v = self.tail_v.data_ptr()
+        self.dc = L.vc_draft_cache()
+        self.dc.kind = self.kv.kind
+        self.dc.tail_cap = self.tail_cap
+        self.dc.body_len = self.kv.body_len
+        self.dc.tail_len = self.kv.tail_len
+        self.dc.tail_k = self.kv.tail_k
+        self.dc.tail_v = self.kv.tail_v
+        self.dc.residual = c.residual
+        if c.kind == "kivi":
+            self._init_kivi()
+        elif c.kind == "tokdrop":
+            self._init_tokdrop()
+        else:
+            if c.staged:
+                raise ValueError("the dense draft cache needs the full cache on the device")
+            self.kv.body_cap = self.dc.body_cap = self.full_cap
+            self.kv.src_k, self.kv.src_v = self.full_k.data_ptr(), self.full_v.data_ptr()
+            self.kv.src_t_cap = self.full_cap
+            self.body_len.fill_(c.context)
+
+        # round buffers (position-major [k+1][B])
+        self.xs = torch.zeros((k + 1, B), dtype=torch.int32, device=self.dev)
+        self.xs[0] = torch.from_numpy(synth.start_tokens(c.seed, B, c.vocab).astype(np.int32)).to(self.dev)
+        self.y = torch.zeros((k + 1, B), dtype=torch.int32, device=self.dev)
+        self.n_accept = torch.zeros((rounds_cap, B), dtype=torch.int32, device=self.dev)
+        self.committed = torch.full((rounds_cap, k + 1, B), -1, dtype=torch.int32, device=self.dev)
+        self.status = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.q_draft = torch.empty((B, Hq, D), dtype=bf, device=self.dev)
+        self.o_draft = torch.empty((B, Hq, D), dtype=torch.float32, device=self.dev)
+        self.qv = torch.empty((k + 1, B, Hq, D), dtype=bf, device=self.dev)
+        self.kn = torch.empty((k + 1, B, Hkv, D), dtype=bf, device=self.dev)
+        self.vn = torch.empty_like(self.kn)
+        self.o_ver = torch.empty((k + 1, B, Hq, D), dtype=torch.float32, device=self.dev)
+
+        # workspaces
+        self.ws_draft = self._ws(L.vc_draft_workspace_bytes(sh, self.kv))
+        max_chunk = c.chunk if c.staged else self.full_cap
+        self.ws_verify = self._ws(L.vc_verify_workspace_bytes(sh, k + 1, max_chunk))
+        self.ws_vocab_d = self._ws(L.vc_vocab_workspace_bytes(B, c.hidden, c.vocab))
+        self.ws_vocab_v = self._ws(L.vc_vocab_workspace_bytes((k + 1) * B, c.hidden, c.vocab))
+        self.ws_commit = self._ws(L.vc_commit_workspace_bytes(sh))
+
+    # ---------------------------------------------------------------- setup
+    def _ws(self, n: int) -> torch.Tensor:
+        return torch.empty((max(n, 256) + 255) // 256 * 256, dtype=torch.uint8, device=self.dev)
+
+    def _fill_context(self, K, V, t_cap):
+        c = self.cfg
+        s = self.stream.cuda_stream
+        sdev.fill_ctx(c.seed, False, c.batch, c.n_kv_heads, c.context, c.head_dim, t_cap, _ptr(self.key_mult),
+                      K.data_ptr(), s)
+        sdev.fill_ctx(c.seed, True, c.batch, c.n_kv_heads, c.context, c.head_dim, t_cap, None, V.data_ptr(), s)
+
+    def _init_staged(self):
+        """Full cache in pinned host memory. The context is drawn on the device,
+        copied to the host cache, and kept on the device only until the
+        compressed cache has been built from it."""
+        c = self.cfg
+        B, Hkv, D, T = c.batch, c.n_kv_heads, c.head_dim, c.context
+        self.full_k = torch.empty((B, Hkv, self.full_cap, D), dtype=torch.bfloat16, pin_memory=True)
+        self.full_v = torch.empty((B, Hkv, self.full_cap, D), dtype=torch.bfloat16, pin_memory=True)
+        big_k = torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device=self.dev)
+        big_v = torch.empty_like(big_k)
+        s = self.stream.cuda_stream
+        sdev.fill_ctx(c.seed, False, B, Hkv, T, D, T, _ptr(self.key_mult), big_k.data_ptr(), s)
+        sdev.fill_ctx(c.seed, True, B, Hkv, T, D, T, None, big_v.data_ptr(), s)
+        self.full_k[:, :, :T].copy_(big_k)
+        self.full_v[:, :, :T].copy_(big_v)
+        torch.cuda.synchronize(self.dev)
+        self._big = (big_k, big_v)
+        self.chunk_k = [torch.empty((B, Hkv, c.chunk, D), dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
+        self.chunk_v = [torch.empty_like(self.chunk_k[0]) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(self.dev)
+
+    def _init_kivi(self):
+        c = self.cfg
+        B, Hkv, D, bits = c.batch, c.n_kv_heads, c.head_dim, c.bits
+        n_body = c.context - c.residual
+        if n_body < 0 or n_body % 32:
+            raise ValueError("context - residual must be a non-negative multiple of 32")
+        self.body_cap = _round32(n_body + self.rounds_cap * (c.k + 1) + 32)
+        nb = self.body_cap // 32
+        dev = self.dev
+        self.k_codes = torch.zeros((B, Hkv, self.body_cap, D * bits // 32), dtype=torch.int32, device=dev)
+        self.k_scale = torch.zeros((B, Hkv, nb, D), dtype=torch.float16, device=dev)
+        self.k_zero = torch.zeros_like(self.k_scale)
+        self.v_codes = torch.zeros((B, Hkv, nb, 64, D * bits // 64), dtype=torch.int32, device=dev)
+        self.v_scale = torch.zeros((B, Hkv, nb, D // 32, 32), dtype=torch.float16, device=dev)
+        self.v_zero = torch.zeros_like(self.v_scale)
+        for o in (self.kv, self.dc):
+            o.bits = bits
+            o.body_cap = self.body_cap
+            o.k_codes, o.v_codes = self.k_codes.data_ptr(), self.v_codes.data_ptr()
+            o.k_scale, o.k_zero = self.k_scale.data_ptr(), self.k_zero.data_ptr()
+            o.v_scale, o.v_zero = self.v_scale.data_ptr(), self.v_zero.data_ptr()
+        if c.staged:
+            src_k, src_v = self._big
+            t_cap = c.context
+        else:
+            src_k, src_v, t_cap = self.full_k, self.full_v, self.full_cap
+        L.vc_kivi_quantize(self.shape, src_k.data_ptr(), src_v.data_ptr(), t_cap, n_body, c.residual, self.dc,
+                           self.stream.cuda_stream)
+        if c.staged:
+            torch.cuda.synchronize(self.dev)
+            del self._big
+
+    def _init_tokdrop(self):
+        c = self.cfg
+        B, Hkv, T = c.batch, c.n_kv_heads, c.context
+        n_keep = int(np.ceil(c.keep * T - 1e-12)) if c.keep < 1.0 else T
+        self.n_keep = n_keep
+        scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=self.dev)
+        sdev.fill_scores(c.seed, B, Hkv, T, scores.data_ptr(), self.stream.cuda_stream)
+        self.kept = torch.empty((B, Hkv, max(n_keep, 1)), dtype=torch.int32, device=self.dev)
+        L.vc_tokdrop_select(self.shape, scores.data_ptr(), T, n_keep, self.kept.data_ptr(), None, 0,
+                            self.stream.cuda_stream)
+        self.kv.body_cap = self.dc.body_cap = max(n_keep, 1)
+        self.kv.kept_idx = self.kept.data_ptr()
+        if self.cfg.staged:
+            raise ValueError("token drop gathers from the full cache and needs it on the device")
+        self.kv.src_k, self.kv.src_v = self.full_k.data_ptr(), self.full_v.data_ptr()
+        self.kv.src_t_cap = self.full_cap
+        self.body_len.fill_(n_keep)
+        self.scores = scores
+
+    # --------------------------------------------------------------- steps
+    def draft_step(self, j: int):
+        c = self.cfg
+        s = self.stream.cuda_stream
+        sdev.embed_draft(c.seed, self.xs[j].data_ptr(), 1, c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                         _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
+                         self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), s)
+        self.draft_attention()
+        L.vc_vocab_logits(c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(),
+                          self.xs[j + 1].data_ptr(), None, None, self.ws_draft_vocab_ptr(), self.ws_vocab_d.numel(),
+                          s)
+
+    def ws_draft_vocab_ptr(self):
+        return self.ws_vocab_d.data_ptr()
+
+    def draft_attention(self):
+        L.vc_draft_decode_attn(self.shape, self.q_draft.data_ptr(), self.kv, self.o_draft.data_ptr(),
+                               self.ws_draft.data_ptr(), self.ws_draft.numel(), self.stream.cuda_stream)
+
+    def embed_block(self):
+        c = self.cfg
+        sdev.embed(c.seed, self.xs.data_ptr(), (c.k + 1) * c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                   _ptr(self.key_mult), self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(),
+                   self.stream.cuda_stream)
+
+    def verify_attention(self):
+        c = self.cfg
+        s = self.stream.cuda_stream
+        if not c.staged:
+            ctx = L.vc_kv_chunk(self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, 0, self.full_cap)
+            L.vc_verify_attn(self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
+                             self.ctx_len.data_ptr(), L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, self.o_ver.data_ptr(),
+                             self.ws_verify.data_ptr(), self.ws_verify.numel(), s)
+            return
+        self.verify_staged()
+
+    def stage_plan(self):
+        """Chunks covering every position that may hold context this round."""
+        c = self.cfg
+        upper = min(self.full_cap, c.context + self.round_idx * (c.k + 1))
+        return [(t0, min(c.chunk, upper - t0)) for t0 in range(0, upper, c.chunk)]
+
+    def verify_staged(self):
+        """Stream the host-resident full cache through two device chunk buffers:
+        the copy of chunk i+1 (side stream) overlaps the verification of chunk
+        i (compute stream)."""
+        c = self.cfg
+        comp = self.stream
+        cs = self.copy_stream
+        plan = self.stage_plan()
+        ready = [torch.cuda.Event() for _ in plan]
+        free = [torch.cuda.Event() for _ in range(2)]
+        cs.wait_stream(comp)  # committed rows of the previous round are in host memory
+        for i, (t0, n) in enumerate(plan):
+            buf = i % 2
+            if i >= 2:
+                cs.wait_event(free[buf])
+            L.vc_stage_full_kv(self.shape, self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, t0, n,
+                               self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), c.chunk, cs.cuda_stream,
+                               None)
+            ready[i].record(cs)
+            comp.wait_event(ready[i])
+            flags = (L.VC_VERIFY_BEGIN if i == 0 else 0) | (L.VC_VERIFY_END if i == len(plan) - 1 else 0)
+            ctx = L.vc_kv_chunk(self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), c.chunk, t0, n)
+            L.vc_verify_attn(self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
+                             self.ctx_len.data_ptr(), flags, self.o_ver.data_ptr(), self.ws_verify.data_ptr(),
+                             self.ws_verify.numel(), comp.cuda_stream)
+            free[buf].record(comp)
+
+    def verify_vocab(self):
+        c = self.cfg
+        L.vc_vocab_logits((c.k + 1) * c.batch, c.hidden, c.vocab, self.o_ver.data_ptr(), self.W.data_ptr(),
+                          self.y.data_ptr(), None, None, self.ws_vocab_v.data_ptr(), self.ws_vocab_v.numel(),
+                          self.stream.cuda_stream)
+
+    def accept_commit(self):
+        c = self.cfg
+        r = self.round_idx
+        if r >= self.rounds_cap:
+            raise RuntimeError("round capacity exhausted; raise rounds_cap")
+        s = self.stream.cuda_stream
+        na = self.n_accept[r]
+        L.vc_greedy_accept(c.batch, c.k, self.xs.data_ptr(), self.y.data_ptr(), na.data_ptr(), self.xs[0].data_ptr(),
+                           self.committed[r].data_ptr(), s)
+        full_k = self.full_k.data_ptr()
+        full_v = self.full_v.data_ptr()
+        L.vc_commit_round(self.shape, c.k, na.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), full_k, full_v,
+                          self.full_cap, self.ctx_len.data_ptr(), self.dc, self.status.data_ptr(),
+                          self.ws_commit.data_ptr(), self.ws_commit.numel(), s)
+        self.round_idx += 1
+
+    def round(self):
+        for j in range(self.cfg.k):
+            self.draft_step(j)
+        self.embed_block()
+        self.verify_attention()
+        self.verify_vocab()
+        self.accept_commit()

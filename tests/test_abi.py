@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/vc.h declares, and rejects bad arguments on the host (nothing is
+launched, so these run anywhere)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc.h")
+
+L = pytest.importorskip("lossless_speculative_kv_amd._lib", reason="libvc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:vc_status|const char \*)\s*(vc_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L.lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def test_version_string():
+    assert "gfx950" in L.version()
+
+
+def shape(B=2, Hq=8, Hkv=2, D=128):
+    return L.vc_attn_shape(B, Hq, Hkv, D)
+
+
+def kivi_kv(**kw):
+    kv = L.vc_draft_kv()
+    kv.kind, kv.bits, kv.body_cap, kv.tail_cap = L.VC_DRAFT_KIVI, 2, 1024, 64
+    fake = 0x10000  # never dereferenced: every test below fails before any launch
+    for f in ("body_len", "tail_len", "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "tail_k",
+              "tail_v"):
+        setattr(kv, f, fake)
+    for k, v in kw.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def status(fn, *args):
+    return fn(*args)
+
+
+def test_bad_shapes_rejected():
+    out = C.c_size_t()
+    for sh, code in [(shape(B=0), L.VC_ERR_INVALID_ARG), (shape(Hq=6, Hkv=4), L.VC_ERR_INVALID_ARG),
+                     (shape(D=96), L.VC_ERR_UNSUPPORTED), (shape(Hq=64, Hkv=2), L.VC_ERR_UNSUPPORTED)]:
+        assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv()), C.byref(out)) == code
+        assert "batch" in L.last_error() or "head" in L.last_error() or "group" in L.last_error()
+
+
+def test_draft_argument_checks():
+    sh = shape()
+    out = C.c_size_t()
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(bits=3)), C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(k_codes=None)), C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert "k_codes" in L.last_error()
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(tail_cap=40)), C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(k_scale=0x10002)), C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert "aligned" in L.last_error()
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv()), C.byref(out)) == L.VC_OK
+    assert out.value > 0
+    # workspace too small
+    rc = L.lib.vc_draft_decode_attn(C.byref(sh), 0x10000, C.byref(kivi_kv()), 0x10000, 0x10000, 16, None)
+    assert rc == L.VC_ERR_WORKSPACE
+    rc = L.lib.vc_draft_decode_attn(C.byref(sh), None, C.byref(kivi_kv()), 0x10000, 0x10000, 1 << 30, None)
+    assert rc == L.VC_ERR_INVALID_ARG
+
+
+def test_verify_vocab_accept_checks():
+    sh = shape()
+    out = C.c_size_t()
+    assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 0, 1024, C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 65, 1024, C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 33, 1024, C.byref(out)) == L.VC_OK
+    sh16 = shape(Hq=32, Hkv=2)  # g = 16, 33 * 16 rows > 384
+    assert L.lib.vc_verify_workspace_bytes(C.byref(sh16), 33, 1024, C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    ctx = L.vc_kv_chunk(0x10000, 0x10000, 100, 0, 200)  # tok_count > t_cap
+    rc = L.lib.vc_verify_attn(C.byref(sh), 4, 0x10000, 0x10000, 0x10000, C.byref(ctx), 0x10000, 3, 0x10000, 0x10000,
+                              1 << 30, None)
+    assert rc == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_vocab_workspace_bytes(8, 100, 1000, C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert L.lib.vc_vocab_workspace_bytes(0, 128, 1000, C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert L.lib.vc_vocab_workspace_bytes(8, 4096, 128256, C.byref(out)) == L.VC_OK
+    assert L.lib.vc_greedy_accept(0, 4, 0x10000, 0x10000, 0x10000, 0x10000, None, None) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_greedy_accept(2, 4, None, 0x10000, 0x10000, 0x10000, None, None) == L.VC_ERR_INVALID_ARG
+
+
+def test_stage_and_compressor_checks():
+    sh = shape()
+    rc = L.lib.vc_stage_full_kv(C.byref(sh), 0x10000, 0x10000, 1000, 900, 200, 0x10000, 0x10000, 4096, None, None)
+    assert rc == L.VC_ERR_INVALID_ARG
+    dc = L.vc_draft_cache()
+    dc.kind = L.VC_DRAFT_TOKDROP
+    assert L.lib.vc_kivi_quantize(C.byref(sh), 0x10000, 0x10000, 1024, 64, 32, C.byref(dc), None) == L.VC_ERR_INVALID_ARG
+    out = C.c_size_t()
+    assert L.lib.vc_tokdrop_workspace_bytes(C.byref(sh), 0, C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_tokdrop_select(C.byref(sh), 0x10000, 100, 101, 0x10000, None, 0, None) == L.VC_ERR_INVALID_ARG

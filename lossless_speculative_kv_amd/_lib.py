@@ -59,6 +59,13 @@ class vc_draft_cache(C.Structure):
 
 
 def _load() -> C.CDLL:
+    # libvc.so needs the HIP runtime (soname libamdhip64.so.7). PyTorch ships its
+    # own copy and a process must hold exactly one runtime, so torch is loaded
+    # first: the dynamic linker then binds libvc.so to the runtime torch uses.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lossless_speculative_kv_amd.build`")
     return C.CDLL(LIB_PATH)

@@ -238,9 +238,10 @@ __device__ __forceinline__ void kivi_block(const DraftParams& P, size_t unit, in
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r >> 1, rr = 2 * (r & 1);
-      const f16x2 ph = __builtin_bit_cast(f16x2, pack_f16(s[h][i][rr], s[h][i][rr + 1]));
-      st.zt[h] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(f16x2, vzw[r]), st.zt[h], false);
-      Bp[h][r] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(f16x2, vsw[r]));
+      const f16x2 ph = as_f16x2(pack_f16(s[h][i][rr], s[h][i][rr + 1]));
+      const uint32_t zw = vzw[r], sw = vsw[r];
+      st.zt[h] = __builtin_amdgcn_fdot2(ph, as_f16x2(zw), st.zt[h], false);
+      Bp[h][r] = as_u32(ph * as_f16x2(sw));
     }
 
   // ---- PV ----

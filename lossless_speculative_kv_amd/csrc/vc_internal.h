@@ -56,6 +56,13 @@ __device__ __forceinline__ uint32_t pack16(float lo, float hi) {
   if constexpr (BF16) return pack_bf16(lo, hi);
   else return pack_f16(lo, hi);
 }
+// Reinterpret a 32-bit word as two fp16 values and back. The word is taken by
+// value on purpose: this hipcc (clang 22) reads element 0 when
+// __builtin_bit_cast is applied directly to an ext-vector subscript such as
+// v[r] inside an unrolled loop, so vector elements must pass through a
+// scalar first.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

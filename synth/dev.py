@@ -5,6 +5,11 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+try:  # bind to the HIP runtime torch already uses (one runtime per process)
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcsynth.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m lossless_speculative_kv_amd.build`")

@@ -375,7 +375,7 @@ def test_tokdrop_select_parity(L, T, keep, ties):
     if ties:
         sc = np.floor(np.log2(sc)).astype(np.float32)  # few distinct values
     n_keep = T if keep >= 1.0 else int(math.ceil(keep * T - 1e-12))
-    sh = L.vc_attn_shape(B, 8, Hkv, 64)
+    sh = L.vc_attn_shape(B, 2 * Hkv, Hkv, 64)
     kept = torch.full((B, Hkv, n_keep), -1, dtype=torch.int32, device="cuda")
     L.vc_tokdrop_select(sh, to_dev(sc).data_ptr(), T, n_keep, kept.data_ptr(), None, 0, stream())
     torch.cuda.synchronize()

@@ -1,0 +1,203 @@
+"""Benchmark: VeriCache rounds on one MI355X, one JSON line on stdout.
+
+A step is one whole round of the hot path on one batch of synthetic input:
+k draft steps (embedding, draft decode attention over the compressed cache,
+vocab projection + argmax), the verification pass over the full cache (verify
+attention, vocab projection + argmax), greedy acceptance and commit (full
+cache append, tail rewrite, residual flush). Inputs are resident in HBM when
+the timed region starts.
+
+metric (per decoder layer): accepted tokens per second per layer,
+    value = sum over timed rounds and sequences of (m + 1)
+            / sum over timed rounds of (k * t_draft_attn + t_verify_attn),
+with the attention times measured by HIP events on the compute stream inside
+the timed region (a real model projects to the vocabulary once per token,
+not once per layer). The whole-round wall clock is reported as ms_per_step
+and round_tok_s.
+
+roofline: the draft decode attention (the dominant term of the metric):
+algorithmic bytes per launch (compressed body + fp16 tail + q + out) over its
+measured average duration, against 8 TB/s.
+cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3-8b-layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg, quiet=False):
+    if not quiet:
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def draft_bytes_per_launch(cfg, body_len, tail_len):
+    """Algorithmic bytes of one draft attention launch: what the method must
+    read for each (sequence, KV head) plus the query and output vectors."""
+    B, Hq, Hkv, D = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    qo = B * Hq * D * (2 + 4)
+    if cfg.kind == "kivi":
+        per_tok = 2 * D * cfg.bits // 8 + 4 * D // 32 + 4 * D // 32   # K,V codes + K scale/zero per token + V scale/zero
+        tail_tok = 4 * D                                            # fp16 K and V
+        return sum(Hkv * (body_len[b] * per_tok + tail_len[b] * tail_tok) for b in range(B)) + qo
+    if cfg.kind == "tokdrop":
+        return sum(Hkv * (body_len[b] * (4 * D + 4) + tail_len[b] * 4 * D) for b in range(B)) + qo
+    return sum(Hkv * (body_len[b] + tail_len[b]) * 4 * D for b in range(B)) + qo
+
+
+def verify_bytes_per_launch(cfg, ctx_len):
+    B, Hq, Hkv, D, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.k + 1
+    return sum(Hkv * (ctx_len[b] + n) * 4 * D for b in range(B)) + n * B * Hq * D * (2 + 4)
+
+
+def cpu_baseline(cfg, accepted_per_round, quiet):
+    """The CPU oracle (fp64 numpy) on a bounded sample: one sequence and one
+    KV-head group (its g query heads) of the same layer, one whole round
+    (k draft steps + verify + accept + commit), projected to the batch by
+    B * Hkv (attention work is linear in it)."""
+    import numpy as np
+
+    from oracle.model import ModelConfig, make_states
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    g = cfg.group
+    ocfg = ModelConfig(batch=1, n_q_heads=g, n_kv_heads=1, head_dim=cfg.head_dim, context=cfg.context,
+                       vocab=8192, k=cfg.k, kind=cfg.kind, bits=cfg.bits, residual=cfg.residual, keep=cfg.keep,
+                       outliers=cfg.outliers, seed=cfg.seed)
+    log("cpu baseline: building the oracle sample", quiet)
+    _, states = make_states(ocfg)
+    t0 = time.perf_counter()
+    states[0].run_round()
+    dt = time.perf_counter() - t0
+    scale = cfg.batch * cfg.n_kv_heads
+    projected = dt * scale
+    value = accepted_per_round / projected
+    log(f"cpu baseline: sample round {dt:.2f} s, projected round {projected:.1f} s", quiet)
+    return {
+        "value": value, "unit": "accepted tok/s/layer", "cores": threads, "kind": "oracle",
+        "sample": (f"1 sequence x 1 KV-head group ({g} q heads) of the {cfg.name} shape, one whole oracle round "
+                   f"(k={cfg.k} draft steps + verify + accept + commit, vocab 8192 x {g * cfg.head_dim}), "
+                   f"{dt:.2f} s, scaled x{scale} (batch x KV heads) to {projected:.1f} s per round; "
+                   f"accepted tokens per round taken from the GPU run (identical by parity)"),
+        "sample_seconds": dt, "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path is measured on a single "
+              "MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from lossless_speculative_kv_amd import configs, engine
+
+    cfg = configs.BY_NAME[args.workload]
+    q = args.quiet
+    log(f"workload {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} D={cfg.head_dim} "
+        f"T={cfg.context} k={cfg.k} V={cfg.vocab} kind={cfg.kind}", q)
+    t_setup = time.perf_counter()
+    eng = engine.Engine(cfg, rounds_cap=args.warmup + args.steps)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s", q)
+
+    for _ in range(args.warmup):
+        eng.round()
+    torch.cuda.synchronize()
+    body0, tail0, ctx0 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
+    eng.events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        eng.round()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    body1, tail1, ctx1 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
+    ev = eng.events
+    eng.events = None
+
+    times = {}
+    for name, a, b in ev:
+        times.setdefault(name, []).append(a.elapsed_time(b) * 1e-3)
+    n_acc = eng.n_accept[args.warmup:args.warmup + args.steps].cpu().numpy()
+    accepted = float((n_acc + 1).sum())
+    t_draft = float(np.sum(times.get("draft_attn", [0.0])))
+    t_verify = float(np.sum(times.get("verify_attn", [0.0])))
+    attn_time = t_draft + t_verify
+    value = accepted / attn_time if attn_time > 0 else 0.0
+    n_draft = len(times.get("draft_attn", []))
+    t_draft_avg = t_draft / max(n_draft, 1)
+    t_verify_avg = t_verify / max(len(times.get("verify_attn", [])), 1)
+
+    mid_body = [(int(a) + int(b)) / 2 for a, b in zip(body0, body1)]
+    mid_tail = [(int(a) + int(b)) / 2 + cfg.k / 2 for a, b in zip(tail0, tail1)]  # tail grows by 1 per draft step
+    draft_bytes = draft_bytes_per_launch(cfg, mid_body, mid_tail)
+    verify_bytes = verify_bytes_per_launch(cfg, [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)])
+    draft_gbs = draft_bytes / t_draft_avg / 1e9
+    verify_gbs = verify_bytes / t_verify_avg / 1e9
+
+    B, k = cfg.batch, cfg.k
+    ceiling = B * (k + 1) / (k * t_draft_avg + t_verify_avg)
+    breakdown = {name: {"avg_us": float(np.mean(v)) * 1e6, "calls": len(v)} for name, v in times.items()}
+    result = {
+        "metric": "accepted tok/s/layer; draft & verify attn HBM GB/s as % of 8 TB/s peak",
+        "value": value,
+        "unit": "accepted tok/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/fp16 MFMA, fp32 accumulate (KIVI-2 codes)",
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "context": cfg.context,
+                   "draft_k": cfg.k, "compressor": cfg.kind if cfg.kind != "kivi" else f"kivi-{cfg.bits}",
+                   "residual": cfg.residual, "vocab": cfg.vocab, "hidden": cfg.hidden},
+        "roofline": {"bound": "hbm", "kernel": "draft decode attention (vc_draft_decode_attn, split + merge)",
+                     "achieved": draft_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": draft_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": draft_bytes, "avg_launch_us": t_draft_avg * 1e6},
+        "verify_attn": {"achieved_GBs": verify_gbs, "frac": verify_gbs / HBM_PEAK_GBS,
+                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_verify_avg * 1e6},
+        "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": accepted / args.steps,
+                   "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
+        "round_tok_s": accepted / wall,
+        "what_if_all_accepted_tok_s_layer": ceiling,
+        "kernels": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, accepted / args.steps, q)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

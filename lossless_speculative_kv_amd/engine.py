@@ -51,6 +51,9 @@ class Engine:
         B, Hq, Hkv, D, k = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.k
         self.rounds_cap = rounds_cap
         self.round_idx = 0
+        # optional timing hook: when a list, (name, start, end) torch events are
+        # appended around the attention calls (recorded on the compute stream)
+        self.events = None
         s = self.stream.cuda_stream
         bf = torch.bfloat16
 
@@ -217,16 +220,24 @@ class Engine:
                          _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
                          self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), s)
         self.draft_attention()
-        L.vc_vocab_logits(c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(),
-                          self.xs[j + 1].data_ptr(), None, None, self.ws_draft_vocab_ptr(), self.ws_vocab_d.numel(),
-                          s)
+        self._timed("draft_vocab", lambda: L.vc_vocab_logits(
+            c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(), self.xs[j + 1].data_ptr(),
+            None, None, self.ws_vocab_d.data_ptr(), self.ws_vocab_d.numel(), s))
 
-    def ws_draft_vocab_ptr(self):
-        return self.ws_vocab_d.data_ptr()
+    def _timed(self, name, fn):
+        if self.events is None:
+            fn()
+            return
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        fn()
+        b.record(self.stream)
+        self.events.append((name, a, b))
 
     def draft_attention(self):
-        L.vc_draft_decode_attn(self.shape, self.q_draft.data_ptr(), self.kv, self.o_draft.data_ptr(),
-                               self.ws_draft.data_ptr(), self.ws_draft.numel(), self.stream.cuda_stream)
+        self._timed("draft_attn", lambda: L.vc_draft_decode_attn(
+            self.shape, self.q_draft.data_ptr(), self.kv, self.o_draft.data_ptr(), self.ws_draft.data_ptr(),
+            self.ws_draft.numel(), self.stream.cuda_stream))
 
     def embed_block(self):
         c = self.cfg
@@ -239,9 +250,10 @@ class Engine:
         s = self.stream.cuda_stream
         if not c.staged:
             ctx = L.vc_kv_chunk(self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, 0, self.full_cap)
-            L.vc_verify_attn(self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
-                             self.ctx_len.data_ptr(), L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, self.o_ver.data_ptr(),
-                             self.ws_verify.data_ptr(), self.ws_verify.numel(), s)
+            self._timed("verify_attn", lambda: L.vc_verify_attn(
+                self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
+                self.ctx_len.data_ptr(), L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, self.o_ver.data_ptr(),
+                self.ws_verify.data_ptr(), self.ws_verify.numel(), s))
             return
         self.verify_staged()
 
@@ -280,9 +292,9 @@ class Engine:
 
     def verify_vocab(self):
         c = self.cfg
-        L.vc_vocab_logits((c.k + 1) * c.batch, c.hidden, c.vocab, self.o_ver.data_ptr(), self.W.data_ptr(),
-                          self.y.data_ptr(), None, None, self.ws_vocab_v.data_ptr(), self.ws_vocab_v.numel(),
-                          self.stream.cuda_stream)
+        self._timed("verify_vocab", lambda: L.vc_vocab_logits(
+            (c.k + 1) * c.batch, c.hidden, c.vocab, self.o_ver.data_ptr(), self.W.data_ptr(), self.y.data_ptr(),
+            None, None, self.ws_vocab_v.data_ptr(), self.ws_vocab_v.numel(), self.stream.cuda_stream))
 
     def accept_commit(self):
         c = self.cfg

@@ -78,9 +78,10 @@ typedef struct {
  *     k_scale, k_zero fp16 [u][Tc/32][D].
  *     v_codes uint32 [u][Tc/32][64][D*bits/64]: per 32-token block, 64 lanes
  *             L = 16*q + c (q 0..3, c 0..15); lane L holds channels 16*m + c
- *             (m 0..D/16-1) of the tokens tau(q,s) = 16*(s/4) + 4*q + s%4
+ *             (m 0..D/16-1) of the tokens tau(q,s) = 4*q + s/2 + 16*(s%2)
  *             (s 0..7); code (m, s) in word (m*bits)/4 at bit
- *             16*(s%2) + bits*(s/2 + 4*(m % (4/bits))).
+ *             8*(s/2) + 4*(s%2) + 2*(m%2)             for bits = 2,
+ *             16*(s/4) + 8*(s%2) + 4*((s/2)%2)        for bits = 4.
  *     v_scale, v_zero fp16 [u][Tc/32][D/32][32]: entry 8*q + s of channel
  *             group j is the parameter of token tau(q,s) of the block.
  * VC_DRAFT_TOKDROP: the body is a sorted list of kept token positions

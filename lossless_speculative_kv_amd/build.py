@@ -32,9 +32,17 @@ LIBS = {
 }
 
 
+# Per-source extra flags. The draft attention kernels keep their MFMA
+# accumulators in VGPRs: the online-softmax rescale touches them with VALU
+# instructions, and in AGPRs every touch is a copy out and back.
+EXTRA = {
+    "draft_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

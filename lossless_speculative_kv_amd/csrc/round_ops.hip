@@ -152,8 +152,9 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
     for (int mm = 0; mm < MPW; ++mm) {
       const int m = w * MPW + mm;
       for (int s = 0; s < 8; ++s) {
-        const int t = 16 * (s >> 2) + 4 * q + (s & 3);
-        const int bit = 16 * (s & 1) + BITS * ((s >> 1) + 4 * (m % MPW));
+        const int t = 4 * q + (s >> 1) + 16 * (s & 1);
+        const int bit = (BITS == 2) ? 8 * (s >> 1) + 4 * (s & 1) + 2 * (m & 1)
+                                    : 16 * (s >> 2) + 8 * (s & 1) + 4 * ((s >> 1) & 1);
         word |= (uint32_t)cv[t][16 * m + c] << bit;
       }
     }
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
   }
   for (int i = tid; i < NG * 32; i += 256) {
     const int j = i / 32, e = i % 32, q = e >> 3, s = e & 7;
-    const int t = 16 * (s >> 2) + 4 * q + (s & 3);
+    const int t = 4 * q + (s >> 1) + 16 * (s & 1);
     P.v_scale[((unit * nbc + dblk) * NG + j) * 32 + e] = sv_s[t][j];
     P.v_zero[((unit * nbc + dblk) * NG + j) * 32 + e] = sv_z[t][j];
   }

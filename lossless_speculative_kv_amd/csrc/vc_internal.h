@@ -97,6 +97,28 @@ __device__ __forceinline__ float max_q(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Rotations within a row of 16 lanes (DPP row_ror:4 / row_ror:8).
+__device__ __forceinline__ float dpp_ror4(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// Max over the 16 lanes of a row; every lane of the row gets the same value.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_xor1(x));
+  x = fmaxf(x, dpp_xor2(x));
+  x = fmaxf(x, dpp_ror4(x));
+  return fmaxf(x, dpp_ror8(x));
+}
+// Sum over the 16 lanes of a row (the order of the last two additions
+// depends on the lane's quad, so lanes may differ in the last bit).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_xor1(x);
+  x += dpp_xor2(x);
+  x += dpp_ror4(x);
+  return x + dpp_ror8(x);
+}
 // Sum over the NG adjacent lanes of a column group (NG in {1, 2, 4}).
 template <int NG>
 __device__ __forceinline__ float sum_group(float x) {

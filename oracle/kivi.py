@@ -94,17 +94,28 @@ def dequantize_values(codes, scale, zero) -> np.ndarray:
 # Value codes, per (sequence, KV head): uint32 [T/32][64][D*b/64]. Each
 # 32-token block is split over 64 "lanes" L = 16*q + c (q in 0..3,
 # c in 0..15). Lane L holds, for every channel 16*m + c (m in 0..D/16-1),
-# the codes of the 8 tokens tau(q, s) = 16*(s // 4) + 4*q + (s % 4),
-# s in 0..7, of the block. Inside the lane's words, the code of
-# (m, s) sits in word (m*b) // 4 at bit 16*(s % 2) + b*f with
-# f = s // 2 + 4*(m % (4 // b)).
+# the codes of the 8 tokens tau(q, s) = 4*q + s // 2 + 16*(s % 2),
+# s in 0..7, of the block (slots 2r and 2r + 1 are tokens 4q + r and
+# 4q + r + 16). Inside the lane's words, the code of (m, s) sits in word
+# (m*b) // 4 at bit
+#   b = 2: 8*(s // 2) + 4*(s % 2) + 2*(m % 2)
+#   b = 4: 16*(s // 4) + 8*(s % 2) + 4*((s // 2) % 2)
+# i.e. each byte holds the two codes of one slot pair (one code per nibble,
+# in the nibble's low bits for b = 2).
 # Value scale / zero: fp16 [T/32][D/32][32]; entry 8*q + s of group j is the
 # parameter of token tau(q, s) of the block, channel group j.
 
 
 def value_slot_token(q: int, s: int) -> int:
     """Token (within a 32-token block) stored in value slot s of lane group q."""
-    return 16 * (s // 4) + 4 * q + (s % 4)
+    return 4 * q + s // 2 + 16 * (s % 2)
+
+
+def value_code_bit(bits: int, m: int, s: int) -> int:
+    """Bit position of the code of (tile m, slot s) inside its lane word."""
+    if bits == 2:
+        return 8 * (s // 2) + 4 * (s % 2) + 2 * (m % 2)
+    return 16 * (s // 4) + 8 * (s % 2) + 4 * ((s // 2) % 2)
 
 
 def pack_key_codes(codes, bits: int) -> np.ndarray:
@@ -135,10 +146,9 @@ def _value_positions(bits: int, D: int):
             t = value_slot_token(q, s)
             for d in range(D):
                 m, c = d // 16, d % 16
-                f = s // 2 + 4 * (m % (4 // bits))
                 lane[t, d] = 16 * q + c
                 word[t, d] = (m * bits) // 4
-                bit[t, d] = 16 * (s % 2) + bits * f
+                bit[t, d] = value_code_bit(bits, m, s)
     return lane, word, bit
 
 

@@ -153,7 +153,7 @@ vc_status vc_verify_workspace_bytes(const vc_attn_shape *shape, int32_t n_rows, 
 /* Position-major block arrays: q: bf16 [n_rows][B][Hq][D]; k_new, v_new:
  * bf16 [n_rows][B][Hkv][D] (the block tokens' keys/values); ctx_len: [B];
  * out: fp32 [n_rows][B][Hq][D], written by the END call. n_rows <= 64 and
- * n_rows * g <= 384. */
+ * n_rows * g <= 288. */
 vc_status vc_verify_attn(const vc_attn_shape *shape, int32_t n_rows, const void *q, const void *k_new,
                          const void *v_new, const vc_kv_chunk *ctx, const int32_t *ctx_len, int32_t flags,
                          float *out, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -3,20 +3,26 @@
 // parallel; "P1": verification loads the full cache and is also
 // compute-bound, since every cached token meets (k+1)*g query rows).
 //
-// Work decomposition: one workgroup per (context split, KV head, sequence).
-// All R = n_rows * g query rows of the KV head (row = j * g + head, j the
-// draft position) live in the workgroup, RT row tiles of 16 per wave, so
-// each K/V tile is read from HBM once and staged in LDS (double-buffered,
-// 32 tokens per stage) for every row tile.
-//   QK: S^T[token][row] on v_mfma_f32_16x16x32_bf16, A = 16 key rows (from
-//       LDS), B = 16 query rows (registers, exact bf16).
-//   PV: O^T[channel][row] += V^T[channel][token] * P^T[token][row]; V^T is
-//       read from LDS as 16-bit values (8 tokens per lane per channel).
-// The draft block (x_0..x_k's own keys/values) is the last split of the END
-// call, with the causal mask (row j sees block rows 0..j). Per-split
-// partials (max, sum, unnormalised output) are folded in split order into a
-// running state kept in the workspace, which allows the context to arrive in
-// staged chunks over several calls.
+// Work decomposition: one workgroup per (context split, KV head, sequence),
+// one per CU (its LDS ring keeps a second one out). All R = n_rows * g query
+// rows of the KV head (row = j * g + head, j the draft position) live in the
+// workgroup, RT row tiles of 16 per consumer wave, so each K/V tile is read
+// from HBM once for every row tile. K/V move in 32-token tiles through a
+// 6-stage LDS ring filled by direct-to-LDS buffer loads issued by two
+// producer waves (K and V halves; no registers, four tiles in flight ahead
+// of the one being computed); one workgroup barrier per tile. Only the
+// producers issue such loads, so the consumers' LDS reads never wait on them.
+//   QK: S^T[token][row] on v_mfma_f32_16x16x32_bf16, A = 16 key rows (LDS,
+//       rows XOR-swizzled in 16-byte units so the 16 rows of a read hit
+//       distinct banks), B = 16 query rows (registers, exact bf16).
+//   PV: O^T[channel][row] += V^T[channel][token] * P^T[token][row]; the V^T
+//       operand comes straight from the row-major V tile through the gfx950
+//       transposing LDS read (four token slots of one channel per lane).
+// The draft block (x_0..x_k's own keys/values) follows the context tiles of
+// the last split of the END call, with the causal mask (row j sees block
+// rows 0..j). Per-split partials (max, sum, unnormalised output) are folded
+// in split order into a running state kept in the workspace, which allows
+// the context to arrive in staged chunks over several calls.
 #include "attn_common.h"
 
 namespace vc {
@@ -36,96 +42,92 @@ struct VerifyParams {
   float* run_o;   // [u][R][D]
   float* run_ml;  // [u][R][2]
   float* out;     // fp32 [NR][B][Hq][D]
-  int B, Hq, Hkv, g, NR, R, S, S_ctx, tps, flags;
+  int B, Hq, Hkv, g, NR, R, S, tps, flags;
   float qscale;
 };
 
-constexpr int kTT = 32;  // tokens per LDS stage
+constexpr int kTT = 32;     // tokens per tile
+constexpr int kStages = 6;  // LDS ring depth
+constexpr int kAhead = 4;   // tiles in flight ahead of the one computed (<= kStages - 2)
 
 template <int D>
-struct VerifyLds {
-  static constexpr int KSTR = D + 8;  // halfs; 16-byte aligned rows
-  static constexpr int VSTR = D + 4;  // halfs; conflict-free 16-bit transposed reads
-  static constexpr int KBUF = kTT * KSTR, VBUF = kTT * VSTR;
-  static constexpr int BYTES = 2 * (KBUF + VBUF) * 2;
+struct Tile {
+  static constexpr int KB = kTT * D * 2;        // bytes of the K (or V) half of a stage
+  static constexpr int CHUNKS = KB / 1024;      // 1 KB direct-to-LDS loads per half
+  static constexpr int UPR = D / 8;             // 16-byte units per row
+  static constexpr int RPC = 1024 / (D * 2);    // rows per 1 KB chunk
 };
 
-// Global -> register prefetch of one 32-token K/V tile. Each thread moves
-// 16-byte chunks; rows of invalid tokens are zero.
-template <int D, int MAXC>
-struct TilePrefetch {
-  u32x4 k[MAXC], v[MAXC];
+// LDS unit of (row, 16-byte unit u): XOR swizzle within the row.
+template <int D>
+__device__ __forceinline__ int swz(int row, int u) {
+  return u ^ (row & (Tile<D>::UPR - 1));
+}
+
+// s_waitcnt on the vector-memory counter only: vmcnt(N), others untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// One segment of tiles: K and V rows at a fixed byte stride, rows past the
+// segment's extent read as zero (buffer range check).
+struct Segment {
+  const uint16_t *k, *v;
+  uint32_t bytes;  // extent of each of k and v
+  int row_bytes;
+  int ntiles;
 };
 
-template <int D, int MAXC, typename RowFn>
-__device__ __forceinline__ void prefetch_tile(TilePrefetch<D, MAXC>& pf, const RowFn& rows, int nvalid, int tid,
-                                              int nthreads) {
-  constexpr int CPR = D / 8, CH = kTT * CPR;
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Issue the direct-to-LDS loads of the K (half 0) or V (half 1) part of one
+// tile; one producer wave per half. Lane l of chunk c fills LDS unit 64c + l,
+// i.e. row RPC*c + l / UPR, unit l % UPR, with the global unit that the
+// swizzle puts there. Every operand that is wave-uniform is made visibly so
+// (the buffer resource must sit in scalar registers).
+template <int D>
+__device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int tile, int lane, int half) {
+  using T = Tile<D>;
+  const uint64_t a = reinterpret_cast<uint64_t>(half ? sg.v : sg.k);
+  const uint64_t au = ((uint64_t)uni((uint32_t)(a >> 32)) << 32) | uni((uint32_t)a);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(au), (short)0, (int)uni(sg.bytes), 0x00020000);
+  const int rb = (int)uni((uint32_t)sg.row_bytes), t0 = (int)uni((uint32_t)(tile * kTT));
+  const int rl = lane / T::UPR, ul = lane % T::UPR;
+  char* dst = stage + half * T::KB;
 #pragma unroll
-  for (int u = 0; u < MAXC; ++u) {
-    const int c = tid + u * nthreads;
-    pf.k[u] = u32x4{0u, 0u, 0u, 0u};
-    pf.v[u] = u32x4{0u, 0u, 0u, 0u};
-    if (c < CH) {
-      const int t = c / CPR, x = c % CPR;
-      if (t < nvalid) {
-        pf.k[u] = *reinterpret_cast<const u32x4*>(rows.k(t) + 8 * x);
-        pf.v[u] = *reinterpret_cast<const u32x4*>(rows.v(t) + 8 * x);
-      }
-    }
+  for (int c = 0; c < T::CHUNKS; ++c) {
+    const int row = T::RPC * c + rl;
+    const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, 0);
   }
 }
 
-template <int D, int MAXC>
-__device__ __forceinline__ void store_tile(const TilePrefetch<D, MAXC>& pf, uint16_t* kb, uint16_t* vb, int tid,
-                                           int nthreads) {
-  constexpr int CPR = D / 8, CH = kTT * CPR;
-  using L = VerifyLds<D>;
-#pragma unroll
-  for (int u = 0; u < MAXC; ++u) {
-    const int c = tid + u * nthreads;
-    if (c < CH) {
-      const int t = c / CPR, x = c % CPR;
-      *reinterpret_cast<u32x4*>(kb + t * L::KSTR + 8 * x) = pf.k[u];
-      uint32_t* d = reinterpret_cast<uint32_t*>(vb + t * L::VSTR + 8 * x);
-      *reinterpret_cast<u32x2*>(d) = u32x2{pf.v[u][0], pf.v[u][1]};
-      *reinterpret_cast<u32x2*>(d + 2) = u32x2{pf.v[u][2], pf.v[u][3]};
-    }
-  }
-}
-
-template <int D>
-struct CtxRows {
-  const uint16_t *kb, *vb;
-  __device__ __forceinline__ const uint16_t* k(int t) const { return kb + (size_t)t * D; }
-  __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)t * D; }
-};
-// Block token i of sequence b: row (i, b, hk) of k_new / v_new.
-template <int D>
-struct BlockRows {
-  const uint16_t *kb, *vb;
-  int stride;  // halfs between consecutive block tokens (B * Hkv * D)
-  __device__ __forceinline__ const uint16_t* k(int t) const { return kb + (size_t)t * stride; }
-  __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)t * stride; }
-};
-
-// One 32-token stage for this wave's RT row tiles. tok_valid(t) masks tokens
-// for all rows; blk_row_min(t) >= 0 marks a block token that only rows with
-// draft position j >= blk_row_min(t) may see.
-template <int D, int RT, bool CAUSAL>
-__device__ __forceinline__ void verify_stage(const uint16_t* kb, const uint16_t* vb, int nvalid, int lane,
-                                             const uint32_t (&Bq)[RT][D / 32][4], const int (&rowj)[RT],
+// One 32-token tile for this wave's RT row tiles. nvalid masks tokens for
+// all rows; token t is visible to row tile rt's rows only when t <= lim[rt]
+// (the causal limit in the draft block, relative to the tile's first token;
+// large for context tiles).
+template <int D, int RT>
+__device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int lane,
+                                             const uint32_t (&Bq)[RT][D / 32][4], const int (&lim)[RT],
                                              float qscale, SoftState<RT, D / 16>& st) {
   constexpr int NG = D / 32, MT = D / 16;
-  using L = VerifyLds<D>;
+  using T = Tile<D>;
   const int n = lane & 15, qg = lane >> 4;
   float s[RT][2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const uint16_t* kr = kb + (16 * i + n) * L::KSTR + qg * (D / 4);
+    const int row = 16 * i + n;
+    const char* kr = stage + row * (D * 2);
     u32x4 A[NG];
 #pragma unroll
-    for (int kk = 0; kk < NG; ++kk) A[kk] = *reinterpret_cast<const u32x4*>(kr + 8 * kk);
+    for (int kk = 0; kk < NG; ++kk)
+      A[kk] = *reinterpret_cast<const u32x4*>(kr + swz<D>(row, qg * NG + kk) * 16);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -135,9 +137,7 @@ __device__ __forceinline__ void verify_stage(const uint16_t* kb, const uint16_t*
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * i + 4 * qg + r;
-        bool ok = t < nvalid;
-        if constexpr (CAUSAL) ok = ok && (t <= rowj[rt]);
-        s[rt][i][r] = ok ? c[r] * qscale : kNegInf;
+        s[rt][i][r] = (t < nvalid && t <= lim[rt]) ? c[r] * qscale : kNegInf;
       }
     }
   }
@@ -150,47 +150,38 @@ __device__ __forceinline__ void verify_stage(const uint16_t* kb, const uint16_t*
       const int i = r >> 1, rr = 2 * (r & 1);
       Bp[rt][r] = pack_bf16(s[rt][i][rr], s[rt][i][rr + 1]);
     }
+  // V^T operand: lane n of slot group qg reads token 16h + 4qg + (n >> 2),
+  // channels 16m + 4(n & 3) .. + 3; the transposing read hands lane n the
+  // four token slots of channel 16m + n.
+  const char* vbase = stage + T::KB;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     uint32_t A[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t lo = vb[slot_token(qg, 2 * r) * L::VSTR + 16 * m + n];
-      const uint32_t hi = vb[slot_token(qg, 2 * r + 1) * L::VSTR + 16 * m + n];
-      A[r] = lo | (hi << 16);
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * h + 4 * qg + (n >> 2);
+      const int u = 2 * m + ((n & 3) >> 1);
+      const char* p = vbase + row * (D * 2) + swz<D>(row, u) * 16 + (n & 1) * 8;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+      A[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+      A[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
       st.acc[rt][m] =
           mfma_bf16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]}, st.acc[rt][m]);
+    }
   }
 }
 
-// Stream a run of 32-token tiles through the double-buffered LDS stages.
-template <int D, int RT, int MAXC, bool CAUSAL, typename RowsAt>
-__device__ __forceinline__ void verify_run(RowsAt rows_at, int ntiles, int nvalid_total, char* smem, int lane,
-                                           int tid, int nthreads, const uint32_t (&Bq)[RT][D / 32][4],
-                                           const int (&rowj)[RT], float qscale, SoftState<RT, D / 16>& st) {
-  using L = VerifyLds<D>;
-  uint16_t* base = reinterpret_cast<uint16_t*>(smem);
-  TilePrefetch<D, MAXC> pf;
-  if (ntiles > 0) prefetch_tile<D, MAXC>(pf, rows_at(0), min(kTT, nvalid_total), tid, nthreads);
-  for (int t = 0; t < ntiles; ++t) {
-    uint16_t* kb = base + (t & 1) * (L::KBUF + L::VBUF);
-    uint16_t* vb = kb + L::KBUF;
-    store_tile<D, MAXC>(pf, kb, vb, tid, nthreads);
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch_tile<D, MAXC>(pf, rows_at(t + 1), min(kTT, nvalid_total - (t + 1) * kTT), tid, nthreads);
-    verify_stage<D, RT, CAUSAL>(kb, vb, min(kTT, nvalid_total - t * kTT), lane, Bq, rowj, qscale, st);
-  }
-}
-
-// MAXC: 16-byte chunks per thread per tensor for one stage, ceil(32*D/8 / threads).
-template <int D, int RT, int MAXC>
-__global__ __launch_bounds__(512) void verify_kernel(const VerifyParams P) {
+// Waves 0..NW-1 compute (RT row tiles each); waves NW and NW+1 load.
+template <int D, int RT>
+__global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   constexpr int NG = D / 32, MT = D / 16;
-  __shared__ __attribute__((aligned(16))) char smem[VerifyLds<D>::BYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x, nthreads = blockDim.x;
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(16))) char ring[kStages * 2 * T::KB];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x / 64 - 2;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
   const int n = lane & 15, qg = lane >> 4;
@@ -216,46 +207,62 @@ __global__ __launch_bounds__(512) void verify_kernel(const VerifyParams P) {
     }
   }
 
+  // segment 0: context rows [r0, r0 + nval) of the chunk, visible below ctx_len
+  const int ctx = P.ctx_len[b];
+  const int r0 = split * P.tps;
+  const int nval = max(0, min(min(r0 + P.tps, P.tok_count), ctx - P.tok_begin) - r0);
+  Segment s0;
+  s0.k = P.ck + (unit * P.t_cap + min(r0, P.t_cap)) * D;
+  s0.v = P.cv + (unit * P.t_cap + min(r0, P.t_cap)) * D;
+  s0.bytes = (uint32_t)nval * D * 2;
+  s0.row_bytes = D * 2;
+  s0.ntiles = (nval + kTT - 1) / kTT;
+  // segment 1: the draft block (last split of the END call), causal
+  const bool with_block = (P.flags & VC_VERIFY_END) && split == P.S - 1;
+  Segment s1;
+  const int stride = P.B * P.Hkv * D;
+  s1.k = P.k_new + unit * D;
+  s1.v = P.v_new + unit * D;
+  s1.bytes = (uint32_t)((size_t)P.NR * stride * 2);
+  s1.row_bytes = stride * 2;
+  s1.ntiles = with_block ? (P.NR + kTT - 1) / kTT : 0;
+  const int ntiles = s0.ntiles + s1.ntiles;
+
+  if (wave >= nw) {
+    // producer: K (wave nw) or V (wave nw + 1) halves, kAhead tiles ahead
+    const int half = wave - nw;
+    auto issue = [&](int t) {
+      char* stage = ring + (t % kStages) * 2 * T::KB;
+      t = min(t, ntiles - 1);  // past the end: reload the last tile into an unused stage
+      if (t < s0.ntiles) issue_half<D>(stage, s0, t, lane, half);
+      else issue_half<D>(stage, s1, t - s0.ntiles, lane, half);
+    };
+    if (ntiles > 0) {
+      for (int t = 0; t < kAhead; ++t) issue(t);
+      for (int t = 0; t < ntiles; ++t) {
+        issue(t + kAhead);
+        wait_vm<kAhead * T::CHUNKS>();  // tile t landed
+        __builtin_amdgcn_s_barrier();
+      }
+      wait_vm<0>();  // nothing may land after the workgroup has gone
+    }
+    return;
+  }
+
   SoftState<RT, MT> st;
   st.init();
-  if (split < P.S_ctx) {
-    // context rows [r0, r1) of the chunk, positions tok_begin + r, visible below ctx_len
-    const int ctx = P.ctx_len[b];
-    const int r0 = split * P.tps;
-    int r1 = min(r0 + P.tps, P.tok_count);
-    r1 = min(r1, ctx - P.tok_begin);
-    const int nval = max(0, r1 - r0);
-    const int ntiles = (nval + kTT - 1) / kTT;
-    const uint16_t* kb = P.ck + (unit * P.t_cap + r0) * D;
-    const uint16_t* vb = P.cv + (unit * P.t_cap + r0) * D;
-    verify_run<D, RT, MAXC, false>(
-        [&](int t) { return CtxRows<D>{kb + (size_t)t * kTT * D, vb + (size_t)t * kTT * D}; }, ntiles, nval, smem,
-        lane, tid, nthreads, Bq, rowj, P.qscale, st);
-  } else {
-    // the draft block: tokens x_0..x_{NR-1}, causal
-    const int stride = P.B * P.Hkv * D;
-    const uint16_t* kb = P.k_new + ((size_t)b * P.Hkv + hk) * D;
-    const uint16_t* vb = P.v_new + ((size_t)b * P.Hkv + hk) * D;
-    const int ntiles = (P.NR + kTT - 1) / kTT;
-    // causal masks need the block-token index, which is tile * 32 + t; shift rowj per tile
-    int rj[RT];
+  for (int t = 0; t < ntiles; ++t) {
+    // pairs with the producers' bare barrier; the fence keeps this tile's LDS
+    // reads below it (consumers have no loads in flight, so it costs nothing)
+    __syncthreads();
+    const char* stage = ring + (t % kStages) * 2 * T::KB;
+    const bool blk = t >= s0.ntiles;
+    const int tb = t - s0.ntiles;
+    int lim[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) rj[rt] = rowj[rt];
-    using L = VerifyLds<D>;
-    uint16_t* base = reinterpret_cast<uint16_t*>(smem);
-    TilePrefetch<D, MAXC> pf;
-    for (int t = 0; t < ntiles; ++t) {
-      const BlockRows<D> rows{kb + (size_t)t * kTT * stride, vb + (size_t)t * kTT * stride, stride};
-      const int nv = min(kTT, P.NR - t * kTT);
-      prefetch_tile<D, MAXC>(pf, rows, nv, tid, nthreads);
-      uint16_t* kbuf = base + (t & 1) * (L::KBUF + L::VBUF);
-      __syncthreads();
-      store_tile<D, MAXC>(pf, kbuf, kbuf + L::KBUF, tid, nthreads);
-      __syncthreads();
-      verify_stage<D, RT, true>(kbuf, kbuf + L::KBUF, nv, lane, Bq, rj, P.qscale, st);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) rj[rt] -= kTT;
-    }
+    for (int rt = 0; rt < RT; ++rt) lim[rt] = blk ? rowj[rt] - tb * kTT : kTT;
+    const int nv = blk ? min(kTT, P.NR - tb * kTT) : min(kTT, nval - t * kTT);
+    tile_compute<D, RT>(stage, nv, lane, Bq, lim, P.qscale, st);
   }
 
   // partial for this split: rows of this wave
@@ -316,25 +323,11 @@ __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
   }
 }
 
-template <int D, int RT>
-void launch_verify_rt(const VerifyParams& P, int nwaves, dim3 grid, hipStream_t s) {
-  const dim3 block(64 * nwaves);
-  const int chunks = kTT * D / 8;
-  const int maxc = (chunks + 64 * nwaves - 1) / (64 * nwaves);
-  if (maxc > 4) hipLaunchKernelGGL((verify_kernel<D, RT, (kTT * D / 8 + 63) / 64>), grid, block, 0, s, P);
-  else if (maxc > 2) hipLaunchKernelGGL((verify_kernel<D, RT, 4>), grid, block, 0, s, P);
-  else if (maxc > 1) hipLaunchKernelGGL((verify_kernel<D, RT, 2>), grid, block, 0, s, P);
-  else hipLaunchKernelGGL((verify_kernel<D, RT, 1>), grid, block, 0, s, P);
-}
-
 template <int D>
 void launch_verify(const VerifyParams& P, int rt, int nwaves, dim3 grid, hipStream_t s) {
-  switch (rt) {
-    case 1: launch_verify_rt<D, 1>(P, nwaves, grid, s); break;
-    case 2: launch_verify_rt<D, 2>(P, nwaves, grid, s); break;
-    case 3: launch_verify_rt<D, 3>(P, nwaves, grid, s); break;
-    default: launch_verify_rt<D, 4>(P, nwaves, grid, s); break;
-  }
+  const dim3 block(64 * (nwaves + 2));
+  if (rt == 2) hipLaunchKernelGGL((verify_kernel<D, 2>), grid, block, 0, s, P);
+  else hipLaunchKernelGGL((verify_kernel<D, 3>), grid, block, 0, s, P);
 }
 
 }  // namespace
@@ -343,24 +336,29 @@ struct VerifyPlan {
   int rt, nwaves, tps, s_ctx;
 };
 
-// Row tiling: up to 8 waves with RT = ceil(tiles / 8) row tiles each (<= 4).
-// Context split of a call: about 512 workgroups, whole 256-token runs.
+// Row tiling: two row tiles per consumer wave up to 12 tiles, else three (at
+// most 6 consumer waves plus the 2 producers, so 2 waves per SIMD and the
+// whole register file for the row tiles' accumulators). Context split of a call:
+// about 256 workgroups (one per CU), whole 32-token tiles, at least 8 tiles
+// per split; the draft block rides on the last split. The split count never
+// decreases with chunk_tokens, so a workspace sized for the largest chunk
+// fits every smaller one.
 VerifyPlan verify_plan(const vc_attn_shape& sh, int n_rows, int chunk_tokens) {
   const int R = n_rows * (sh.n_q_heads / sh.n_kv_heads);
   const int tiles = (R + 15) / 16;
-  int rt = (tiles + 7) / 8;
-  if (rt < 1) rt = 1;
+  const int rt = tiles > 12 ? 3 : 2;
   const int nwaves = (tiles + rt - 1) / rt;
   const long long units = (long long)sh.batch * sh.n_kv_heads;
-  long long tps = ((long long)chunk_tokens * units + 511) / 512;
-  tps = ((tps + 255) / 256) * 256;
-  if (tps < 256) tps = 256;
-  int s_ctx = (int)((chunk_tokens + tps - 1) / tps);
+  const long long ctx_tiles = ((long long)chunk_tokens + kTT - 1) / kTT;
+  long long s_ctx = (256 + units - 1) / units;
+  const long long max_s = (ctx_tiles + 7) / 8;
+  if (s_ctx > max_s) s_ctx = max_s;
   if (s_ctx < 1) s_ctx = 1;
-  return VerifyPlan{rt, nwaves, (int)tps, s_ctx};
+  const long long tps = ((ctx_tiles + s_ctx - 1) / s_ctx) * kTT;
+  return VerifyPlan{rt, nwaves, (int)(tps > 0 ? tps : kTT), (int)s_ctx};
 }
 
-int verify_max_rows() { return 8 * 3 * 16; }
+int verify_max_rows() { return 6 * 3 * 16; }
 
 // Workspace: running state first (fixed offsets for every call of one
 // verification), then this call's split partials.
@@ -376,7 +374,7 @@ static size_t part_bytes(const vc_attn_shape& sh, size_t R, size_t S) {
 size_t verify_ws_bytes(const vc_attn_shape& sh, int n_rows, int max_chunk_tokens) {
   const VerifyPlan p = verify_plan(sh, n_rows, max_chunk_tokens);
   const size_t R = (size_t)n_rows * (sh.n_q_heads / sh.n_kv_heads);
-  return run_bytes(sh, R) + part_bytes(sh, R, (size_t)p.s_ctx + 1);
+  return run_bytes(sh, R) + part_bytes(sh, R, (size_t)p.s_ctx);
 }
 
 vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, const void* k_new, const void* v_new,
@@ -387,7 +385,7 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   VerifyParams P{};
   const size_t R = (size_t)n_rows * (sh.n_q_heads / sh.n_kv_heads);
   const size_t units = (size_t)sh.batch * sh.n_kv_heads;
-  const size_t S = (size_t)plan.s_ctx + ((flags & VC_VERIFY_END) ? 1 : 0);
+  const size_t S = (size_t)plan.s_ctx;
   char* w = static_cast<char*>(ws);
   P.run_o = reinterpret_cast<float*>(w);
   w += align_up(units * R * sh.head_dim * 4, 256);
@@ -413,7 +411,6 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   P.NR = n_rows;
   P.R = (int)R;
   P.tps = plan.tps;
-  P.S_ctx = plan.s_ctx;
   P.S = (int)S;
   P.flags = flags;
   P.qscale = kLog2e / sqrtf((float)sh.head_dim);

@@ -82,7 +82,7 @@ def test_verify_vocab_accept_checks():
     assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 0, 1024, C.byref(out)) == L.VC_ERR_INVALID_ARG
     assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 65, 1024, C.byref(out)) == L.VC_ERR_INVALID_ARG
     assert L.lib.vc_verify_workspace_bytes(C.byref(sh), 33, 1024, C.byref(out)) == L.VC_OK
-    sh16 = shape(Hq=32, Hkv=2)  # g = 16, 33 * 16 rows > 384
+    sh16 = shape(Hq=32, Hkv=2)  # g = 16, 33 * 16 rows > 288
     assert L.lib.vc_verify_workspace_bytes(C.byref(sh16), 33, 1024, C.byref(out)) == L.VC_ERR_UNSUPPORTED
     ctx = L.vc_kv_chunk(0x10000, 0x10000, 100, 0, 200)  # tok_count > t_cap
     rc = L.lib.vc_verify_attn(C.byref(sh), 4, 0x10000, 0x10000, 0x10000, C.byref(ctx), 0x10000, 3, 0x10000, 0x10000,

@@ -11,21 +11,24 @@
 // unnormalised output) are merged in split order by draft_merge_kernel.
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
-// for bf16 rows). NG = D/32 channel groups, HS = 16/NG query heads per head
-// set, HPL = 4/NG heads per lane row.
+// for bf16 rows). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
+// row groups per head, HS = 16/NR query heads per head set, HPL = 4/NR heads
+// per lane row. The KIVI kernel takes the narrowest W with HS >= g (one head
+// set); the row kernel uses W = 1 and several head sets when g > HS.
 //   QK: S[row][token] = sum_k A[row][k] B[k][token], B = the keys of 16
-//       tokens, A = the query. Row (hl, j) = NG*hl + j pairs query head hl
-//       with channel group j: in K-step kk the A row is nonzero only when
-//       j == kk, so a lane folds the key scales of one 8-channel run only.
-//       The result lane (q, t) holds rows 4q + r: every channel group of
+//       tokens, A = the query. Row (hl, jr) = NR*hl + jr pairs query head hl
+//       with row group jr: in K-step kk the A row is nonzero only when
+//       kk / W == jr, so a lane folds the key scales of W 8-channel runs
+//       only. The result lane (q, t) holds rows 4q + r: every row group of
 //       HPL heads for token t. A full score is the sum of the lane's own
 //       registers, and each lane owns distinct (head, token) scores, so the
 //       softmax runs once per score.
 //   P: a lane packs the probabilities of its tokens t and t + 16 into one
 //       16-bit pair and hands them over through a small per-wave LDS area.
 //   PV: O^T[channel][col] = sum_t V^T[channel][t] P~[t][col] with
-//       P~[t][(hl, j)] = p[t][hl] * value_scale[t][group j]; output column
-//       (hl, j) is kept only for channels of group j. Contraction slots 2r and
+//       P~[t][(hl, jr)] = p[t][hl] * value_scale[t][group of the channel
+//       tile] (one P~ per group of the row group); output column (hl, jr) is
+//       kept only for channels of row group jr. Contraction slots 2r and
 //       2r + 1 of lane group q are tokens 4q + r and 4q + r + 16.
 //   The key scale and log2(e)/sqrt(D) are folded into the fp16 query per
 //   32-token key group; key zero points give a per-(head, block) score
@@ -35,6 +38,9 @@
 // conversions, two per instruction: a 2-bit code in the two low bits of a
 // nibble is the e2m1 value code/2, a 4-bit code in the low nibble of a byte
 // is the e4m3 value code * 2^-9, so scales 2 and 2^9 give the code exactly.
+#include <map>
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace vc {
@@ -66,10 +72,6 @@ struct DraftParams {
   const uint16_t* tail_v;
 };
 
-template <int D>
-struct Geo {
-  static constexpr int NG = D / 32, HS = 16 / NG, HPL = 4 / NG, MT = D / 16, CPL = D / 16;
-};
 
 // ---------------------------------------------------------------- codes ----
 template <int BYTE>
@@ -135,15 +137,26 @@ __device__ __forceinline__ void value_operand(const uint32_t (&vw)[VWL], int m, 
   }
 }
 
+// ------------------------------------------------------ head geometry ----
+// W channel groups per MFMA row: NR = NG/W row groups per head, HS = 16/NR
+// query heads per head set, HPL = 4/NR heads per lane row of the score
+// layout, MT = D/16 output channel tiles, CPL = D/16 key channels per lane
+// for the zero-point bias.
+template <int D, int W>
+struct Geo {
+  static constexpr int NG = D / 32, NR = NG / W, HS = 16 / NR, HPL = 4 / NR, MT = D / 16, CPL = D / 16;
+  static_assert(W >= 1 && NG % W == 0, "row width");
+};
+
 // ------------------------------------------------------ softmax state ----
 // m, l: score layout (lane (q, t) owns heads HPL*q + u of each set);
-// zt, acc: PV layout (lane n = (hl, j) owns output column (hl, j)).
-template <int D, int NHS>
+// zt, acc: PV layout (lane n = (hl, jr) owns output column (hl, jr)).
+template <int D, int W, int NHS>
 struct DState {
-  static constexpr int HPL = Geo<D>::HPL, MT = Geo<D>::MT;
+  static constexpr int HPL = Geo<D, W>::HPL, MT = Geo<D, W>::MT;
   float m[NHS][HPL];  // running max, uniform over the lane row
   float l[NHS][HPL];  // this lane's share of sum p
-  float zt[NHS];      // this lane's share of sum p * value zero point (KIVI)
+  float zt[NHS][W];   // this lane's share of sum p * value zero point, per group (KIVI)
   f32x4 acc[NHS][MT];
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -153,7 +166,8 @@ struct DState {
         m[h][u] = kNegInf;
         l[h][u] = 0.f;
       }
-      zt[h] = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) zt[h][w] = 0.f;
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -161,9 +175,9 @@ struct DState {
 };
 
 // Per-wave LDS area for the probability hand-over: [NHS][HS][16] words.
-template <int D, int NHS>
+template <int D, int W, int NHS>
 constexpr int p_area_words() {
-  return NHS * Geo<D>::HS * 16;
+  return NHS * Geo<D, W>::HS * 16;
 }
 
 // Online softmax over one 32-token block of head set h and hand-over of the
@@ -175,12 +189,13 @@ constexpr int p_area_words() {
 // The max only moves when a score exceeds it by more than kRescaleThreshold
 // (so p <= 2^8), which makes the rescale of the accumulators rare; the
 // result is the same softmax.
-template <int D, int NHS, bool BF16>
-__device__ __forceinline__ void soft_block(DState<D, NHS>& st, int h, const float (&s)[Geo<D>::HPL][2],
-                                           const float (&bias)[Geo<D>::HPL], int lane, uint32_t* lds_p,
+template <int D, int W, int NHS, bool BF16>
+__device__ __forceinline__ void soft_block(DState<D, W, NHS>& st, int h, const float (&s)[Geo<D, W>::HPL][2],
+                                           const float (&bias)[Geo<D, W>::HPL], int lane, uint32_t* lds_p,
                                            uint32_t (&P)[4]) {
-  constexpr int NG = Geo<D>::NG, HS = Geo<D>::HS, HPL = Geo<D>::HPL, MT = Geo<D>::MT;
-  const int t = lane & 15, qg = lane >> 4, n = lane & 15, hl = n / NG;
+  using G = Geo<D, W>;
+  constexpr int NR = G::NR, HS = G::HS, HPL = G::HPL, MT = G::MT;
+  const int t = lane & 15, qg = lane >> 4, n = lane & 15, hl = n / NR;
   bool need = false;
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
@@ -197,14 +212,16 @@ __device__ __forceinline__ void soft_block(DState<D, NHS>& st, int h, const floa
       st.m[h][u] = up ? bm : st.m[h][u];
       st.l[h][u] *= alpha[u];
     }
-    // the PV column (hl, j) takes the factor of head hl from lane row hl / HPL
+    // the PV column (hl, jr) takes the factor of head hl from lane row hl / HPL
     const int src = 4 * 16 * (hl / HPL);
     float a = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(alpha[0])));
-    if constexpr (HPL == 2) {
-      const float a1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(alpha[1])));
-      a = (hl & 1) ? a1 : a;
+#pragma unroll
+    for (int u = 1; u < HPL; ++u) {
+      const float au = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(alpha[u])));
+      a = (hl % HPL == u) ? au : a;
     }
-    st.zt[h] *= a;
+#pragma unroll
+    for (int w = 0; w < W; ++w) st.zt[h][w] *= a;
 #pragma unroll
     for (int m = 0; m < MT; ++m) st.acc[h][m] *= a;
   }
@@ -226,57 +243,102 @@ __device__ __forceinline__ void soft_block(DState<D, NHS>& st, int h, const floa
   P[3] = v[3];
 }
 
-// Full scores of the lane's HPL heads from the NG partial rows.
-template <int D>
-__device__ __forceinline__ void row_scores(const f32x4 (&c)[2], float scale, float (&s)[Geo<D>::HPL][2]) {
-  constexpr int NG = Geo<D>::NG, HPL = Geo<D>::HPL;
+// Full scores of the lane's HPL heads from the NR partial rows.
+template <int D, int W>
+__device__ __forceinline__ void row_scores(const f32x4 (&c)[2], float scale, float (&s)[Geo<D, W>::HPL][2]) {
+  constexpr int NR = Geo<D, W>::NR, HPL = Geo<D, W>::HPL;
 #pragma unroll
   for (int u = 0; u < HPL; ++u)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      float x = c[i][NG * u];
+      float x = c[i][NR * u];
 #pragma unroll
-      for (int jj = 1; jj < NG; ++jj) x += c[i][NG * u + jj];
+      for (int jj = 1; jj < NR; ++jj) x += c[i][NR * u + jj];
       s[u][i] = x * scale;
     }
 }
 
 // ------------------------------------------------------- KIVI body block ----
-// Buffer resources of one (sequence, KV head) unit; per-block offsets go in
-// the scalar offset, so the loop does no vector address arithmetic. Loads
-// past a unit's extent return zero.
+// Each wave streams its own 32-token blocks into a private 3-stage LDS ring
+// with direct-to-LDS buffer loads issued two blocks ahead, then reads its
+// operands from LDS. One stage holds a block's six pieces back to back.
+template <int D, int BITS>
+struct BlockLayout {
+  static constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64;
+  static constexpr int KC = 0, KC_B = 32 * WPT * 4;        // key codes, token-major
+  static constexpr int VC = KC + KC_B, VC_B = 64 * VWL * 4; // value codes, lane-major
+  static constexpr int KS = VC + VC_B, KS_B = D * 2;        // key scales / zeros
+  static constexpr int KZ = KS + KS_B;
+  static constexpr int VS = KZ + KS_B, VS_B = NG * 32 * 2;  // value scales / zeros
+  static constexpr int VZ = VS + VS_B;
+  static constexpr int BYTES = VZ + VS_B;
+  // direct-to-LDS instructions per piece: 1 KB (16 B per lane), then 256 B
+  // (4 B per lane), then a 128 B rest (4 B for half the lanes)
+  static constexpr int pieces(int b) { return b / 1024 + (b % 1024) / 256 + ((b % 256) ? 1 : 0); }
+  static constexpr int NI = pieces(KC_B) + pieces(VC_B) + 2 * pieces(KS_B) + 2 * pieces(VS_B);
+  static_assert(KC_B % 128 == 0 && VC_B % 128 == 0 && KS_B % 128 == 0 && VS_B % 128 == 0, "128-byte pieces");
+};
+
+// s_waitcnt on the vector-memory counter only: vmcnt(N), others untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Copy BYTES from global byte offset soff of r to dst (wave-uniform).
+template <int BYTES>
+__device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* dst, int soff, int lane) {
+  constexpr int N1K = BYTES / 1024, N256 = (BYTES % 1024) / 256, R128 = BYTES % 256;
+#pragma unroll
+  for (int i = 0; i < N1K; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, lane * 16, soff + i * 1024, 0, 0);
+#pragma unroll
+  for (int i = 0; i < N256; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + N1K * 1024 + i * 256), 4, lane * 4,
+                                             soff + N1K * 1024 + i * 256, 0, 0);
+  if constexpr (R128 != 0) {
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + N1K * 1024 + N256 * 256), 4, lane * 4,
+                                               soff + N1K * 1024 + N256 * 256, 0, 0);
+  }
+}
+
+// The unit's six arrays.
 struct KiviRes {
   __amdgpu_buffer_rsrc_t kc, ks, kz, vc, vs, vz;
 };
-constexpr int kRsrcWord3 = 0x00020000;
-
-template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
 
 template <int D, int BITS>
-struct KiviRaw {
-  static constexpr int NWL = D * BITS / 128, VWL = D * BITS / 64, CPL = Geo<D>::CPL;
-  uint32_t kw[2][NWL];   // key codes of tokens t and t + 16
-  uint32_t vw[VWL];      // value codes of the lane's slots
-  uint32_t ks[4];        // key scales of the lane's 8-channel run
-  uint32_t kz[CPL / 2];  // key zero points of channels CPL*t ..
-  u32x4 vs, vz;          // value scales / zeros of the lane's 8 slots
-};
+__device__ __forceinline__ void issue_block(char* dst, const KiviRes& res, int blk, int lane) {
+  using BL = BlockLayout<D, BITS>;
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  dma_piece<BL::KC_B>(res.kc, dst + BL::KC, blk * BL::KC_B, lane);
+  dma_piece<BL::VC_B>(res.vc, dst + BL::VC, blk * BL::VC_B, lane);
+  dma_piece<BL::KS_B>(res.ks, dst + BL::KS, blk * BL::KS_B, lane);
+  dma_piece<BL::KS_B>(res.kz, dst + BL::KZ, blk * BL::KS_B, lane);
+  dma_piece<BL::VS_B>(res.vs, dst + BL::VS, blk * BL::VS_B, lane);
+  dma_piece<BL::VS_B>(res.vz, dst + BL::VZ, blk * BL::VS_B, lane);
+}
 
 template <int N>
-__device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* w) {
+__device__ __forceinline__ void lds_words(const char* p, uint32_t* w) {
   if constexpr (N == 1) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
   } else if constexpr (N == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
     w[0] = v[0];
     w[1] = v[1];
   } else {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, 0);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p + 4 * i);
       w[i] = v[0];
       w[i + 1] = v[1];
       w[i + 2] = v[2];
@@ -285,95 +347,97 @@ __device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, int voff, in
   }
 }
 
-// Lane-constant byte offsets into the unit's arrays.
-struct KiviOffs {
-  int kc0, kc1, ksc, kzc, vc, vsd;
+template <int D, int BITS, int W>
+struct KiviRaw {
+  static constexpr int NWL = D * BITS / 128, VWL = D * BITS / 64, CPL = Geo<D, W>::CPL;
+  uint32_t kw[2][NWL];   // key codes of tokens t and t + 16
+  uint32_t vw[VWL];      // value codes of the lane's slots
+  uint32_t ks[4 * W];    // key scales of the lane's W 8-channel runs
+  uint32_t kz[CPL / 2];  // key zero points of channels CPL*t ..
+  u32x4 vs[W], vz[W];    // value scales / zeros of the lane's 8 slots, per group
 };
 
-template <int D, int BITS>
-__device__ __forceinline__ KiviOffs kivi_offsets(int lane) {
-  constexpr int NG = D / 32, WPT = D * BITS / 32, NWL = D * BITS / 128, VWL = D * BITS / 64, CPL = D / 16;
-  const int n = lane & 15, qg = lane >> 4, j = n % NG;
-  KiviOffs o;
-  o.kc0 = (n * WPT + qg * NWL) * 4;
-  o.kc1 = ((16 + n) * WPT + qg * NWL) * 4;
-  o.ksc = 8 * (qg * NG + j) * 2;
-  o.kzc = CPL * n * 2;
-  o.vc = lane * VWL * 4;
-  o.vsd = (j * 32 + qg * 8) * 2;
-  return o;
+// The lane's operands of one staged block.
+template <int D, int BITS, int W>
+__device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* blk, int lane) {
+  using BL = BlockLayout<D, BITS>;
+  constexpr int NG = D / 32, NR = NG / W, WPT = BL::WPT, NWL = KiviRaw<D, BITS, W>::NWL, VWL = BL::VWL;
+  constexpr int CPL = D / 16;
+  const int n = lane & 15, qg = lane >> 4, jr = n % NR;
+  lds_words<NWL>(blk + BL::KC + (n * WPT + qg * NWL) * 4, r.kw[0]);
+  lds_words<NWL>(blk + BL::KC + ((16 + n) * WPT + qg * NWL) * 4, r.kw[1]);
+  lds_words<VWL>(blk + BL::VC + lane * VWL * 4, r.vw);
+  lds_words<4 * W>(blk + BL::KS + (qg * NG + W * jr) * 16, r.ks);
+  lds_words<CPL / 2>(blk + BL::KZ + CPL * n * 2, r.kz);
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    uint32_t t[4];
+    lds_words<4>(blk + BL::VS + ((W * jr + w) * 32 + qg * 8) * 2, t);
+    r.vs[w] = u32x4{t[0], t[1], t[2], t[3]};
+    lds_words<4>(blk + BL::VZ + ((W * jr + w) * 32 + qg * 8) * 2, t);
+    r.vz[w] = u32x4{t[0], t[1], t[2], t[3]};
+  }
 }
 
-template <int D, int BITS>
-__device__ __forceinline__ void kivi_load(KiviRaw<D, BITS>& r, const KiviRes& res, const KiviOffs& o, int blk) {
-  constexpr int NG = D / 32, WPT = D * BITS / 32, NWL = D * BITS / 128, VWL = D * BITS / 64, CPL = D / 16;
-  // blk is wave-uniform; the scalar offsets must live in SGPRs
-  blk = __builtin_amdgcn_readfirstlane(blk);
-  const int skc = blk * 32 * WPT * 4, sks = blk * D * 2, svc = blk * 64 * VWL * 4, svs = blk * NG * 32 * 2;
-  buf_words<NWL>(res.kc, o.kc0, skc, r.kw[0]);
-  buf_words<NWL>(res.kc, o.kc1, skc, r.kw[1]);
-  buf_words<VWL>(res.vc, o.vc, svc, r.vw);
-  buf_words<4>(res.ks, o.ksc, sks, r.ks);
-  buf_words<CPL / 2>(res.kz, o.kzc, sks, r.kz);
-  uint32_t t[4];
-  buf_words<4>(res.vs, o.vsd, svs, t);
-  r.vs = u32x4{t[0], t[1], t[2], t[3]};
-  buf_words<4>(res.vz, o.vsd, svs, t);
-  r.vz = u32x4{t[0], t[1], t[2], t[3]};
-}
-
-// Query data of one wave, fixed over the body.
-//   qf: PV/A layout, lane (q, (hl, j)): q[h*HS + hl][8(q*NG + j) + kperm(s)]
-//       * log2(e)/sqrt(D), zero for padding heads;
+// Query data of one wave, fixed over the body (one head set, g <= HS).
+//   qp: A layout, lane (q, (hl, jr)), run w = K-step W*jr + w: fp16 pairs
+//       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)] *
+//       log2(e)/sqrt(D), zero for padding heads;
 //   qh, ql: score layout, lane (q, t): the same scaled query of head
-//       h*HS + HPL*q + u at channels CPL*t + 2p, + 1, split into an fp16
-//       pair and the fp16 pair of its remainder.
-template <int D, int NHS>
+//       HPL*q + u at channels CPL*t + 2p, + 1, split into an fp16 pair and
+//       the fp16 pair of its remainder.
+template <int D, int W>
 struct KiviQuery {
-  static constexpr int HPL = Geo<D>::HPL, CPL = Geo<D>::CPL;
-  float qf[NHS][8];
-  uint32_t qh[NHS][HPL][CPL / 2], ql[NHS][HPL][CPL / 2];
+  static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL;
+  uint32_t qp[W][4];
+  uint32_t qh[HPL][CPL / 2], ql[HPL][CPL / 2];
 };
 
-template <int D, int NHS>
-__device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, int lane, KiviQuery<D, NHS>& Q) {
-  constexpr int NG = Geo<D>::NG, HS = Geo<D>::HS, HPL = Geo<D>::HPL, CPL = Geo<D>::CPL;
-  const int n = lane & 15, qg = lane >> 4, j = n % NG, hl = n / NG;
+template <int D, int W>
+__device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, int lane, KiviQuery<D, W>& Q) {
+  using G = Geo<D, W>;
+  constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, CPL = G::CPL;
+  const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
   const uint16_t* qb = P.q + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
+  const bool ok = hl < P.g;
 #pragma unroll
-  for (int h = 0; h < NHS; ++h) {
-    const int head = h * HS + hl;
-    const bool ok = head < P.g;
+  for (int w = 0; w < W; ++w)
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      Q.qf[h][s] = ok ? bf16_bits_to_f32(qb[(size_t)head * D + 8 * (qg * NG + j) + kperm(s)]) * P.qscale : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      float x[2];
 #pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      const int hb = h * HS + HPL * qg + u;
-      const bool okb = hb < P.g;
+      for (int e = 0; e < 2; ++e)
+        x[e] = ok ? bf16_bits_to_f32(qb[(size_t)hl * D + 8 * (qg * NG + W * jr + w) + kperm(2 * r + e)]) * P.qscale
+                  : 0.f;
+      Q.qp[w][r] = pack_f16(x[0], x[1]);
+    }
 #pragma unroll
-      for (int p = 0; p < CPL / 2; ++p) {
-        float x[2], hi[2], lo[2];
+  for (int u = 0; u < HPL; ++u) {
+    const int hb = HPL * qg + u;
+    const bool okb = hb < P.g;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          x[e] = okb ? bf16_bits_to_f32(qb[(size_t)hb * D + CPL * n + 2 * p + e]) * P.qscale : 0.f;
-          hi[e] = (float)(_Float16)x[e];
-          lo[e] = x[e] - hi[e];
-        }
-        Q.qh[h][u][p] = pack_f16(hi[0], hi[1]);
-        Q.ql[h][u][p] = pack_f16(lo[0], lo[1]);
+    for (int p = 0; p < CPL / 2; ++p) {
+      float x[2], hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        x[e] = okb ? bf16_bits_to_f32(qb[(size_t)hb * D + CPL * n + 2 * p + e]) * P.qscale : 0.f;
+        hi[e] = (float)(_Float16)x[e];
+        lo[e] = x[e] - hi[e];
       }
+      Q.qh[u][p] = pack_f16(hi[0], hi[1]);
+      Q.ql[u][p] = pack_f16(lo[0], lo[1]);
     }
   }
 }
 
 // One 32-token block of the quantised body.
-template <int D, int BITS, int NHS>
-__device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS>& raw, int lane, const KiviQuery<D, NHS>& Q,
-                                             DState<D, NHS>& st, uint32_t* lds_p) {
-  constexpr int NG = Geo<D>::NG, HPL = Geo<D>::HPL, MT = Geo<D>::MT, CPL = Geo<D>::CPL;
-  constexpr int NWL = KiviRaw<D, BITS>::NWL, VWL = KiviRaw<D, BITS>::VWL;
-  const int n = lane & 15, j = n % NG;
+template <int D, int BITS, int W>
+__device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int lane, const KiviQuery<D, W>& Q,
+                                             DState<D, W, 1>& st, uint32_t* lds_p) {
+  using G = Geo<D, W>;
+  constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, MT = G::MT, CPL = G::CPL;
+  constexpr int NWL = KiviRaw<D, BITS, W>::NWL, VWL = KiviRaw<D, BITS, W>::VWL;
+  const int n = lane & 15, jr = n % NR;
 
   // key operands of both token tiles, all K-steps
   uint32_t Bk[2][NG][4];
@@ -382,91 +446,90 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS>& raw, int la
 #pragma unroll
     for (int kk = 0; kk < NG; ++kk) key_operand<BITS, NWL>(raw.kw[i], kk, Bk[i][kk]);
 
-  uint32_t vs[4], vz[4];
+  // query with the key scales of this lane's runs folded in: register r of
+  // run w pairs run channels kperm(2r), kperm(2r + 1), i.e. the low (r even)
+  // or high (r odd) halves of scale words 4w + 2(r >> 1) and the next one
+  uint32_t Aq[W][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    vs[r] = raw.vs[r];
-    vz[r] = raw.vz[r];
-  }
-
-  uint32_t Pv[NHS][4];
-#pragma unroll
-  for (int h = 0; h < NHS; ++h) {
-    // query with the key scales of this lane's run folded in (one rounding)
-    uint32_t Aq[4];
+  for (int w = 0; w < W; ++w)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t w0 = raw.ks[2 * (r >> 1)], w1 = raw.ks[2 * (r >> 1) + 1];
-      const float s0 = (r & 1) ? f16_hi(w0) : f16_lo(w0);
-      const float s1 = (r & 1) ? f16_hi(w1) : f16_lo(w1);
-      Aq[r] = pack_f16(Q.qf[h][2 * r] * s0, Q.qf[h][2 * r + 1] * s1);
+      const uint32_t w0 = raw.ks[4 * w + 2 * (r >> 1)], w1 = raw.ks[4 * w + 2 * (r >> 1) + 1];
+      const uint32_t sp = __builtin_amdgcn_perm(w1, w0, (r & 1) ? 0x07060302u : 0x05040100u);
+      Aq[w][r] = as_u32(as_f16x2(Q.qp[w][r]) * as_f16x2(sp));
     }
-    // zero-point bias of the lane's heads: sum over channels CPL*t .. and the row
-    float bias[HPL];
+  // zero-point bias of the lane's heads: sum over channels CPL*t .. and the
+  // row (two independent accumulation chains)
+  float bias[HPL];
 #pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      float x = 0.f;
+  for (int u = 0; u < HPL; ++u) {
+    float xh = 0.f, xl = 0.f;
 #pragma unroll
-      for (int p = 0; p < CPL / 2; ++p) {
-        x = __builtin_amdgcn_fdot2(as_f16x2(Q.qh[h][u][p]), as_f16x2(raw.kz[p]), x, false);
-        x = __builtin_amdgcn_fdot2(as_f16x2(Q.ql[h][u][p]), as_f16x2(raw.kz[p]), x, false);
-      }
-      bias[u] = row_sum16(x);
+    for (int p = 0; p < CPL / 2; ++p) {
+      xh = __builtin_amdgcn_fdot2(as_f16x2(Q.qh[u][p]), as_f16x2(raw.kz[p]), xh, false);
+      xl = __builtin_amdgcn_fdot2(as_f16x2(Q.ql[u][p]), as_f16x2(raw.kz[p]), xl, false);
     }
-    f32x4 c[2];
+    bias[u] = row_sum16(xh + xl);
+  }
+  f32x4 c[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i) {
+    c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NG; ++kk) {
-        const bool on = (j == kk);
-        const u32x4 a = {on ? Aq[0] : 0u, on ? Aq[1] : 0u, on ? Aq[2] : 0u, on ? Aq[3] : 0u};
-        c[i] = mfma_f16(a, u32x4{Bk[i][kk][0], Bk[i][kk][1], Bk[i][kk][2], Bk[i][kk][3]}, c[i]);
-      }
-    }
-    float s[HPL][2];
-    row_scores<D>(c, 1.f, s);
-    uint32_t Pp[4];
-    soft_block<D, NHS, false>(st, h, s, bias, lane, lds_p, Pp);
-    // value scales into P~, value zero points into zt
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t pr = Pp[r];
-      st.zt[h] = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(vz[r]), st.zt[h], false);
-      Pv[h][r] = as_u32(as_f16x2(pr) * as_f16x2(vs[r]));
+    for (int kk = 0; kk < NG; ++kk) {
+      const bool on = (jr == kk / W);
+      const uint32_t* a = Aq[kk % W];
+      const u32x4 av = {on ? a[0] : 0u, on ? a[1] : 0u, on ? a[2] : 0u, on ? a[3] : 0u};
+      c[i] = mfma_f16(av, u32x4{Bk[i][kk][0], Bk[i][kk][1], Bk[i][kk][2], Bk[i][kk][3]}, c[i]);
     }
   }
+  float s[HPL][2];
+  row_scores<D, W>(c, 1.f, s);
+  uint32_t Pp[4];
+  soft_block<D, W, 1, false>(st, 0, s, bias, lane, lds_p, Pp);
+  // value scales into P~ (one per channel group of the column), value zero
+  // points into zt
+  uint32_t Pv[W][4];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t pr = Pp[r], zw = raw.vz[w][r], sw = raw.vs[w][r];
+      st.zt[0][w] = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(zw), st.zt[0][w], false);
+      Pv[w][r] = as_u32(as_f16x2(pr) * as_f16x2(sw));
+    }
 
-  // ---- PV ----
+  // ---- PV: channel tile m belongs to group m/2, i.e. run (m/2) % W of the column ----
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     uint32_t A[4];
     value_operand<BITS, VWL>(raw.vw, m, A);
-#pragma unroll
-    for (int h = 0; h < NHS; ++h)
-      st.acc[h][m] = mfma_f16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Pv[h][0], Pv[h][1], Pv[h][2], Pv[h][3]},
-                              st.acc[h][m]);
+    const uint32_t* pv = Pv[(m >> 1) % W];
+    st.acc[0][m] = mfma_f16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{pv[0], pv[1], pv[2], pv[3]}, st.acc[0][m]);
   }
 }
 
 // ------------------------------------------------ unquantised row block ----
 // A 32-token block of 16-bit rows (fp16 KIVI tail, or bf16 rows for token
-// drop / dense). rows.k(t) / rows.v(t) give the row pointers of token
-// t < nvalid. Aqm[h][kk] is the unscaled query operand of K-step kk (exact
-// in fp16 and bf16, zero unless kk is the lane's group); scores are scaled
-// by log2(e)/sqrt(D) after the MFMA.
-// lds: this wave's staging area, 32 rows of D halfs with a stride of D + 4.
-template <int D, int NHS, bool BF16, typename RowFn>
+// drop / dense), W = 1 rows. rows.k(t) / rows.v(t) give the row pointers of
+// token t < nvalid. Aqm[h][kk] is the unscaled query operand of K-step kk
+// (exact in fp16 and bf16, zero unless kk is the lane's group); scores are
+// scaled by log2(e)/sqrt(D) after the MFMA.
+// lds: this wave's staging area, 32 rows of D halfs with a stride of D + 4
+// (STAGE); without STAGE the V^T operand is gathered from global memory with
+// 16-bit loads (the short unquantised tail of the KIVI cache).
+template <int D, int W, int NHS, bool BF16, bool STAGE, typename RowFn>
 __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lane, float qscale,
-                                          const uint32_t (&Aqm)[NHS][D / 32][4], DState<D, NHS>& st,
+                                          const uint32_t (&Aqm)[NHS][D / 32][4], DState<D, W, NHS>& st,
                                           uint16_t* lds, uint32_t* lds_p) {
-  constexpr int NG = Geo<D>::NG, HPL = Geo<D>::HPL, MT = Geo<D>::MT, LSTR = D + 4;
+  using G = Geo<D, W>;
+  constexpr int NG = G::NG, HPL = G::HPL, MT = G::MT, LSTR = D + 4;
   const int n = lane & 15, qg = lane >> 4;
 
   // ---- stage V rows in LDS (invalid rows as zeros) ----
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  {
+  if constexpr (STAGE) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;
 #pragma unroll
@@ -514,14 +577,14 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
                             u32x4{Bk[i][kk][0], Bk[i][kk][1], Bk[i][kk][2], Bk[i][kk][3]}, c[i]);
     }
     float s[HPL][2];
-    row_scores<D>(c, qscale, s);
+    row_scores<D, W>(c, qscale, s);
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
       if (n >= nvalid) s[u][0] = kNegInf;
       if (16 + n >= nvalid) s[u][1] = kNegInf;
     }
     const float bias[HPL] = {};
-    soft_block<D, NHS, BF16>(st, h, s, bias, lane, lds_p, Pv[h]);
+    soft_block<D, W, NHS, BF16>(st, h, s, bias, lane, lds_p, Pv[h]);
   }
 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -531,8 +594,15 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     uint32_t A[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t lo = lds[(4 * qg + r) * LSTR + 16 * m + n];
-      const uint32_t hi = lds[(16 + 4 * qg + r) * LSTR + 16 * m + n];
+      uint32_t lo, hi;
+      if constexpr (STAGE) {
+        lo = lds[(4 * qg + r) * LSTR + 16 * m + n];
+        hi = lds[(16 + 4 * qg + r) * LSTR + 16 * m + n];
+      } else {
+        const int t0 = 4 * qg + r, t1 = 16 + 4 * qg + r;
+        lo = t0 < nvalid ? rows.v(t0)[16 * m + n] : 0u;
+        hi = t1 < nvalid ? rows.v(t1)[16 * m + n] : 0u;
+      }
       A[r] = lo | (hi << 16);
     }
 #pragma unroll
@@ -542,12 +612,12 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
   }
 }
 
-// Unscaled query operands of the row path, one per K-step (zero unless the
-// step is the lane's channel group).
+// Unscaled query operands of the row path (W = 1), one per K-step (zero
+// unless the step is the lane's channel group).
 template <int D, int NHS, bool BF16>
 __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, int lane,
                                           uint32_t (&Aqm)[NHS][D / 32][4]) {
-  constexpr int NG = Geo<D>::NG, HS = Geo<D>::HS;
+  constexpr int NG = Geo<D, 1>::NG, HS = Geo<D, 1>::HS;
   const int n = lane & 15, qg = lane >> 4, j = n % NG, hl = n / NG;
   const uint16_t* qb = P.q + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
 #pragma unroll
@@ -575,35 +645,37 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
 // kernel: a merge by the last workgroup to finish would need a device-scope
 // release and acquire in every workgroup, which on a part whose L2 is split
 // per XCD means an L2 writeback and invalidate each.
-template <int D, int NHS>
+template <int D, int W, int NHS>
 __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int hk, int split, int lane, int wave,
-                                              DState<D, NHS>& st, bool has_zero, float* lds) {
-  constexpr int NG = Geo<D>::NG, HS = Geo<D>::HS, HPL = Geo<D>::HPL, NH = NHS * HS;
-  const int n = lane & 15, qg = lane >> 4, j = n % NG, hl = n / NG;
+                                              DState<D, W, NHS>& st, bool has_zero, float* lds) {
+  using G = Geo<D, W>;
+  constexpr int NR = G::NR, HS = G::HS, HPL = G::HPL, NH = NHS * HS;
+  const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
   float* lds_o = lds;
   float* lds_ml = lds + kWaves * NH * D;
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < NHS; ++h) {
-    const float zt = has_zero ? sum_q(st.zt[h]) : 0.f;
     const int head = h * HS + hl;
     float* o = lds_o + ((size_t)wave * NH + head) * D;
-    // column (hl, j) is valid for the two channel tiles of group j. The tile
-    // index is lane-dependent, so the values are picked with selects: an
-    // indexed access (or branches the compiler folds into one) would move the
-    // accumulators to scratch memory.
+    // column (hl, jr) is valid for the 2W channel tiles of row group jr. The
+    // tile index is lane-dependent, so the values are picked with selects:
+    // an indexed access (or branches the compiler folds into one) would move
+    // the accumulators to scratch memory.
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+    for (int mm = 0; mm < 2 * W; ++mm) {
+      const float zt = has_zero ? sum_q(st.zt[h][mm >> 1]) : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = st.acc[h][mm][r];
 #pragma unroll
-        for (int jj = 1; jj < NG; ++jj) {
-          const float w = st.acc[h][2 * jj + mm][r];
-          v = (j == jj) ? w : v;
+        for (int jj = 1; jj < NR; ++jj) {
+          const float x = st.acc[h][2 * W * jj + mm][r];
+          v = (jr == jj) ? x : v;
         }
-        o[16 * (2 * j + mm) + 4 * qg + r] = v + zt;
+        o[16 * (2 * W * jr + mm) + 4 * qg + r] = v + zt;
       }
+    }
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
       const float l = row_sum16(st.l[h][u]);
@@ -660,38 +732,60 @@ struct SourceRows {
   __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)pos(t) * D; }
 };
 
-// LDS: the row staging area (aliased by the wave merge), then the per-wave
-// probability hand-over areas.
+// LDS of the row kernel: the row staging area (aliased by the wave merge),
+// then the per-wave probability hand-over areas.
 template <int D, int NHS>
 constexpr size_t draft_stage_bytes() {
-  constexpr int NH = NHS * Geo<D>::HS;
+  constexpr int NH = NHS * Geo<D, 1>::HS;
   constexpr size_t part = (size_t)kWaves * NH * (D + 2) * sizeof(float);
   constexpr size_t rows = (size_t)kWaves * 32 * (D + 4) * sizeof(uint16_t);
   return part > rows ? part : rows;
 }
 template <int D, int NHS>
 constexpr size_t draft_lds_bytes() {
-  return draft_stage_bytes<D, NHS>() + (size_t)kWaves * p_area_words<D, NHS>() * sizeof(uint32_t);
+  return draft_stage_bytes<D, NHS>() + (size_t)kWaves * p_area_words<D, 1, NHS>() * sizeof(uint32_t);
 }
 
 // ---------------------------------------------------------------- kernels ----
-template <int D, int BITS, int NHS>
-__global__ __launch_bounds__(256) void draft_kivi_kernel(const DraftParams P) {
-  constexpr int NG = Geo<D>::NG, WPT = D * BITS / 32, VWL = D * BITS / 64;
-  __shared__ __attribute__((aligned(16))) char smem[draft_lds_bytes<D, NHS>()];
+// LDS of the KIVI kernel: three ring stages (one per variable, so the
+// compiler can tell which pending direct-to-LDS loads a read depends on; the
+// first also hosts the wave merge at the end), then the probability areas.
+template <int D, int BITS, int W>
+struct KiviLds {
+  static constexpr int STAGE = kWaves * BlockLayout<D, BITS>::BYTES;
+  static constexpr int MERGE = kWaves * Geo<D, W>::HS * (D + 2) * 4;
+  static constexpr int STAGE0 = STAGE > MERGE ? STAGE : MERGE;
+};
+
+// Waves per SIMD to plan registers for (wider rows hold more heads per lane).
+template <int D, int W>
+constexpr int kivi_min_waves() {
+  return W == 1 ? 4 : (Geo<D, W>::NR > 1 ? 2 : 1);
+}
+
+// KIVI body + fp16 tail, one head set of HS = 16*W/NG >= g query heads.
+template <int D, int BITS, int W>
+__global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kernel(const DraftParams P) {
+  constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64;
+  using BL = BlockLayout<D, BITS>;
+  using LL = KiviLds<D, BITS, W>;
+  __shared__ __attribute__((aligned(16))) char rs0[LL::STAGE0];
+  __shared__ __attribute__((aligned(16))) char rs1[LL::STAGE];
+  __shared__ __attribute__((aligned(16))) char rs2[LL::STAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t parea[kWaves * p_area_words<D, W, 1>()];
   // the wave index is uniform across the wave; saying so keeps the per-block
-  // buffer offsets in SGPRs (no waterfall loops around the loads)
+  // offsets in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
-  uint32_t* lds_p = reinterpret_cast<uint32_t*>(smem + draft_stage_bytes<D, NHS>()) + wave * p_area_words<D, NHS>();
+  uint32_t* lds_p = parea + wave * p_area_words<D, W, 1>();
 
-  DState<D, NHS> st;
+  DState<D, W, 1> st;
   st.init();
   const bool tail_split = (split == P.S - 1);
   if (!tail_split) {
-    KiviQuery<D, NHS> Q;
-    kivi_query<D, NHS>(P, b, hk, lane, Q);
+    KiviQuery<D, W> Q;
+    kivi_query<D, W>(P, b, hk, lane, Q);
     const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;
     const int b0 = (split * kWaves + wave) * P.bpw;
     const int b1 = min(b0 + P.bpw, nblk);
@@ -704,36 +798,55 @@ __global__ __launch_bounds__(256) void draft_kivi_kernel(const DraftParams P) {
       res.vc = make_rsrc(P.v_codes + unit * nbc * 64 * VWL, nbc * 64 * VWL * 4);
       res.vs = make_rsrc(P.v_scale + unit * nbc * NG * 32, nbc * NG * 32 * 2);
       res.vz = make_rsrc(P.v_zero + unit * nbc * NG * 32, nbc * NG * 32 * 2);
-      const KiviOffs offs = kivi_offsets<D, BITS>(lane);
-      // two register sets in ping-pong: the loads of block i+1 are in flight
-      // while block i is computed. The loads are unconditional (the index is
-      // clamped to the wave's last block, a cache hit) so that no register
-      // copy has to wait for a load that was just issued.
+      char* w0 = rs0 + wave * BL::BYTES;
+      char* w1 = rs1 + wave * BL::BYTES;
+      char* w2 = rs2 + wave * BL::BYTES;
+      // three-stage ring, two blocks in flight ahead of the one computed.
+      // Past the wave's last block the last one is loaded again (into a stage
+      // that is not read), which keeps every wait count constant. (The
+      // compiler adds a stricter wait after the loop header, where it loses
+      // track of which stage the pending loads write.)
       const int last = b1 - 1;
-      KiviRaw<D, BITS> ra, rb;
-      kivi_load<D, BITS>(ra, res, offs, b0);
-      for (int blk = b0;; blk += 2) {
-        kivi_load<D, BITS>(rb, res, offs, min(blk + 1, last));
-        kivi_compute<D, BITS, NHS>(ra, lane, Q, st, lds_p);
+      auto step = [&](const char* stage) {
+        wait_vm<2 * BL::NI>();
+        KiviRaw<D, BITS, W> raw;
+        kivi_read<D, BITS, W>(raw, stage, lane);
+        kivi_compute<D, BITS, W>(raw, lane, Q, st, lds_p);
+      };
+      issue_block<D, BITS>(w0, res, b0, lane);
+      issue_block<D, BITS>(w1, res, min(b0 + 1, last), lane);
+      for (int blk = b0;; blk += 3) {
+        issue_block<D, BITS>(w2, res, min(blk + 2, last), lane);
+        step(w0);
         if (blk + 1 > last) break;
-        kivi_load<D, BITS>(ra, res, offs, min(blk + 2, last));
-        kivi_compute<D, BITS, NHS>(rb, lane, Q, st, lds_p);
+        issue_block<D, BITS>(w0, res, min(blk + 3, last), lane);
+        step(w1);
         if (blk + 2 > last) break;
+        issue_block<D, BITS>(w1, res, min(blk + 4, last), lane);
+        step(w2);
+        if (blk + 3 > last) break;
       }
+      wait_vm<0>();
     }
   } else {
-    uint32_t Aqm[NHS][D / 32][4];
-    row_query<D, NHS, false>(P, b, hk, lane, Aqm);
+    // the fp16 tail with one-group rows: a separate state whose head set
+    // covers the same heads, folded into st below
+    constexpr int NHS1 = (Geo<D, W>::HS + Geo<D, 1>::HS - 1) / Geo<D, 1>::HS;
+    DState<D, 1, NHS1> st1;
+    st1.init();
+    uint32_t Aqm[NHS1][D / 32][4];
+    row_query<D, NHS1, false>(P, b, hk, lane, Aqm);
     const int nt = min(max(P.tail_len[b], 0), P.tail_cap);
     const uint16_t* tk = P.tail_k + unit * P.tail_cap * D;
     const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
-    uint16_t* my_lds = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 4);
     for (int blk = wave; blk * 32 < nt; blk += kWaves) {
       const PlainRows<D> rows{tk + (size_t)blk * 32 * D, tv + (size_t)blk * 32 * D};
-      row_block<D, NHS, false>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+      row_block<D, 1, NHS1, false, false>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, nullptr, lds_p);
     }
+    store_partial<D, 1, NHS1>(P, b, hk, split, lane, wave, st1, false, reinterpret_cast<float*>(rs0));
+    return;
   }
-  store_partial<D, NHS>(P, b, hk, split, lane, wave, st, !tail_split, reinterpret_cast<float*>(smem));
+  store_partial<D, W, 1>(P, b, hk, split, lane, wave, st, true, reinterpret_cast<float*>(rs0));
 }
 
 // Token-drop (GATHER) and dense draft caches: bf16 rows everywhere.
@@ -743,9 +856,10 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
-  uint32_t* lds_p = reinterpret_cast<uint32_t*>(smem + draft_stage_bytes<D, NHS>()) + wave * p_area_words<D, NHS>();
+  uint32_t* lds_p =
+      reinterpret_cast<uint32_t*>(smem + draft_stage_bytes<D, NHS>()) + wave * p_area_words<D, 1, NHS>();
 
-  DState<D, NHS> st;
+  DState<D, 1, NHS> st;
   st.init();
   uint32_t Aqm[NHS][D / 32][4];
   row_query<D, NHS, true>(P, b, hk, lane, Aqm);
@@ -760,7 +874,7 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
     const int32_t* kept = GATHER ? P.kept_idx + unit * (size_t)P.body_cap : nullptr;
     for (int blk = b0; blk < b1; ++blk) {
       const SourceRows<D, GATHER> rows{sk, sv, kept, blk * 32, P.src_t_cap};
-      row_block<D, NHS, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+      row_block<D, 1, NHS, true, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
     }
   } else {
     const int nt = min(max(P.tail_len[b], 0), P.tail_cap);
@@ -768,10 +882,10 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
     const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
     for (int blk = wave; blk * 32 < nt; blk += kWaves) {
       const PlainRows<D> rows{tk + (size_t)blk * 32 * D, tv + (size_t)blk * 32 * D};
-      row_block<D, NHS, true>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+      row_block<D, 1, NHS, true, true>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
     }
   }
-  store_partial<D, NHS>(P, b, hk, split, lane, wave, st, false, reinterpret_cast<float*>(smem));
+  store_partial<D, 1, NHS>(P, b, hk, split, lane, wave, st, false, reinterpret_cast<float*>(smem));
 }
 
 // Merge the splits of one (sequence, query head) in split order, so the
@@ -796,34 +910,89 @@ __global__ __launch_bounds__(D) void draft_merge_kernel(const DraftParams P) {
   P.out[((size_t)b * P.Hq + hq) * D + c] = (L > 0.f) ? O / L : 0.f;
 }
 
+// Head sets of the row kernel (W = 1).
 template <int D>
 int pick_nhs(int g) {
-  constexpr int HS = 16 / (D / 32);
+  constexpr int HS = Geo<D, 1>::HS;
   return (g + HS - 1) / HS;
 }
+// Row width of the KIVI kernel: the narrowest W whose head set holds g heads.
+template <int D>
+int pick_w(int g) {
+  constexpr int NG = D / 32;
+  int w = 1;
+  while (w < NG && 16 * w / NG < g) w *= 2;
+  return w;
+}
+
+using DraftKernel = void (*)(DraftParams);
 
 template <int D, int BITS>
-void launch_kivi(const DraftParams& P, dim3 grid, hipStream_t s) {
-  switch (pick_nhs<D>(P.g)) {
-    case 1: hipLaunchKernelGGL((draft_kivi_kernel<D, BITS, 1>), grid, dim3(256), 0, s, P); break;
-    case 2: hipLaunchKernelGGL((draft_kivi_kernel<D, BITS, 2>), grid, dim3(256), 0, s, P); break;
-    case 3: hipLaunchKernelGGL((draft_kivi_kernel<D, BITS, 3>), grid, dim3(256), 0, s, P); break;
-    default: hipLaunchKernelGGL((draft_kivi_kernel<D, BITS, 4>), grid, dim3(256), 0, s, P); break;
+DraftKernel kivi_kernel_for(int w) {
+  if constexpr (D == 128) {
+    switch (w) {
+      case 1: return draft_kivi_kernel<D, BITS, 1>;
+      case 2: return draft_kivi_kernel<D, BITS, 2>;
+      default: return draft_kivi_kernel<D, BITS, 4>;
+    }
+  } else {
+    return w == 1 ? draft_kivi_kernel<D, BITS, 1> : draft_kivi_kernel<D, BITS, 2>;
   }
 }
 template <int D, bool GATHER>
-void launch_rows(const DraftParams& P, dim3 grid, hipStream_t s) {
-  switch (pick_nhs<D>(P.g)) {
-    case 1: hipLaunchKernelGGL((draft_rows_kernel<D, 1, GATHER>), grid, dim3(256), 0, s, P); break;
-    case 2: hipLaunchKernelGGL((draft_rows_kernel<D, 2, GATHER>), grid, dim3(256), 0, s, P); break;
-    case 3: hipLaunchKernelGGL((draft_rows_kernel<D, 3, GATHER>), grid, dim3(256), 0, s, P); break;
-    default: hipLaunchKernelGGL((draft_rows_kernel<D, 4, GATHER>), grid, dim3(256), 0, s, P); break;
+DraftKernel rows_kernel_for(int nhs) {
+  switch (nhs) {
+    case 1: return draft_rows_kernel<D, 1, GATHER>;
+    case 2: return draft_rows_kernel<D, 2, GATHER>;
+    case 3: return draft_rows_kernel<D, 3, GATHER>;
+    default: return draft_rows_kernel<D, 4, GATHER>;
   }
+}
+
+DraftKernel pick_kernel(const vc_attn_shape& sh, const vc_draft_kv& kv) {
+  const int D = sh.head_dim, g = sh.n_q_heads / sh.n_kv_heads;
+  if (kv.kind == VC_DRAFT_KIVI) {
+    const int w = D == 128 ? pick_w<128>(g) : pick_w<64>(g);
+    if (D == 128) return kv.bits == 2 ? kivi_kernel_for<128, 2>(w) : kivi_kernel_for<128, 4>(w);
+    return kv.bits == 2 ? kivi_kernel_for<64, 2>(w) : kivi_kernel_for<64, 4>(w);
+  }
+  const int nhs = D == 128 ? pick_nhs<128>(g) : pick_nhs<64>(g);
+  if (kv.kind == VC_DRAFT_TOKDROP) return D == 128 ? rows_kernel_for<128, true>(nhs) : rows_kernel_for<64, true>(nhs);
+  return D == 128 ? rows_kernel_for<128, false>(nhs) : rows_kernel_for<64, false>(nhs);
+}
+
+// Workgroups of kernel k that the current device holds at once (CUs times
+// workgroups per CU), cached per (device, kernel). Without a device (a
+// workspace query on a host with no GPU) the 256-CU part is assumed.
+long long resident_wgs(DraftKernel k) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, long long> cache;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256 * 4;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(k));
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 64 * kWaves, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256 * 4;
+  }
+  const long long n = (long long)(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  cache[key] = n;
+  return n;
 }
 
 }  // namespace
 
-// Split plan shared by the workspace query and the launch.
+// Split plan shared by the workspace query and the launch: as many body
+// splits as let every workgroup (body splits plus the tail split of each
+// (sequence, KV head)) be resident at once, so the kernel runs in one round.
 struct DraftPlan {
   int bpw;     // body blocks per wave
   int splits;  // body splits + 1 tail split
@@ -832,11 +1001,12 @@ struct DraftPlan {
 DraftPlan draft_plan(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   const long long blocks = (kv.body_cap + 31) / 32;
   const long long units = (long long)sh.batch * sh.n_kv_heads;
-  const long long target_waves = 4096;  // about 16 waves per CU on 256 CUs
-  long long bpw = (blocks * units + target_waves - 1) / target_waves;
+  long long body_splits = resident_wgs(pick_kernel(sh, kv)) / units - 1;
+  if (body_splits < 1) body_splits = 1;
+  long long bpw = (blocks + body_splits * kWaves - 1) / (body_splits * kWaves);
   if (bpw < 1) bpw = 1;
-  if (bpw > 128) bpw = 128;
-  const long long body_splits = (blocks + kWaves * bpw - 1) / (kWaves * bpw);
+  body_splits = (blocks + kWaves * bpw - 1) / (kWaves * bpw);
+  if (body_splits < 1) body_splits = 1;
   return DraftPlan{(int)bpw, (int)body_splits + 1};
 }
 
@@ -884,18 +1054,7 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
 
   const dim3 grid(plan.splits, sh.n_kv_heads, sh.batch);
   const int D = sh.head_dim;
-  if (kv.kind == VC_DRAFT_KIVI) {
-    if (D == 128 && kv.bits == 2) launch_kivi<128, 2>(P, grid, stream);
-    else if (D == 128 && kv.bits == 4) launch_kivi<128, 4>(P, grid, stream);
-    else if (D == 64 && kv.bits == 2) launch_kivi<64, 2>(P, grid, stream);
-    else launch_kivi<64, 4>(P, grid, stream);
-  } else if (kv.kind == VC_DRAFT_TOKDROP) {
-    if (D == 128) launch_rows<128, true>(P, grid, stream);
-    else launch_rows<64, true>(P, grid, stream);
-  } else {
-    if (D == 128) launch_rows<128, false>(P, grid, stream);
-    else launch_rows<64, false>(P, grid, stream);
-  }
+  hipLaunchKernelGGL(pick_kernel(sh, kv), grid, dim3(64 * kWaves), 0, stream, P);
   vc_status st = check_launch("draft attention");
   if (st != VC_OK) return st;
   const dim3 mgrid(sh.n_q_heads, sh.batch);

@@ -132,7 +132,9 @@ KIVI_CASES = [
     (1, 64, 8, 128, 2, [4096], [160], False),            # Llama-70B layer shape, g = 8
     (2, 8, 2, 128, 4, [0, 64], [5, 32], False),          # empty body; tail only
     (1, 4, 2, 64, 2, [96], [1], False),                  # g = 2, single tail token
-    (1, 32, 2, 64, 2, [640], [40], False),               # g = 16 (two head sets at D = 64)
+    (1, 32, 2, 64, 2, [640], [40], False),               # g = 16 (rows of two channel groups at D = 64)
+    (1, 64, 4, 128, 2, [1024], [50], False),             # g = 16 (rows of four channel groups)
+    (2, 48, 4, 128, 4, [512, 224], [40, 7], True),       # g = 12, 4-bit, padding heads in the set
 ]
 
 

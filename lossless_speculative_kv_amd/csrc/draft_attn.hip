@@ -383,14 +383,13 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
 //   qp: A layout, lane (q, (hl, jr)), run w = K-step W*jr + w: fp16 pairs
 //       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)] *
 //       log2(e)/sqrt(D), zero for padding heads;
-//   qh, ql: score layout, lane (q, t): the same scaled query of head
-//       HPL*q + u at channels CPL*t + 2p, + 1, split into an fp16 pair and
-//       the fp16 pair of its remainder.
+//   qz: score layout, lane (q, t): the same scaled query of head HPL*q + u
+//       at channels CPL*t + e, in fp32.
 template <int D, int W>
 struct KiviQuery {
   static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL;
   uint32_t qp[W][4];
-  uint32_t qh[HPL][CPL / 2], ql[HPL][CPL / 2];
+  float qz[HPL][CPL];
 };
 
 template <int D, int W>
@@ -416,17 +415,7 @@ __device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, 
     const int hb = HPL * qg + u;
     const bool okb = hb < P.g;
 #pragma unroll
-    for (int p = 0; p < CPL / 2; ++p) {
-      float x[2], hi[2], lo[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        x[e] = okb ? bf16_bits_to_f32(qb[(size_t)hb * D + CPL * n + 2 * p + e]) * P.qscale : 0.f;
-        hi[e] = (float)(_Float16)x[e];
-        lo[e] = x[e] - hi[e];
-      }
-      Q.qh[u][p] = pack_f16(hi[0], hi[1]);
-      Q.ql[u][p] = pack_f16(lo[0], lo[1]);
-    }
+    for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(qb[(size_t)hb * D + CPL * n + e]) * P.qscale : 0.f;
   }
 }
 
@@ -458,18 +447,19 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
       const uint32_t sp = __builtin_amdgcn_perm(w1, w0, (r & 1) ? 0x07060302u : 0x05040100u);
       Aq[w][r] = as_u32(as_f16x2(Q.qp[w][r]) * as_f16x2(sp));
     }
-  // zero-point bias of the lane's heads: sum over channels CPL*t .. and the
-  // row (two independent accumulation chains)
+  // zero-point bias of the lane's heads: sum over channels CPL*t .. (fp32
+  // query times fp16 zero point, mixed-precision FMAs in two chains) and
+  // over the row
   float bias[HPL];
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
-    float xh = 0.f, xl = 0.f;
+    float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int p = 0; p < CPL / 2; ++p) {
-      xh = __builtin_amdgcn_fdot2(as_f16x2(Q.qh[u][p]), as_f16x2(raw.kz[p]), xh, false);
-      xl = __builtin_amdgcn_fdot2(as_f16x2(Q.ql[u][p]), as_f16x2(raw.kz[p]), xl, false);
+      x0 = fmaf(Q.qz[u][2 * p], f16_lo(raw.kz[p]), x0);
+      x1 = fmaf(Q.qz[u][2 * p + 1], f16_hi(raw.kz[p]), x1);
     }
-    bias[u] = row_sum16(xh + xl);
+    bias[u] = row_sum16(x0 + x1);
   }
   f32x4 c[2];
 #pragma unroll
@@ -495,7 +485,7 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t pr = Pp[r], zw = raw.vz[w][r], sw = raw.vs[w][r];
-      st.zt[0][w] = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(zw), st.zt[0][w], false);
+      st.zt[0][w] = fmaf(f16_hi(pr), f16_hi(zw), fmaf(f16_lo(pr), f16_lo(zw), st.zt[0][w]));
       Pv[w][r] = as_u32(as_f16x2(pr) * as_f16x2(sw));
     }
 
@@ -747,12 +737,15 @@ constexpr size_t draft_lds_bytes() {
 }
 
 // ---------------------------------------------------------------- kernels ----
-// LDS of the KIVI kernel: three ring stages (one per variable, so the
-// compiler can tell which pending direct-to-LDS loads a read depends on; the
-// first also hosts the wave merge at the end), then the probability areas.
+// LDS of the KIVI kernel: NS ring stages (one per variable, so the compiler
+// can tell which pending direct-to-LDS loads a read depends on; the first
+// also hosts the wave merge at the end), then the probability areas.
 template <int D, int BITS, int W>
 struct KiviLds {
   static constexpr int STAGE = kWaves * BlockLayout<D, BITS>::BYTES;
+  // ring depth: four stages while they fit in 48 KB (three workgroups per
+  // CU) and the rows are one group wide (wider rows need the registers)
+  static constexpr int NS = (W == 1 && 4 * STAGE <= 48 * 1024) ? 4 : 3;
   static constexpr int MERGE = kWaves * Geo<D, W>::HS * (D + 2) * 4;
   static constexpr int STAGE0 = STAGE > MERGE ? STAGE : MERGE;
 };
@@ -760,7 +753,7 @@ struct KiviLds {
 // Waves per SIMD to plan registers for (wider rows hold more heads per lane).
 template <int D, int W>
 constexpr int kivi_min_waves() {
-  return W == 1 ? 4 : (Geo<D, W>::NR > 1 ? 2 : 1);
+  return W == 1 ? 3 : (Geo<D, W>::NR > 1 ? 2 : 1);
 }
 
 // KIVI body + fp16 tail, one head set of HS = 16*W/NG >= g query heads.
@@ -772,6 +765,7 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
   __shared__ __attribute__((aligned(16))) char rs0[LL::STAGE0];
   __shared__ __attribute__((aligned(16))) char rs1[LL::STAGE];
   __shared__ __attribute__((aligned(16))) char rs2[LL::STAGE];
+  __shared__ __attribute__((aligned(16))) char rs3[LL::NS > 3 ? LL::STAGE : 16];
   __shared__ __attribute__((aligned(16))) uint32_t parea[kWaves * p_area_words<D, W, 1>()];
   // the wave index is uniform across the wave; saying so keeps the per-block
   // offsets in SGPRs
@@ -798,33 +792,58 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
       res.vc = make_rsrc(P.v_codes + unit * nbc * 64 * VWL, nbc * 64 * VWL * 4);
       res.vs = make_rsrc(P.v_scale + unit * nbc * NG * 32, nbc * NG * 32 * 2);
       res.vz = make_rsrc(P.v_zero + unit * nbc * NG * 32, nbc * NG * 32 * 2);
-      char* w0 = rs0 + wave * BL::BYTES;
-      char* w1 = rs1 + wave * BL::BYTES;
-      char* w2 = rs2 + wave * BL::BYTES;
-      // three-stage ring, two blocks in flight ahead of the one computed.
-      // Past the wave's last block the last one is loaded again (into a stage
-      // that is not read), which keeps every wait count constant. (The
-      // compiler adds a stricter wait after the loop header, where it loses
-      // track of which stage the pending loads write.)
+      constexpr int NS = LL::NS;
+      char* const w0 = rs0 + wave * BL::BYTES;
+      char* const w1 = rs1 + wave * BL::BYTES;
+      char* const w2 = rs2 + wave * BL::BYTES;
+      char* const w3 = rs3 + (NS > 3 ? wave * BL::BYTES : 0);
+      // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of the
+      // next block move from LDS to registers at the end of a step, so their
+      // latency overlaps the step's last MFMAs. Past the wave's last block
+      // the last one is loaded again (into a stage that is not read), which
+      // keeps every wait count constant.
       const int last = b1 - 1;
-      auto step = [&](const char* stage) {
-        wait_vm<2 * BL::NI>();
-        KiviRaw<D, BITS, W> raw;
-        kivi_read<D, BITS, W>(raw, stage, lane);
-        kivi_compute<D, BITS, W>(raw, lane, Q, st, lds_p);
+      KiviRaw<D, BITS, W> ra, rb;
+      auto step = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt, char* refill, int refill_blk,
+                      const char* next_stage) {
+        issue_block<D, BITS>(refill, res, min(refill_blk, last), lane);
+        kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
+        wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
+        kivi_read<D, BITS, W>(nxt, next_stage, lane);
       };
       issue_block<D, BITS>(w0, res, b0, lane);
       issue_block<D, BITS>(w1, res, min(b0 + 1, last), lane);
-      for (int blk = b0;; blk += 3) {
-        issue_block<D, BITS>(w2, res, min(blk + 2, last), lane);
-        step(w0);
-        if (blk + 1 > last) break;
-        issue_block<D, BITS>(w0, res, min(blk + 3, last), lane);
-        step(w1);
-        if (blk + 2 > last) break;
-        issue_block<D, BITS>(w1, res, min(blk + 4, last), lane);
-        step(w2);
-        if (blk + 3 > last) break;
+      if constexpr (NS == 4) {
+        issue_block<D, BITS>(w2, res, min(b0 + 2, last), lane);
+        wait_vm<2 * BL::NI>();
+        kivi_read<D, BITS, W>(ra, w0, lane);
+        for (int blk = b0;; blk += 4) {
+          step(ra, rb, w3, blk + 3, w1);
+          if (blk + 1 > last) break;
+          step(rb, ra, w0, blk + 4, w2);
+          if (blk + 2 > last) break;
+          step(ra, rb, w1, blk + 5, w3);
+          if (blk + 3 > last) break;
+          step(rb, ra, w2, blk + 6, w0);
+          if (blk + 4 > last) break;
+        }
+      } else {
+        wait_vm<BL::NI>();
+        kivi_read<D, BITS, W>(ra, w0, lane);
+        for (int blk = b0;; blk += 6) {
+          step(ra, rb, w2, blk + 2, w1);
+          if (blk + 1 > last) break;
+          step(rb, ra, w0, blk + 3, w2);
+          if (blk + 2 > last) break;
+          step(ra, rb, w1, blk + 4, w0);
+          if (blk + 3 > last) break;
+          step(rb, ra, w2, blk + 5, w1);
+          if (blk + 4 > last) break;
+          step(ra, rb, w0, blk + 6, w2);
+          if (blk + 5 > last) break;
+          step(rb, ra, w1, blk + 7, w0);
+          if (blk + 6 > last) break;
+        }
       }
       wait_vm<0>();
     }

@@ -9,15 +9,22 @@ the timed region starts.
 
 metric (per decoder layer): accepted tokens per second per layer,
     value = sum over timed rounds and sequences of (m + 1)
-            / sum over timed rounds of (k * t_draft_attn + t_verify_attn),
-with the attention times measured by HIP events on the compute stream inside
-the timed region (a real model projects to the vocabulary once per token,
-not once per layer). The whole-round wall clock is reported as ms_per_step
-and round_tok_s.
+            / (timed rounds * (k * t_draft_attn + t_verify_attn)),
+with t_draft_attn / t_verify_attn the average duration of a whole draft /
+verification attention call (attention kernel + split merge), measured inside
+the timed region by HIP events that the calls' own kernel dispatches record
+(vc_time_next_call: no queue markers, so timing does not idle the GPU). A
+real model projects to the vocabulary once per token, not once per layer,
+so the vocab projection is outside the per-layer metric; the whole-round
+wall clock is reported as ms_per_step and round_tok_s.
 
-roofline: the draft decode attention (the dominant term of the metric):
-algorithmic bytes per launch (compressed body + fp16 tail + q + out) over its
-measured average duration, against 8 TB/s.
+roofline: the draft decode attention kernel (the dominant term of the
+metric): algorithmic bytes per launch (compressed body + fp16 tail + q + out)
+over the kernel's own average duration (events around the attention kernel
+alone, on alternate draft steps), against 8 TB/s; `traffic` is the HBM bytes
+per launch from the committed FETCH_SIZE / WRITE_SIZE measurement when the
+kernel source has not changed since. The same figures for the verification
+kernel are under verify_attn.
 cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,7 +49,24 @@ def parse():
     ap.add_argument("--workload", default="llama3-8b-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (5 times) and print its byte counts; the "
+                         "HBM counters of this run calibrate the traffic figures of the hot-path kernels")
     return ap.parse_args()
+
+
+def copy_calibration(mb: int):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mb * 1024 * 1024
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 5}}))
 
 
 def log(msg, quiet=False):
@@ -67,6 +91,36 @@ def draft_bytes_per_launch(cfg, body_len, tail_len):
 def verify_bytes_per_launch(cfg, ctx_len):
     B, Hq, Hkv, D, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.k + 1
     return sum(Hkv * (ctx_len[b] + n) * 4 * D for b in range(B)) + n * B * Hq * D * (2 + 4)
+
+
+def draft_kernel_name(cfg):
+    return {"kivi": "draft_kivi_kernel", "tokdrop": "draft_rows_kernel"}.get(cfg.kind, "draft_rows_kernel")
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter measurement (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE,
+    scaled by a plain copy of known size), or None when no measurement exists
+    or the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = table.get("kernels", {}).get(f"{kernel}@{workload}")
+    if not entry:
+        return None
+    src = os.path.join(ROOT, entry["source"])
+    try:
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if digest != entry["source_sha256"]:
+        return None
+    return entry["fetch_bytes"] + entry["write_bytes"]
 
 
 def cpu_baseline(cfg, accepted_per_round, quiet):
@@ -107,6 +161,9 @@ def cpu_baseline(cfg, accepted_per_round, quiet):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path is measured on a single "
               "MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
@@ -129,7 +186,7 @@ def main():
         eng.round()
     torch.cuda.synchronize()
     body0, tail0, ctx0 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
-    eng.events = []
+    eng.prepare_timing(args.steps * (2 * cfg.k + 2) + 4)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -145,23 +202,26 @@ def main():
         times.setdefault(name, []).append(a.elapsed_time(b) * 1e-3)
     n_acc = eng.n_accept[args.warmup:args.warmup + args.steps].cpu().numpy()
     accepted = float((n_acc + 1).sum())
-    t_draft = float(np.sum(times.get("draft_attn", [0.0])))
-    t_verify = float(np.sum(times.get("verify_attn", [0.0])))
-    attn_time = t_draft + t_verify
+    # whole calls (attention kernel + split merge) were timed on even draft
+    # steps / even rounds, the attention kernel alone on odd ones; the events
+    # are recorded by the kernels' own dispatches (vc_time_next_call)
+    def avg(name):
+        v = times.get(name, [])
+        return float(np.mean(v)) if v else 0.0
+    t_draft_avg, t_draft_main = avg("draft_attn"), avg("draft_attn_main")
+    t_verify_avg, t_verify_main = avg("verify_attn"), avg("verify_attn_main")
+    attn_time = args.steps * (cfg.k * t_draft_avg + t_verify_avg)
     value = accepted / attn_time if attn_time > 0 else 0.0
-    n_draft = len(times.get("draft_attn", []))
-    t_draft_avg = t_draft / max(n_draft, 1)
-    t_verify_avg = t_verify / max(len(times.get("verify_attn", [])), 1)
 
     mid_body = [(int(a) + int(b)) / 2 for a, b in zip(body0, body1)]
     mid_tail = [(int(a) + int(b)) / 2 + cfg.k / 2 for a, b in zip(tail0, tail1)]  # tail grows by 1 per draft step
     draft_bytes = draft_bytes_per_launch(cfg, mid_body, mid_tail)
     verify_bytes = verify_bytes_per_launch(cfg, [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)])
-    draft_gbs = draft_bytes / t_draft_avg / 1e9
-    verify_gbs = verify_bytes / t_verify_avg / 1e9
+    draft_gbs = draft_bytes / t_draft_main / 1e9 if t_draft_main > 0 else 0.0
+    verify_gbs = verify_bytes / t_verify_main / 1e9 if t_verify_main > 0 else 0.0
 
     B, k = cfg.batch, cfg.k
-    ceiling = B * (k + 1) / (k * t_draft_avg + t_verify_avg)
+    ceiling = B * (k + 1) / (k * t_draft_avg + t_verify_avg) if (k * t_draft_avg + t_verify_avg) > 0 else 0.0
     breakdown = {name: {"avg_us": float(np.mean(v)) * 1e6, "calls": len(v)} for name, v in times.items()}
     result = {
         "metric": "accepted tok/s/layer; draft & verify attn HBM GB/s as % of 8 TB/s peak",
@@ -180,12 +240,15 @@ def main():
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "context": cfg.context,
                    "draft_k": cfg.k, "compressor": cfg.kind if cfg.kind != "kivi" else f"kivi-{cfg.bits}",
                    "residual": cfg.residual, "vocab": cfg.vocab, "hidden": cfg.hidden},
-        "roofline": {"bound": "hbm", "kernel": "draft decode attention (vc_draft_decode_attn, split + merge)",
+        "roofline": {"bound": "hbm", "kernel": draft_kernel_name(cfg),
                      "achieved": draft_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": draft_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": draft_bytes, "avg_launch_us": t_draft_avg * 1e6},
-        "verify_attn": {"achieved_GBs": verify_gbs, "frac": verify_gbs / HBM_PEAK_GBS,
-                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_verify_avg * 1e6},
+                     "frac": draft_gbs / HBM_PEAK_GBS, "traffic": traffic_for(draft_kernel_name(cfg), cfg.name),
+                     "bytes_per_launch": draft_bytes, "avg_launch_us": t_draft_main * 1e6,
+                     "call_us": t_draft_avg * 1e6},
+        "verify_attn": {"kernel": "verify_kernel", "achieved_GBs": verify_gbs, "frac": verify_gbs / HBM_PEAK_GBS,
+                        "traffic": traffic_for("verify_kernel", cfg.name),
+                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_verify_main * 1e6,
+                        "call_us": t_verify_avg * 1e6},
         "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": accepted / args.steps,
                    "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
         "round_tok_s": accepted / wall,

@@ -45,9 +45,27 @@ enum {
   VC_ERR_HIP = -4          /* a HIP launch or copy reported an error */
 };
 
-/* Text of the last non-OK status returned on this thread ("" if none). */
+/* Library version string, and the text of the last non-OK status returned on
+ * this thread ("" if none). */
 const char *vc_version(void);
 const char *vc_last_error(void);
+
+/* Kernel timing without extra queue packets (for callers that measure the
+ * calls). The next call made on this thread has its own kernel dispatches
+ * record the given events: with VC_TIME_CALL, start_event when the call's
+ * first kernel starts and stop_event when its last kernel ends; with
+ * VC_TIME_MAIN_KERNEL, both around the call's main kernel (the attention
+ * kernel before its split merge, the vocab product before its argmax
+ * reduction). Recording events around a call from the host instead adds a
+ * marker to the queue before and after it, which idles the GPU for a few
+ * microseconds each time. Calls that take part: vc_draft_decode_attn,
+ * vc_verify_attn, vc_vocab_logits; any other call discards the setting.
+ * The events are hipEvent_t handles created by the caller on the device of
+ * the call (passed as void *); either may be NULL. The setting is consumed by
+ * the next call whatever its outcome. Returns VC_ERR_INVALID_ARG for an
+ * unknown scope. */
+enum { VC_TIME_CALL = 0, VC_TIME_MAIN_KERNEL = 1 };
+vc_status vc_time_next_call(void *start_event, void *stop_event, int32_t scope);
 
 /* Attention shape. head_dim is 64 or 128; n_q_heads % n_kv_heads == 0 and the
  * group g = n_q_heads / n_kv_heads is at most 16. Query head h reads KV head

@@ -16,9 +16,10 @@ LIB_PATH = os.path.join(_HERE, "libvc.so")
 VC_OK, VC_ERR_INVALID_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE, VC_ERR_HIP = 0, -1, -2, -3, -4
 VC_DRAFT_DENSE, VC_DRAFT_KIVI, VC_DRAFT_TOKDROP = 0, 1, 2
 VC_VERIFY_BEGIN, VC_VERIFY_END = 1, 2
+VC_TIME_CALL, VC_TIME_MAIN_KERNEL = 0, 1
 
 EXPORTS = [
-    "vc_version", "vc_last_error", "vc_draft_workspace_bytes", "vc_draft_decode_attn",
+    "vc_version", "vc_last_error", "vc_time_next_call", "vc_draft_workspace_bytes", "vc_draft_decode_attn",
     "vc_verify_workspace_bytes", "vc_verify_attn", "vc_vocab_workspace_bytes", "vc_vocab_logits",
     "vc_greedy_accept", "vc_commit_workspace_bytes", "vc_commit_round", "vc_kivi_quantize",
     "vc_tokdrop_workspace_bytes", "vc_tokdrop_select", "vc_stage_full_kv",
@@ -78,6 +79,7 @@ _S = C.POINTER(vc_attn_shape)
 _sigs = {
     "vc_version": ([], C.c_char_p),
     "vc_last_error": ([], C.c_char_p),
+    "vc_time_next_call": ([_P, _P, C.c_int32], C.c_int32),
     "vc_draft_workspace_bytes": ([_S, C.POINTER(vc_draft_kv), C.POINTER(C.c_size_t)], C.c_int32),
     "vc_draft_decode_attn": ([_S, _P, C.POINTER(vc_draft_kv), _P, _P, C.c_size_t, _P], C.c_int32),
     "vc_verify_workspace_bytes": ([_S, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
@@ -106,6 +108,12 @@ def last_error() -> str:
 
 def version() -> str:
     return lib.vc_version().decode()
+
+
+def vc_time_next_call(start_event, stop_event, scope=VC_TIME_CALL):
+    """The next call on this thread records these hipEvent_t handles (ints or
+    None) from its own kernel dispatches; see include/vc.h."""
+    check(lib.vc_time_next_call(start_event, stop_event, scope), "vc_time_next_call")
 
 
 def check(status: int, where: str) -> None:

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/vc.h"
+#include "vc_internal.h"
 
 namespace vc {
 
@@ -40,6 +41,13 @@ vc_status tokdrop_launch(const vc_attn_shape& sh, const float* scores, int T, in
                          hipStream_t stream);
 
 static thread_local std::string g_last_error;
+static thread_local Timing g_timing;
+
+Timing take_timing() {
+  const Timing t = g_timing;
+  g_timing = Timing{};
+  return t;
+}
 
 void set_error(const char* fmt, ...) {
   char buf[512];
@@ -138,6 +146,12 @@ vc_status check_ws(void* ws, size_t have, size_t need) {
   return VC_OK;
 }
 
+// Clears a pending vc_time_next_call setting when an entry point returns,
+// whether or not a launcher consumed it.
+struct TimingClear {
+  ~TimingClear() { (void)vc::take_timing(); }
+};
+
 }  // namespace
 
 extern "C" {
@@ -145,7 +159,17 @@ extern "C" {
 const char* vc_version(void) { return "vericache-mi355x 0.1 (gfx950)"; }
 const char* vc_last_error(void) { return vc::g_last_error.c_str(); }
 
+vc_status vc_time_next_call(void* start_event, void* stop_event, int32_t scope) {
+  if (scope != VC_TIME_CALL && scope != VC_TIME_MAIN_KERNEL)
+    return fail(VC_ERR_INVALID_ARG, "scope %d is neither VC_TIME_CALL nor VC_TIME_MAIN_KERNEL", scope);
+  vc::g_timing.start = static_cast<hipEvent_t>(start_event);
+  vc::g_timing.stop = static_cast<hipEvent_t>(stop_event);
+  vc::g_timing.scope = scope;
+  return VC_OK;
+}
+
 vc_status vc_draft_workspace_bytes(const vc_attn_shape* shape, const vc_draft_kv* kv, size_t* bytes) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if ((st = check_draft_kv(shape, kv)) != VC_OK) return st;
@@ -156,6 +180,7 @@ vc_status vc_draft_workspace_bytes(const vc_attn_shape* shape, const vc_draft_kv
 
 vc_status vc_draft_decode_attn(const vc_attn_shape* shape, const void* q, const vc_draft_kv* kv, float* out, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if ((st = check_draft_kv(shape, kv)) != VC_OK) return st;
@@ -167,6 +192,7 @@ vc_status vc_draft_decode_attn(const vc_attn_shape* shape, const void* q, const 
 
 vc_status vc_verify_workspace_bytes(const vc_attn_shape* shape, int32_t n_rows, int32_t max_chunk_tokens,
                                     size_t* bytes) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (n_rows < 1 || n_rows > 64) return fail(VC_ERR_INVALID_ARG, "n_rows %d not in [1, 64]", n_rows);
@@ -182,6 +208,7 @@ vc_status vc_verify_workspace_bytes(const vc_attn_shape* shape, int32_t n_rows, 
 vc_status vc_verify_attn(const vc_attn_shape* shape, int32_t n_rows, const void* q, const void* k_new,
                          const void* v_new, const vc_kv_chunk* ctx, const int32_t* ctx_len, int32_t flags, float* out,
                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (n_rows < 1 || n_rows > 64) return fail(VC_ERR_INVALID_ARG, "n_rows %d not in [1, 64]", n_rows);
@@ -205,7 +232,10 @@ vc_status vc_verify_attn(const vc_attn_shape* shape, int32_t n_rows, const void*
   return vc::verify_launch(*shape, n_rows, q, k_new, v_new, *ctx, ctx_len, flags, out, ws, ws_bytes, stream);
 }
 
-vc_status vc_vocab_workspace_bytes(int32_t m_rows, int32_t hidden, int32_t vocab, size_t* bytes) {
+// Argument checks and sizes behind the *_workspace_bytes entry points; the
+// launching calls use these directly, so that no entry point calls another
+// (each one consumes a pending vc_time_next_call setting when it returns).
+static vc_status vocab_ws_query(int32_t m_rows, int32_t hidden, int32_t vocab, size_t* bytes) {
   if (m_rows < 1 || m_rows > vc::vocab_max_rows())
     return fail(VC_ERR_UNSUPPORTED, "m_rows %d not in [1, %d]", m_rows, vc::vocab_max_rows());
   if (hidden < 128 || hidden % 128) return fail(VC_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128", hidden);
@@ -215,11 +245,17 @@ vc_status vc_vocab_workspace_bytes(int32_t m_rows, int32_t hidden, int32_t vocab
   return VC_OK;
 }
 
+vc_status vc_vocab_workspace_bytes(int32_t m_rows, int32_t hidden, int32_t vocab, size_t* bytes) {
+  TimingClear timing_clear;
+  return vocab_ws_query(m_rows, hidden, vocab, bytes);
+}
+
 vc_status vc_vocab_logits(int32_t m_rows, int32_t hidden, int32_t vocab, const float* h, const void* w,
                           int32_t* argmax, float* max_logit, float* logits, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
+  TimingClear timing_clear;
   size_t need = 0;
-  vc_status st = vc_vocab_workspace_bytes(m_rows, hidden, vocab, &need);
+  vc_status st = vocab_ws_query(m_rows, hidden, vocab, &need);
   if (st != VC_OK) return st;
   VC_REQ(h, 16, "h");
   VC_REQ(w, 16, "w");
@@ -232,6 +268,7 @@ vc_status vc_vocab_logits(int32_t m_rows, int32_t hidden, int32_t vocab, const f
 
 vc_status vc_greedy_accept(int32_t batch, int32_t k, const int32_t* x, const int32_t* y, int32_t* n_accept,
                            int32_t* next_token, int32_t* committed, hipStream_t stream) {
+  TimingClear timing_clear;
   if (batch < 1) return fail(VC_ERR_INVALID_ARG, "batch %d < 1", batch);
   if (k < 0 || k > 1024) return fail(VC_ERR_INVALID_ARG, "k %d not in [0, 1024]", k);
   VC_REQ(x, 4, "x");
@@ -243,6 +280,7 @@ vc_status vc_greedy_accept(int32_t batch, int32_t k, const int32_t* x, const int
 }
 
 vc_status vc_commit_workspace_bytes(const vc_attn_shape* shape, size_t* bytes) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (bytes == nullptr) return fail(VC_ERR_INVALID_ARG, "bytes is NULL");
@@ -254,6 +292,7 @@ vc_status vc_commit_round(const vc_attn_shape* shape, int32_t k, const int32_t* 
                           const void* v_new, void* full_k, void* full_v, int32_t full_t_cap, int32_t* ctx_len,
                           const vc_draft_cache* draft, int32_t* status_flags, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (k < 0 || k > 63) return fail(VC_ERR_INVALID_ARG, "k %d not in [0, 63]", k);
@@ -296,6 +335,7 @@ vc_status vc_commit_round(const vc_attn_shape* shape, int32_t k, const int32_t* 
 
 vc_status vc_kivi_quantize(const vc_attn_shape* shape, const void* src_k, const void* src_v, int32_t src_t_cap,
                            int32_t n_body, int32_t n_tail, const vc_draft_cache* draft, hipStream_t stream) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (draft == nullptr || draft->kind != VC_DRAFT_KIVI) return fail(VC_ERR_INVALID_ARG, "draft must be a KIVI cache");
@@ -328,7 +368,7 @@ vc_status vc_kivi_quantize(const vc_attn_shape* shape, const void* src_k, const 
   return vc::fill_i32_launch(draft->tail_len, shape->batch, n_tail, stream);
 }
 
-vc_status vc_tokdrop_workspace_bytes(const vc_attn_shape* shape, int32_t T, size_t* bytes) {
+static vc_status tokdrop_ws_query(const vc_attn_shape* shape, int32_t T, size_t* bytes) {
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (T < 1 || T > (1 << 24)) return fail(VC_ERR_INVALID_ARG, "T %d not in [1, 2^24]", T);
@@ -337,10 +377,16 @@ vc_status vc_tokdrop_workspace_bytes(const vc_attn_shape* shape, int32_t T, size
   return VC_OK;
 }
 
+vc_status vc_tokdrop_workspace_bytes(const vc_attn_shape* shape, int32_t T, size_t* bytes) {
+  TimingClear timing_clear;
+  return tokdrop_ws_query(shape, T, bytes);
+}
+
 vc_status vc_tokdrop_select(const vc_attn_shape* shape, const float* scores, int32_t T, int32_t n_keep,
                             int32_t* kept_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  TimingClear timing_clear;
   size_t need = 0;
-  vc_status st = vc_tokdrop_workspace_bytes(shape, T, &need);
+  vc_status st = tokdrop_ws_query(shape, T, &need);
   if (st != VC_OK) return st;
   (void)ws;
   (void)ws_bytes;
@@ -353,6 +399,7 @@ vc_status vc_tokdrop_select(const vc_attn_shape* shape, const float* scores, int
 vc_status vc_stage_full_kv(const vc_attn_shape* shape, const void* host_k, const void* host_v, int64_t t_host,
                            int32_t tok_begin, int32_t tok_count, void* dev_k, void* dev_v, int32_t chunk_cap,
                            hipStream_t copy_stream, hipEvent_t done) {
+  TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (host_k == nullptr || host_v == nullptr || dev_k == nullptr || dev_v == nullptr)

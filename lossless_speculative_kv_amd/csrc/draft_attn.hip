@@ -1073,12 +1073,15 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
 
   const dim3 grid(plan.splits, sh.n_kv_heads, sh.batch);
   const int D = sh.head_dim;
-  hipLaunchKernelGGL(pick_kernel(sh, kv), grid, dim3(64 * kWaves), 0, stream, P);
+  const Timing tm = take_timing();
+  const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
+  launch_ev(pick_kernel(sh, kv), grid, dim3(64 * kWaves), 0, stream, tm.start, main_only ? tm.stop : nullptr, P);
   vc_status st = check_launch("draft attention");
   if (st != VC_OK) return st;
   const dim3 mgrid(sh.n_q_heads, sh.batch);
-  if (D == 128) hipLaunchKernelGGL((draft_merge_kernel<128>), mgrid, dim3(128), 0, stream, P);
-  else hipLaunchKernelGGL((draft_merge_kernel<64>), mgrid, dim3(64), 0, stream, P);
+  hipEvent_t mstop = main_only ? nullptr : tm.stop;
+  if (D == 128) launch_ev(draft_merge_kernel<128>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
+  else launch_ev(draft_merge_kernel<64>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
   return check_launch("draft merge");
 }
 

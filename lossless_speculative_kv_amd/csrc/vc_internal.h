@@ -1,5 +1,6 @@
 // Internal helpers shared by the gfx950 kernels of libvc (not part of the ABI).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -141,5 +142,21 @@ vc_status fail(vc_status code, const char* fmt, ...);
 vc_status check_launch(const char* what);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Events the caller asked the next call on this thread to record (see
+// vc_time_next_call); take_timing() hands them over once and clears them.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int scope = VC_TIME_CALL;
+};
+Timing take_timing();
+
+// Launch, with the dispatch itself recording start / stop events when given.
+template <typename F, typename... A>
+void launch_ev(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+               A... args) {
+  if (start != nullptr || stop != nullptr) hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, start, stop, 0u, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 }  // namespace vc

@@ -324,10 +324,11 @@ __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
 }
 
 template <int D>
-void launch_verify(const VerifyParams& P, int rt, int nwaves, dim3 grid, hipStream_t s) {
+void launch_verify(const VerifyParams& P, int rt, int nwaves, dim3 grid, hipStream_t s, hipEvent_t start,
+                   hipEvent_t stop) {
   const dim3 block(64 * (nwaves + 2));
-  if (rt == 2) hipLaunchKernelGGL((verify_kernel<D, 2>), grid, block, 0, s, P);
-  else hipLaunchKernelGGL((verify_kernel<D, 3>), grid, block, 0, s, P);
+  if (rt == 2) launch_ev(verify_kernel<D, 2>, grid, block, 0, s, start, stop, P);
+  else launch_ev(verify_kernel<D, 3>, grid, block, 0, s, start, stop, P);
 }
 
 }  // namespace
@@ -415,13 +416,16 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   P.flags = flags;
   P.qscale = kLog2e / sqrtf((float)sh.head_dim);
   const dim3 grid(P.S, sh.n_kv_heads, sh.batch);
-  if (sh.head_dim == 128) launch_verify<128>(P, plan.rt, plan.nwaves, grid, stream);
-  else launch_verify<64>(P, plan.rt, plan.nwaves, grid, stream);
+  const Timing tm = take_timing();
+  const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
+  if (sh.head_dim == 128) launch_verify<128>(P, plan.rt, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
+  else launch_verify<64>(P, plan.rt, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
   vc_status st = check_launch("verify attention");
   if (st != VC_OK) return st;
   const dim3 mgrid((unsigned)R, sh.n_kv_heads, sh.batch);
-  if (sh.head_dim == 128) hipLaunchKernelGGL((verify_merge_kernel<128>), mgrid, dim3(128), 0, stream, P);
-  else hipLaunchKernelGGL((verify_merge_kernel<64>), mgrid, dim3(64), 0, stream, P);
+  hipEvent_t mstop = main_only ? nullptr : tm.stop;
+  if (sh.head_dim == 128) launch_ev(verify_merge_kernel<128>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
+  else launch_ev(verify_merge_kernel<64>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
   return check_launch("verify merge");
 }
 

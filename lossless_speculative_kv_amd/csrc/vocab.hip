@@ -274,13 +274,13 @@ __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) 
 }
 
 template <int NMT>
-void launch_staged(const VocabParams& P, hipStream_t s) {
+void launch_staged(const VocabParams& P, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const size_t lds = (size_t)2 * P.Mp * (kKC + 8) * 2;
   const size_t red = (size_t)kStagedWaves * P.Mp * 8;
   const size_t bytes = lds > red ? lds : red;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&vocab_staged_kernel<NMT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  hipLaunchKernelGGL((vocab_staged_kernel<NMT>), dim3(P.nwg), dim3(64 * kStagedWaves), bytes, s, P);
+  launch_ev(vocab_staged_kernel<NMT>, dim3(P.nwg), dim3(64 * kStagedWaves), (uint32_t)bytes, s, start, stop, P);
 }
 
 }  // namespace
@@ -333,27 +333,30 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.K = K;
   P.V = V;
   P.nwg = plan.nwg;
+  const Timing tm = take_timing();
+  const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
+  hipEvent_t mstart = main_only ? tm.start : nullptr, mstop = main_only ? tm.stop : nullptr;
   {
     const size_t n = (size_t)plan.Mp * K;
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, P);
+    launch_ev(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, main_only ? nullptr : tm.start, nullptr, P);
   }
   if (plan.stream) {
-    if (plan.ms == 1) hipLaunchKernelGGL((vocab_stream_kernel<1>), dim3(plan.nwg), dim3(256), 0, stream, P);
-    else hipLaunchKernelGGL((vocab_stream_kernel<2>), dim3(plan.nwg), dim3(256), 0, stream, P);
+    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
+    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
   } else {
     switch (plan.nmt) {
-      case 4: launch_staged<4>(P, stream); break;
-      case 8: launch_staged<8>(P, stream); break;
-      case 12: launch_staged<12>(P, stream); break;
-      case 18: launch_staged<18>(P, stream); break;
-      case 24: launch_staged<24>(P, stream); break;
-      default: launch_staged<28>(P, stream); break;
+      case 4: launch_staged<4>(P, stream, mstart, mstop); break;
+      case 8: launch_staged<8>(P, stream, mstart, mstop); break;
+      case 12: launch_staged<12>(P, stream, mstart, mstop); break;
+      case 18: launch_staged<18>(P, stream, mstart, mstop); break;
+      case 24: launch_staged<24>(P, stream, mstart, mstop); break;
+      default: launch_staged<28>(P, stream, mstart, mstop); break;
     }
   }
   vc_status st = check_launch("vocab projection");
   if (st != VC_OK) return st;
-  hipLaunchKernelGGL(vocab_reduce_kernel, dim3(M), dim3(256), 0, stream, P);
+  launch_ev(vocab_reduce_kernel, dim3(M), dim3(256), 0, stream, nullptr, main_only ? nullptr : tm.stop, P);
   return check_launch("vocab argmax reduce");
 }
 

@@ -51,9 +51,10 @@ class Engine:
         B, Hq, Hkv, D, k = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.k
         self.rounds_cap = rounds_cap
         self.round_idx = 0
-        # optional timing hook: when a list, (name, start, end) torch events are
-        # appended around the attention calls (recorded on the compute stream)
+        # optional timing: when a list (see prepare_timing), (name, start, end)
+        # torch events recorded by the timed calls' own kernel dispatches
         self.events = None
+        self._ev_pool = []
         s = self.stream.cuda_stream
         bf = torch.bfloat16
 
@@ -219,25 +220,45 @@ class Engine:
         sdev.embed_draft(c.seed, self.xs[j].data_ptr(), 1, c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
                          _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
                          self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), s)
-        self.draft_attention()
+        self.draft_attention(j)
         self._timed("draft_vocab", lambda: L.vc_vocab_logits(
             c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(), self.xs[j + 1].data_ptr(),
             None, None, self.ws_vocab_d.data_ptr(), self.ws_vocab_d.numel(), s))
 
-    def _timed(self, name, fn):
+    def prepare_timing(self, n_calls: int):
+        """Create the events of n_calls timed calls before a timed region and
+        switch timing on. The events are materialised here (one host record
+        each), so inside the region the library records them from its own
+        kernel dispatches (vc_time_next_call) and nothing is added to the
+        queue."""
+        pool = []
+        for _ in range(n_calls):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            b.record(self.stream)
+            pool.append((a, b))
+        torch.cuda.synchronize(self.dev)
+        self._ev_pool = pool
+        self.events = []
+
+    def _timed(self, name, fn, scope=L.VC_TIME_CALL):
         if self.events is None:
             fn()
             return
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
+        if not self._ev_pool:
+            raise RuntimeError("prepare_timing() was given too few calls for this timed region")
+        a, b = self._ev_pool.pop()
+        L.vc_time_next_call(a.cuda_event, b.cuda_event, scope)
         fn()
-        b.record(self.stream)
         self.events.append((name, a, b))
 
-    def draft_attention(self):
-        self._timed("draft_attn", lambda: L.vc_draft_decode_attn(
+    def draft_attention(self, j: int = 0):
+        # even steps time the whole call (attention kernel + split merge), odd
+        # steps the attention kernel alone
+        name, scope = ("draft_attn", L.VC_TIME_CALL) if j % 2 == 0 else ("draft_attn_main", L.VC_TIME_MAIN_KERNEL)
+        self._timed(name, lambda: L.vc_draft_decode_attn(
             self.shape, self.q_draft.data_ptr(), self.kv, self.o_draft.data_ptr(), self.ws_draft.data_ptr(),
-            self.ws_draft.numel(), self.stream.cuda_stream))
+            self.ws_draft.numel(), self.stream.cuda_stream), scope)
 
     def embed_block(self):
         c = self.cfg
@@ -250,10 +271,13 @@ class Engine:
         s = self.stream.cuda_stream
         if not c.staged:
             ctx = L.vc_kv_chunk(self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, 0, self.full_cap)
-            self._timed("verify_attn", lambda: L.vc_verify_attn(
+            # even rounds time the whole call, odd rounds the attention kernel alone
+            name, scope = (("verify_attn", L.VC_TIME_CALL) if self.round_idx % 2 == 0
+                           else ("verify_attn_main", L.VC_TIME_MAIN_KERNEL))
+            self._timed(name, lambda: L.vc_verify_attn(
                 self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
                 self.ctx_len.data_ptr(), L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, self.o_ver.data_ptr(),
-                self.ws_verify.data_ptr(), self.ws_verify.numel(), s))
+                self.ws_verify.data_ptr(), self.ws_verify.numel(), s), scope)
             return
         self.verify_staged()
 

@@ -105,3 +105,13 @@ def test_stage_and_compressor_checks():
     out = C.c_size_t()
     assert L.lib.vc_tokdrop_workspace_bytes(C.byref(sh), 0, C.byref(out)) == L.VC_ERR_INVALID_ARG
     assert L.lib.vc_tokdrop_select(C.byref(sh), 0x10000, 100, 101, 0x10000, None, 0, None) == L.VC_ERR_INVALID_ARG
+
+
+def test_time_next_call_scope():
+    """The timing hook validates its scope without touching a GPU."""
+    from lossless_speculative_kv_amd import _lib as L
+    L.vc_time_next_call(None, None, L.VC_TIME_CALL)
+    L.vc_time_next_call(None, None, L.VC_TIME_MAIN_KERNEL)
+    with pytest.raises(L.VCError) as e:
+        L.vc_time_next_call(None, None, 7)
+    assert e.value.status == L.VC_ERR_INVALID_ARG

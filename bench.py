@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 
 
 def parse():
@@ -91,6 +92,20 @@ def draft_bytes_per_launch(cfg, body_len, tail_len):
 def verify_bytes_per_launch(cfg, ctx_len):
     B, Hq, Hkv, D, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.k + 1
     return sum(Hkv * (ctx_len[b] + n) * 4 * D for b in range(B)) + n * B * Hq * D * (2 + 4)
+
+
+def verify_flops_per_launch(cfg, ctx_len):
+    """Algorithmic MFMA work of one verification launch: QK^T and PV (2 * 2 * D
+    flops per query row and visible key); row j of the block sees the context
+    and block rows 0..j."""
+    B, Hq, D, n = cfg.batch, cfg.n_q_heads, cfg.head_dim, cfg.k + 1
+    return sum(Hq * (n * ctx_len[b] + n * (n + 1) / 2) * 4 * D for b in range(B))
+
+
+def mfma_entry(kernel, flops, seconds):
+    tflops = flops / seconds / 1e12 if seconds > 0 else 0.0
+    return {"kernel": kernel, "flops_per_launch": flops, "avg_launch_us": seconds * 1e6, "achieved_TFLOPs": tflops,
+            "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
 
 
 def draft_kernel_name(cfg):
@@ -218,9 +233,23 @@ def main():
     draft_bytes = draft_bytes_per_launch(cfg, mid_body, mid_tail)
     verify_bytes = verify_bytes_per_launch(cfg, [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)])
     draft_gbs = draft_bytes / t_draft_main / 1e9 if t_draft_main > 0 else 0.0
-    verify_gbs = verify_bytes / t_verify_main / 1e9 if t_verify_main > 0 else 0.0
+    t_vmain = t_verify_main if t_verify_main > 0 else t_verify_avg   # staged: whole chunked pass only
+    verify_gbs = verify_bytes / t_vmain / 1e9 if t_vmain > 0 else 0.0
 
     B, k = cfg.batch, cfg.k
+    # MFMA utilisation: algorithmic flops over the main kernel's own duration
+    mid_ctx = [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)]
+    mfma = {
+        "verify_attn": mfma_entry("verify_kernel", verify_flops_per_launch(cfg, mid_ctx), t_vmain),
+        "draft_vocab": mfma_entry("vocab product, M = batch", 2.0 * B * cfg.hidden * cfg.vocab,
+                                  avg("draft_vocab_main")),
+        "verify_vocab": mfma_entry("vocab product, M = (k+1) * batch", 2.0 * (k + 1) * B * cfg.hidden * cfg.vocab,
+                                   avg("verify_vocab_main")),
+    }
+    w_bytes = 2.0 * cfg.hidden * cfg.vocab
+    for key in ("draft_vocab", "verify_vocab"):
+        t = mfma[key]["avg_launch_us"] * 1e-6
+        mfma[key]["weight_GBs"] = w_bytes / t / 1e9 if t > 0 else 0.0
     ceiling = B * (k + 1) / (k * t_draft_avg + t_verify_avg) if (k * t_draft_avg + t_verify_avg) > 0 else 0.0
     breakdown = {name: {"avg_us": float(np.mean(v)) * 1e6, "calls": len(v)} for name, v in times.items()}
     result = {
@@ -247,8 +276,9 @@ def main():
                      "call_us": t_draft_avg * 1e6},
         "verify_attn": {"kernel": "verify_kernel", "achieved_GBs": verify_gbs, "frac": verify_gbs / HBM_PEAK_GBS,
                         "traffic": traffic_for("verify_kernel", cfg.name),
-                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_verify_main * 1e6,
+                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_vmain * 1e6,
                         "call_us": t_verify_avg * 1e6},
+        "mfma": mfma,
         "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": accepted / args.steps,
                    "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
         "round_tok_s": accepted / wall,

@@ -221,9 +221,11 @@ class Engine:
                          _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
                          self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), s)
         self.draft_attention(j)
-        self._timed("draft_vocab", lambda: L.vc_vocab_logits(
+        # even steps time the whole call, odd steps the vocab product alone
+        name, scope = ("draft_vocab", L.VC_TIME_CALL) if j % 2 == 0 else ("draft_vocab_main", L.VC_TIME_MAIN_KERNEL)
+        self._timed(name, lambda: L.vc_vocab_logits(
             c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(), self.xs[j + 1].data_ptr(),
-            None, None, self.ws_vocab_d.data_ptr(), self.ws_vocab_d.numel(), s))
+            None, None, self.ws_vocab_d.data_ptr(), self.ws_vocab_d.numel(), s), scope)
 
     def prepare_timing(self, n_calls: int):
         """Create the events of n_calls timed calls before a timed region and
@@ -298,6 +300,13 @@ class Engine:
         ready = [torch.cuda.Event() for _ in plan]
         free = [torch.cuda.Event() for _ in range(2)]
         cs.wait_stream(comp)  # committed rows of the previous round are in host memory
+        # timed: from the first chunk's verify kernel start to the last chunk's end
+        timing = None
+        if self.events is not None:
+            if not self._ev_pool:
+                raise RuntimeError("prepare_timing() was given too few calls for this timed region")
+            timing = self._ev_pool.pop()
+            self.events.append(("verify_attn",) + timing)
         for i, (t0, n) in enumerate(plan):
             buf = i % 2
             if i >= 2:
@@ -309,6 +318,9 @@ class Engine:
             comp.wait_event(ready[i])
             flags = (L.VC_VERIFY_BEGIN if i == 0 else 0) | (L.VC_VERIFY_END if i == len(plan) - 1 else 0)
             ctx = L.vc_kv_chunk(self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), c.chunk, t0, n)
+            if timing is not None and (i == 0 or i == len(plan) - 1):
+                L.vc_time_next_call(timing[0].cuda_event if i == 0 else None,
+                                    timing[1].cuda_event if i == len(plan) - 1 else None, L.VC_TIME_CALL)
             L.vc_verify_attn(self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
                              self.ctx_len.data_ptr(), flags, self.o_ver.data_ptr(), self.ws_verify.data_ptr(),
                              self.ws_verify.numel(), comp.cuda_stream)
@@ -316,9 +328,11 @@ class Engine:
 
     def verify_vocab(self):
         c = self.cfg
-        self._timed("verify_vocab", lambda: L.vc_vocab_logits(
+        name, scope = (("verify_vocab", L.VC_TIME_CALL) if self.round_idx % 2 == 0
+                       else ("verify_vocab_main", L.VC_TIME_MAIN_KERNEL))
+        self._timed(name, lambda: L.vc_vocab_logits(
             (c.k + 1) * c.batch, c.hidden, c.vocab, self.o_ver.data_ptr(), self.W.data_ptr(), self.y.data_ptr(),
-            None, None, self.ws_vocab_v.data_ptr(), self.ws_vocab_v.numel(), self.stream.cuda_stream))
+            None, None, self.ws_vocab_v.data_ptr(), self.ws_vocab_v.numel(), self.stream.cuda_stream), scope)
 
     def accept_commit(self):
         c = self.cfg

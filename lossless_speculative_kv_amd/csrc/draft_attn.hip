@@ -911,20 +911,34 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
 // result does not depend on the order in which workgroups ran.
 template <int D>
 __global__ __launch_bounds__(D) void draft_merge_kernel(const DraftParams P) {
+  constexpr int kBatch = 8;  // splits whose loads are issued together
   const int c = threadIdx.x, hq = blockIdx.x, b = blockIdx.y;
   const size_t row0 = ((size_t)b * P.Hq + hq) * P.S;
-  float M = kNegInf;
-  for (int s = 0; s < P.S; ++s) M = fmaxf(M, P.part_ml[(row0 + s) * 2]);
-  float O = 0.f, L = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < P.S; ++s) {
-      const float ms = P.part_ml[(row0 + s) * 2];
-      if (ms != kNegInf) {
-        const float a = fast_exp2(ms - M);
-        O += P.part_o[(row0 + s) * D + c] * a;
-        L += P.part_ml[(row0 + s) * 2 + 1] * a;
-      }
+  float M = kNegInf, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < P.S; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch], os[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const size_t r = row0 + min(s0 + i, P.S - 1);
+      ms[i] = s0 + i < P.S ? P.part_ml[r * 2] : kNegInf;
+      ls[i] = P.part_ml[r * 2 + 1];
+      os[i] = P.part_o[r * D + c];
     }
+    float mx = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
+    if (mx == kNegInf) continue;  // nothing visible so far
+    const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
+    O *= a;
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const bool ok = ms[i] != kNegInf;
+      const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
+      O = ok ? fmaf(os[i], w, O) : O;
+      L = ok ? fmaf(ls[i], w, L) : L;
+    }
+    M = mx;
   }
   P.out[((size_t)b * P.Hq + hq) * D + c] = (L > 0.f) ? O / L : 0.f;
 }

@@ -6,15 +6,22 @@
 // Work decomposition: one workgroup per (context split, KV head, sequence),
 // one per CU (its LDS ring keeps a second one out). All R = n_rows * g query
 // rows of the KV head (row = j * g + head, j the draft position) live in the
-// workgroup, RT row tiles of 16 per consumer wave, so each K/V tile is read
-// from HBM once for every row tile. K/V move in 32-token tiles through a
-// 6-stage LDS ring filled by direct-to-LDS buffer loads issued by two
-// producer waves (K and V halves; no registers, four tiles in flight ahead
-// of the one being computed); one workgroup barrier per tile. Only the
-// producers issue such loads, so the consumers' LDS reads never wait on them.
+// workgroup, RT row tiles of 16 per row group, so each K/V tile is read from
+// HBM once for every row tile. K/V move in 32-token tiles through an LDS
+// ring filled by direct-to-LDS buffer loads issued by two producer waves (K
+// and V halves; no registers); only the producers issue such loads, so the
+// consumers' LDS reads never wait on them. Up to 9 row tiles, each row group
+// has two consumer waves that take the even and odd tiles of each two-tile
+// step (8-stage ring): a SIMD then holds waves of two groups, whose softmax
+// (VALU) and products (MFMA) overlap; the pair's states merge through LDS at
+// the end. Beyond 9 row tiles, one wave per group takes every tile (6-stage
+// ring).
 //   QK: S^T[token][row] on v_mfma_f32_16x16x32_bf16, A = 16 key rows (LDS,
 //       rows XOR-swizzled in 16-byte units so the 16 rows of a read hit
 //       distinct banks), B = 16 query rows (registers, exact bf16).
+//   softmax: log2 domain; the 1/sqrt(D) * log2(e) scale is folded into the
+//       exponent's FMA; the row sums come from one more MFMA of P^T with a
+//       ones operand (the same bf16 probabilities as the numerator).
 //   PV: O^T[channel][row] += V^T[channel][token] * P^T[token][row]; the V^T
 //       operand comes straight from the row-major V tile through the gfx950
 //       transposing LDS read (four token slots of one channel per lane).
@@ -46,9 +53,7 @@ struct VerifyParams {
   float qscale;
 };
 
-constexpr int kTT = 32;     // tokens per tile
-constexpr int kStages = 6;  // LDS ring depth
-constexpr int kAhead = 4;   // tiles in flight ahead of the one computed (<= kStages - 2)
+constexpr int kTT = 32;  // tokens per tile
 
 template <int D>
 struct Tile {
@@ -108,14 +113,83 @@ __device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int t
   }
 }
 
+// Online-softmax state of RT row tiles. The row sums live in an MFMA
+// accumulator (lsum): P^T contracted with a ones operand, so each sum is
+// complete after the MFMA (no cross-lane reduction) and uses the same bf16
+// probabilities as the numerator.
+template <int RT, int MT>
+struct VState {
+  float m[RT];  // running max (log2 domain, scaled), identical on all lanes of a column
+  f32x4 acc[RT][MT];
+  f32x4 lsum[RT];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      m[rt] = kNegInf;
+      lsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+// Raw scores s (unscaled q.k, -inf where masked) of one tile become
+// p = 2^(s * qscale - m). The running max moves only when the tile's max
+// exceeds it by more than kRescaleThreshold (so p <= 2^8), which keeps the
+// accumulator rescale rare; the result is the same softmax.
+// Maximum that propagates NaN (v_maximum3_f32): unlike fmaxf it needs no
+// canonicalising of operands that come from the MFMA or a lane permute.
+// Scores are finite or -inf on every row whose result is kept.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax_q(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int RT, int MT>
+__device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT][2][4], float qscale) {
+  float bm[RT];
+  bool need = false;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float x = vmax(vmax(vmax(s[rt][0][0], s[rt][0][1]), vmax(s[rt][0][2], s[rt][0][3])),
+                         vmax(vmax(s[rt][1][0], s[rt][1][1]), vmax(s[rt][1][2], s[rt][1][3])));
+    bm[rt] = vmax_q(x) * qscale;
+    need = need || (bm[rt] > st.m[rt] + kRescaleThreshold);
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const bool up = bm[rt] > st.m[rt] + kRescaleThreshold;
+      const float alpha = up ? fast_exp2(st.m[rt] - bm[rt]) : 1.f;
+      st.m[rt] = up ? bm[rt] : st.m[rt];
+      st.lsum[rt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) st.acc[rt][t] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    // a row that has seen no visible token yet (max still -inf) gets p = 0
+    // from its -inf scores instead of 2^(-inf + inf)
+    const float nm = st.m[rt] == kNegInf ? 0.f : -st.m[rt];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[rt][i][r] = fast_exp2(fmaf(s[rt][i][r], qscale, nm));
+  }
+}
+
 // One 32-token tile for this wave's RT row tiles. nvalid masks tokens for
 // all rows; token t is visible to row tile rt's rows only when t <= lim[rt]
 // (the causal limit in the draft block, relative to the tile's first token;
 // large for context tiles).
-template <int D, int RT>
+template <int D, int RT, bool MASK>
 __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int lane,
                                              const uint32_t (&Bq)[RT][D / 32][4], const int (&lim)[RT],
-                                             float qscale, SoftState<RT, D / 16>& st) {
+                                             float qscale, VState<RT, D / 16>& st) {
   constexpr int NG = D / 32, MT = D / 16;
   using T = Tile<D>;
   const int n = lane & 15, qg = lane >> 4;
@@ -137,11 +211,12 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * i + 4 * qg + r;
-        s[rt][i][r] = (t < nvalid && t <= lim[rt]) ? c[r] * qscale : kNegInf;
+        if constexpr (MASK) s[rt][i][r] = (t < nvalid && t <= lim[rt]) ? c[r] : kNegInf;
+        else s[rt][i][r] = c[r];
       }
     }
   }
-  softmax_block<RT, MT>(st, s);
+  verify_softmax<RT, MT>(st, s, qscale);
   uint32_t Bp[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -172,40 +247,35 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
           mfma_bf16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]}, st.acc[rt][m]);
     }
   }
+  constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+    st.lsum[rt] = mfma_bf16(u32x4{kOnes, kOnes, kOnes, kOnes}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]},
+                            st.lsum[rt]);
 }
 
-// Waves 0..NW-1 compute (RT row tiles each); waves NW and NW+1 load.
-template <int D, int RT>
+// Consumer waves compute, the last two waves load. Without PAIR, consumer
+// wave w holds row tiles RT*w .. RT*w+RT-1 and computes every tile, one tile
+// per workgroup barrier. With PAIR, waves w and w + NW (NW row groups) hold
+// the same row tiles and take the even and odd tiles of each two-tile step:
+// the two waves of a pair sit on different SIMDs next to a wave of another
+// pair, so one wave's softmax (VALU) runs while another's products (MFMA)
+// do, and the pair's two partial states are merged through LDS at the end.
+template <int D, int RT, bool PAIR>
 __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   constexpr int NG = D / 32, MT = D / 16;
+  constexpr int TPS = PAIR ? 2 : 1;          // tiles per barrier step
+  constexpr int STAGES = PAIR ? 8 : 6;       // LDS ring depth in tiles
+  constexpr int AHEAD = STAGES / TPS - 2;    // steps in flight ahead of the one computed
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char ring[kStages * 2 * T::KB];
+  __shared__ __attribute__((aligned(16))) char ring[STAGES * 2 * T::KB];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x / 64 - 2;
+  const int ncons = blockDim.x / 64 - 2;
+  const int nw = ncons / TPS;  // row groups
+  const int grp = wave % nw, parity = wave / nw;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
   const int n = lane & 15, qg = lane >> 4;
-
-  // query operands of this wave's row tiles (unscaled bf16, exact)
-  uint32_t Bq[RT][NG][4];
-  int rowj[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = 16 * (wave * RT + rt) + n;
-    const bool ok = row < P.R;
-    const int jj = ok ? row / P.g : 0, hl = ok ? row % P.g : 0;
-    rowj[rt] = ok ? jj : -1;
-    const uint16_t* qp = P.q + (((size_t)jj * P.B + b) * P.Hq + (size_t)hk * P.g + hl) * D + qg * (D / 4);
-#pragma unroll
-    for (int kk = 0; kk < NG; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(qp + 8 * kk);
-      Bq[rt][kk][0] = v[0];
-      Bq[rt][kk][1] = v[1];
-      Bq[rt][kk][2] = v[2];
-      Bq[rt][kk][3] = v[3];
-    }
-  }
 
   // segment 0: context rows [r0, r0 + nval) of the chunk, visible below ctx_len
   const int ctx = P.ctx_len[b];
@@ -227,49 +297,126 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   s1.row_bytes = stride * 2;
   s1.ntiles = with_block ? (P.NR + kTT - 1) / kTT : 0;
   const int ntiles = s0.ntiles + s1.ntiles;
+  const int nsteps = (ntiles + TPS - 1) / TPS;
 
-  if (wave >= nw) {
-    // producer: K (wave nw) or V (wave nw + 1) halves, kAhead tiles ahead
-    const int half = wave - nw;
+  if (wave >= ncons) {
+    // producer: K (first) or V (second) halves, AHEAD steps ahead
+    const int half = wave - ncons;
     auto issue = [&](int t) {
-      char* stage = ring + (t % kStages) * 2 * T::KB;
+      char* stage = ring + (t % STAGES) * 2 * T::KB;
       t = min(t, ntiles - 1);  // past the end: reload the last tile into an unused stage
       if (t < s0.ntiles) issue_half<D>(stage, s0, t, lane, half);
       else issue_half<D>(stage, s1, t - s0.ntiles, lane, half);
     };
     if (ntiles > 0) {
-      for (int t = 0; t < kAhead; ++t) issue(t);
-      for (int t = 0; t < ntiles; ++t) {
-        issue(t + kAhead);
-        wait_vm<kAhead * T::CHUNKS>();  // tile t landed
+      for (int t = 0; t < AHEAD * TPS; ++t) issue(t);
+      for (int st = 0; st < nsteps; ++st) {
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) issue((st + AHEAD) * TPS + i);
+        wait_vm<AHEAD * TPS * T::CHUNKS>();  // step st landed
         __builtin_amdgcn_s_barrier();
       }
       wait_vm<0>();  // nothing may land after the workgroup has gone
     }
+    if constexpr (PAIR) {
+      // the consumers' two hand-over barriers (the first one also tells them
+      // that no load into the ring is in flight any more)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+    }
     return;
   }
 
-  SoftState<RT, MT> st;
-  st.init();
-  for (int t = 0; t < ntiles; ++t) {
-    // pairs with the producers' bare barrier; the fence keeps this tile's LDS
-    // reads below it (consumers have no loads in flight, so it costs nothing)
-    __syncthreads();
-    const char* stage = ring + (t % kStages) * 2 * T::KB;
-    const bool blk = t >= s0.ntiles;
-    const int tb = t - s0.ntiles;
-    int lim[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) lim[rt] = blk ? rowj[rt] - tb * kTT : kTT;
-    const int nv = blk ? min(kTT, P.NR - tb * kTT) : min(kTT, nval - t * kTT);
-    tile_compute<D, RT>(stage, nv, lane, Bq, lim, P.qscale, st);
-  }
-
-  // partial for this split: rows of this wave
+  // query operands of this wave's row tiles (unscaled bf16, exact)
+  uint32_t Bq[RT][NG][4];
+  int rowj[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = 16 * (wave * RT + rt) + n;
-    const float l = sum_q(st.l[rt]);
+    const int row = 16 * (grp * RT + rt) + n;
+    const bool ok = row < P.R;
+    const int jj = ok ? row / P.g : 0, hl = ok ? row % P.g : 0;
+    rowj[rt] = ok ? jj : -1;
+    const uint16_t* qp = P.q + (((size_t)jj * P.B + b) * P.Hq + (size_t)hk * P.g + hl) * D + qg * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < NG; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(qp + 8 * kk);
+      Bq[rt][kk][0] = v[0];
+      Bq[rt][kk][1] = v[1];
+      Bq[rt][kk][2] = v[2];
+      Bq[rt][kk][3] = v[3];
+    }
+  }
+
+  VState<RT, MT> st;
+  st.init();
+  // steps made of full context tiles need no mask; the partial last context
+  // tile and the causal draft-block tiles follow in a second loop
+  const int nfull_steps = (nval / kTT) / TPS;
+  int lim_all[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) lim_all[rt] = kTT;
+  for (int sp = 0; sp < nfull_steps; ++sp) {
+    // pairs with the producers' bare barrier; the fence keeps this step's LDS
+    // reads below it (consumers have no loads in flight, so it costs nothing)
+    __syncthreads();
+    const int t = sp * TPS + parity;
+    tile_compute<D, RT, false>(ring + (t % STAGES) * 2 * T::KB, kTT, lane, Bq, lim_all, P.qscale, st);
+  }
+  for (int sp = nfull_steps; sp < nsteps; ++sp) {
+    __syncthreads();
+    const int t = sp * TPS + parity;
+    if (t < ntiles) {
+      const char* stage = ring + (t % STAGES) * 2 * T::KB;
+      const bool blk = t >= s0.ntiles;
+      const int tb = t - s0.ntiles;
+      int lim[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) lim[rt] = blk ? rowj[rt] - tb * kTT : kTT;
+      const int nv = blk ? min(kTT, P.NR - tb * kTT) : min(kTT, nval - t * kTT);
+      tile_compute<D, RT, true>(stage, nv, lane, Bq, lim, P.qscale, st);
+    }
+  }
+
+  if constexpr (PAIR) {
+    // hand the odd wave's state to the even wave through the (now idle) ring:
+    // per row tile MT*4 accumulator words, the max and the sum, lane-major
+    __syncthreads();
+    constexpr int WORDS = MT * 4 + 2;
+    float* xa = reinterpret_cast<float*>(ring) + (size_t)grp * RT * WORDS * 64 + lane;
+    if (parity == 1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xa[(rt * WORDS + 4 * m + r) * 64] = st.acc[rt][m][r];
+        xa[(rt * WORDS + MT * 4) * 64] = st.m[rt];
+        xa[(rt * WORDS + MT * 4 + 1) * 64] = st.lsum[rt][0];
+      }
+    }
+    __syncthreads();
+    if (parity == 1) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mb = xa[(rt * WORDS + MT * 4) * 64], lb = xa[(rt * WORDS + MT * 4 + 1) * 64];
+      const float ma = st.m[rt], mx = vmax(ma, mb);
+      const float fa = ma == kNegInf ? 0.f : fast_exp2(ma - mx);
+      const float fb = mb == kNegInf ? 0.f : fast_exp2(mb - mx);
+      st.m[rt] = mx;
+      st.lsum[rt][0] = st.lsum[rt][0] * fa + lb * fb;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.acc[rt][m][r] = st.acc[rt][m][r] * fa + xa[(rt * WORDS + 4 * m + r) * 64] * fb;
+    }
+  }
+
+  // partial for this split: rows of this wave's row tiles
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * (grp * RT + rt) + n;
+    const float l = st.lsum[rt][0];
     if (row < P.R) {
       const size_t pr = (unit * P.S + split) * P.R + row;
       float* o = P.part_o + pr * D;
@@ -283,9 +430,11 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   }
 }
 
-// Fold this call's splits (in order) into the running state; on END write out.
+// Fold this call's splits (in order, eight at a time: the loads of a batch
+// are issued together) into the running state; on END write out.
 template <int D>
 __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
+  constexpr int kBatch = 8;
   const int c = threadIdx.x, row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
   const size_t rr = unit * P.R + row;
@@ -295,21 +444,30 @@ __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
     L = P.run_ml[rr * 2 + 1];
     O = P.run_o[rr * D + c];
   }
-  for (int s = 0; s < P.S; ++s) {
-    const size_t pr = (unit * P.S + s) * P.R + row;
-    const float ms = P.part_ml[pr * 2];
-    if (ms == kNegInf) continue;
-    const float ls = P.part_ml[pr * 2 + 1], os = P.part_o[pr * D + c];
-    if (ms > M) {
-      const float a = fast_exp2(M - ms);  // 0 when M is -inf
-      O = O * a + os;
-      L = L * a + ls;
-      M = ms;
-    } else {
-      const float a = fast_exp2(ms - M);
-      O += os * a;
-      L += ls * a;
+  for (int s0 = 0; s0 < P.S; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch], os[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const size_t pr = (unit * P.S + min(s0 + i, P.S - 1)) * P.R + row;
+      ms[i] = s0 + i < P.S ? P.part_ml[pr * 2] : kNegInf;
+      ls[i] = P.part_ml[pr * 2 + 1];
+      os[i] = P.part_o[pr * D + c];
     }
+    float mx = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
+    if (mx == kNegInf) continue;  // nothing visible so far
+    const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
+    O *= a;
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const bool ok = ms[i] != kNegInf;
+      const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
+      O = ok ? fmaf(os[i], w, O) : O;
+      L = ok ? fmaf(ls[i], w, L) : L;
+    }
+    M = mx;
   }
   if (P.flags & VC_VERIFY_END) {
     const int j = row / P.g, hl = row % P.g;
@@ -324,17 +482,23 @@ __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
 }
 
 template <int D>
-void launch_verify(const VerifyParams& P, int rt, int nwaves, dim3 grid, hipStream_t s, hipEvent_t start,
-                   hipEvent_t stop) {
+void launch_verify(const VerifyParams& P, int rt, bool pair, int nwaves, dim3 grid, hipStream_t s,
+                   hipEvent_t start, hipEvent_t stop) {
   const dim3 block(64 * (nwaves + 2));
-  if (rt == 2) launch_ev(verify_kernel<D, 2>, grid, block, 0, s, start, stop, P);
-  else launch_ev(verify_kernel<D, 3>, grid, block, 0, s, start, stop, P);
+  if (pair) {
+    if (rt == 2) launch_ev(verify_kernel<D, 2, true>, grid, block, 0, s, start, stop, P);
+    else launch_ev(verify_kernel<D, 3, true>, grid, block, 0, s, start, stop, P);
+  } else {
+    if (rt == 2) launch_ev(verify_kernel<D, 2, false>, grid, block, 0, s, start, stop, P);
+    else launch_ev(verify_kernel<D, 3, false>, grid, block, 0, s, start, stop, P);
+  }
 }
 
 }  // namespace
 
 struct VerifyPlan {
   int rt, nwaves, tps, s_ctx;
+  bool pair;
 };
 
 // Row tiling: two row tiles per consumer wave up to 12 tiles, else three (at
@@ -347,8 +511,11 @@ struct VerifyPlan {
 VerifyPlan verify_plan(const vc_attn_shape& sh, int n_rows, int chunk_tokens) {
   const int R = n_rows * (sh.n_q_heads / sh.n_kv_heads);
   const int tiles = (R + 15) / 16;
-  const int rt = tiles > 12 ? 3 : 2;
-  const int nwaves = (tiles + rt - 1) / rt;
+  // up to 9 row tiles: wave pairs (at most 3 groups, 6 consumer waves);
+  // beyond: one wave per group of three row tiles (at most 6 waves)
+  const bool pair = tiles <= 9;
+  const int rt = (pair && tiles <= 6) ? 2 : 3;
+  const int nwaves = ((tiles + rt - 1) / rt) * (pair ? 2 : 1);
   const long long units = (long long)sh.batch * sh.n_kv_heads;
   const long long ctx_tiles = ((long long)chunk_tokens + kTT - 1) / kTT;
   long long s_ctx = (256 + units - 1) / units;
@@ -356,7 +523,7 @@ VerifyPlan verify_plan(const vc_attn_shape& sh, int n_rows, int chunk_tokens) {
   if (s_ctx > max_s) s_ctx = max_s;
   if (s_ctx < 1) s_ctx = 1;
   const long long tps = ((ctx_tiles + s_ctx - 1) / s_ctx) * kTT;
-  return VerifyPlan{rt, nwaves, (int)(tps > 0 ? tps : kTT), (int)s_ctx};
+  return VerifyPlan{rt, nwaves, (int)(tps > 0 ? tps : kTT), (int)s_ctx, pair};
 }
 
 int verify_max_rows() { return 6 * 3 * 16; }
@@ -418,8 +585,8 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   const dim3 grid(P.S, sh.n_kv_heads, sh.batch);
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
-  if (sh.head_dim == 128) launch_verify<128>(P, plan.rt, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
-  else launch_verify<64>(P, plan.rt, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
+  if (sh.head_dim == 128) launch_verify<128>(P, plan.rt, plan.pair, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
+  else launch_verify<64>(P, plan.rt, plan.pair, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
   vc_status st = check_launch("verify attention");
   if (st != VC_OK) return st;
   const dim3 mgrid((unsigned)R, sh.n_kv_heads, sh.batch);

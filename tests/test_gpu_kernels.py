@@ -234,6 +234,8 @@ VERIFY_CASES = [
     (2, 40, 8, 128, 26, [700, 64], None),
     (1, 32, 8, 128, 41, [1111], 512),
     (2, 8, 2, 128, 1, [33, 1], None),
+    (2, 16, 2, 128, 36, [1024, 300], None),   # R = 288, the largest row count; ragged context
+    (1, 36, 4, 128, 15, [1024], None),        # R = 135: nine row tiles, the last one partly filled
 ]
 
 

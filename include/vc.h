@@ -89,19 +89,25 @@ typedef struct {
  *   groups of 32 tokens, values per token over groups of 32 channels, each
  *   group with an fp16 scale and zero point (x = code * scale + zero). The
  *   tail holds the most recent tokens unquantised, as fp16. body_len[b] must
- *   be a multiple of 32. Stored layout (per sequence b and KV head h, with
- *   u = b * n_kv_heads + h, Tc = body_cap):
- *     k_codes uint32 [u][Tc][D*bits/32]: token-major; channel d of a token in
- *             word floor(d*bits/32) at bit (d*bits) % 32, LSB first.
- *     k_scale, k_zero fp16 [u][Tc/32][D].
- *     v_codes uint32 [u][Tc/32][64][D*bits/64]: per 32-token block, 64 lanes
- *             L = 16*q + c (q 0..3, c 0..15); lane L holds channels 16*m + c
- *             (m 0..D/16-1) of the tokens tau(q,s) = 4*q + s/2 + 16*(s%2)
- *             (s 0..7); code (m, s) in word (m*bits)/4 at bit
- *             8*(s/2) + 4*(s%2) + 2*(m%2)             for bits = 2,
- *             16*(s/4) + 8*(s%2) + 4*((s/2)%2)        for bits = 4.
- *     v_scale, v_zero fp16 [u][Tc/32][D/32][32]: entry 8*q + s of channel
- *             group j is the parameter of token tau(q,s) of the block.
+ *   be a multiple of 32. Stored layout: the body is block-major, one record
+ *   of BLK = 8 * D * (bits + 1) bytes (vc_kivi_block_bytes) per 32-token
+ *   block, kivi_blocks [u][body_cap/32][BLK] with u = b * n_kv_heads + h, so
+ *   that a block is one contiguous read. A record holds, at byte offsets:
+ *     0          key codes uint32 [32][D*bits/32]: token-major; channel d of
+ *                a token in word floor(d*bits/32) at bit (d*bits) % 32, LSB
+ *                first.
+ *     4*D*bits   value codes uint32 [64][D*bits/64]: lanes L = 16*q + c
+ *                (q 0..3, c 0..15); lane L holds channels 16*m + c
+ *                (m 0..D/16-1) of the tokens tau(q,s) = 4*q + s/2 + 16*(s%2)
+ *                (s 0..7); code (m, s) in word (m*bits)/4 at bit
+ *                8*(s/2) + 4*(s%2) + 2*(m%2)             for bits = 2,
+ *                16*(s/4) + 8*(s%2) + 4*((s/2)%2)        for bits = 4.
+ *     8*D*bits   key scale fp16 [D] (per channel, over the block's tokens),
+ *                then key zero fp16 [D].
+ *     8*D*bits + 4*D
+ *                value scale fp16 [D/32][32], then value zero fp16
+ *                [D/32][32]: entry 8*q + s of channel group j is the
+ *                parameter of token tau(q,s) of the block.
  * VC_DRAFT_TOKDROP: the body is a sorted list of kept token positions
  *   kept_idx int32 [u][body_cap] (ascending, each < src_t_cap) into the bf16
  *   source rows src_k / src_v [u][src_t_cap][D]; the tail is bf16.
@@ -117,15 +123,15 @@ typedef struct {
   int32_t tail_cap;   /* tail capacity in tokens (multiple of 32) */
   const int32_t *body_len; /* [B] */
   const int32_t *tail_len; /* [B], >= 1 when attending */
-  const uint32_t *k_codes;
-  const void *k_scale, *k_zero;
-  const uint32_t *v_codes;
-  const void *v_scale, *v_zero;
+  const void *kivi_blocks; /* KIVI body records, 256-byte aligned */
   const int32_t *kept_idx;
   const void *src_k, *src_v;
   int32_t src_t_cap;
   const void *tail_k, *tail_v;
 } vc_draft_kv;
+
+/* Bytes of one KIVI block record: 8 * head_dim * (bits + 1). */
+vc_status vc_kivi_block_bytes(int32_t head_dim, int32_t bits, size_t *bytes);
 
 /* Workspace size for vc_draft_decode_attn with this shape and cache. */
 vc_status vc_draft_workspace_bytes(const vc_attn_shape *shape, const vc_draft_kv *kv, size_t *bytes);
@@ -212,10 +218,7 @@ vc_status vc_greedy_accept(int32_t batch, int32_t k, const int32_t *x, const int
 typedef struct {
   int32_t kind, bits, body_cap, tail_cap;
   int32_t *body_len, *tail_len;
-  uint32_t *k_codes;
-  void *k_scale, *k_zero;
-  uint32_t *v_codes;
-  void *v_scale, *v_zero;
+  void *kivi_blocks;
   void *tail_k, *tail_v;
   int32_t residual; /* KIVI: recent-token window R kept unquantised */
 } vc_draft_cache;

@@ -19,7 +19,7 @@ VC_VERIFY_BEGIN, VC_VERIFY_END = 1, 2
 VC_TIME_CALL, VC_TIME_MAIN_KERNEL = 0, 1
 
 EXPORTS = [
-    "vc_version", "vc_last_error", "vc_time_next_call", "vc_draft_workspace_bytes", "vc_draft_decode_attn",
+    "vc_version", "vc_last_error", "vc_time_next_call", "vc_kivi_block_bytes", "vc_draft_workspace_bytes", "vc_draft_decode_attn",
     "vc_verify_workspace_bytes", "vc_verify_attn", "vc_vocab_workspace_bytes", "vc_vocab_logits",
     "vc_greedy_accept", "vc_commit_workspace_bytes", "vc_commit_round", "vc_kivi_quantize",
     "vc_tokdrop_workspace_bytes", "vc_tokdrop_select", "vc_stage_full_kv",
@@ -40,8 +40,7 @@ class vc_attn_shape(C.Structure):
 class vc_draft_kv(C.Structure):
     _fields_ = [("kind", C.c_int32), ("bits", C.c_int32), ("body_cap", C.c_int32), ("tail_cap", C.c_int32),
                 ("body_len", C.c_void_p), ("tail_len", C.c_void_p),
-                ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
-                ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p),
+                ("kivi_blocks", C.c_void_p),
                 ("kept_idx", C.c_void_p), ("src_k", C.c_void_p), ("src_v", C.c_void_p),
                 ("src_t_cap", C.c_int32), ("tail_k", C.c_void_p), ("tail_v", C.c_void_p)]
 
@@ -54,8 +53,7 @@ class vc_kv_chunk(C.Structure):
 class vc_draft_cache(C.Structure):
     _fields_ = [("kind", C.c_int32), ("bits", C.c_int32), ("body_cap", C.c_int32), ("tail_cap", C.c_int32),
                 ("body_len", C.c_void_p), ("tail_len", C.c_void_p),
-                ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
-                ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p),
+                ("kivi_blocks", C.c_void_p),
                 ("tail_k", C.c_void_p), ("tail_v", C.c_void_p), ("residual", C.c_int32)]
 
 
@@ -80,6 +78,7 @@ _sigs = {
     "vc_version": ([], C.c_char_p),
     "vc_last_error": ([], C.c_char_p),
     "vc_time_next_call": ([_P, _P, C.c_int32], C.c_int32),
+    "vc_kivi_block_bytes": ([C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "vc_draft_workspace_bytes": ([_S, C.POINTER(vc_draft_kv), C.POINTER(C.c_size_t)], C.c_int32),
     "vc_draft_decode_attn": ([_S, _P, C.POINTER(vc_draft_kv), _P, _P, C.c_size_t, _P], C.c_int32),
     "vc_verify_workspace_bytes": ([_S, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
@@ -128,6 +127,10 @@ def _size(fn, *args) -> int:
 
 
 # --- entry points with the C names (raise VCError on a non-OK status) -------
+
+def vc_kivi_block_bytes(head_dim: int, bits: int) -> int:
+    return _size(lib.vc_kivi_block_bytes, head_dim, bits)
+
 
 def vc_draft_workspace_bytes(shape: vc_attn_shape, kv: vc_draft_kv) -> int:
     return _size(lib.vc_draft_workspace_bytes, C.byref(shape), C.byref(kv))

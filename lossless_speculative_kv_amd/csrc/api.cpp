@@ -115,12 +115,7 @@ vc_status check_draft_kv(const vc_attn_shape* sh, const vc_draft_kv* kv) {
     case VC_DRAFT_KIVI:
       if (kv->bits != 2 && kv->bits != 4) return fail(VC_ERR_UNSUPPORTED, "KIVI bits %d (supported: 2, 4)", kv->bits);
       if (kv->body_cap % 32) return fail(VC_ERR_INVALID_ARG, "KIVI body_cap %d must be a multiple of 32", kv->body_cap);
-      VC_REQ(kv->k_codes, 16, "k_codes");
-      VC_REQ(kv->v_codes, 16, "v_codes");
-      VC_REQ(kv->k_scale, 16, "k_scale");
-      VC_REQ(kv->k_zero, 16, "k_zero");
-      VC_REQ(kv->v_scale, 16, "v_scale");
-      VC_REQ(kv->v_zero, 16, "v_zero");
+      VC_REQ(kv->kivi_blocks, 256, "kivi_blocks");
       break;
     case VC_DRAFT_TOKDROP:
       VC_REQ(kv->kept_idx, 4, "kept_idx");
@@ -165,6 +160,15 @@ vc_status vc_time_next_call(void* start_event, void* stop_event, int32_t scope) 
   vc::g_timing.start = static_cast<hipEvent_t>(start_event);
   vc::g_timing.stop = static_cast<hipEvent_t>(stop_event);
   vc::g_timing.scope = scope;
+  return VC_OK;
+}
+
+vc_status vc_kivi_block_bytes(int32_t head_dim, int32_t bits, size_t* bytes) {
+  TimingClear timing_clear;
+  if (head_dim != 64 && head_dim != 128) return fail(VC_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (bits != 2 && bits != 4) return fail(VC_ERR_UNSUPPORTED, "KIVI bits %d (supported: 2, 4)", bits);
+  if (bytes == nullptr) return fail(VC_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = (size_t)8 * head_dim * (bits + 1);
   return VC_OK;
 }
 
@@ -279,12 +283,14 @@ vc_status vc_greedy_accept(int32_t batch, int32_t k, const int32_t* x, const int
   return vc::accept_launch(batch, k, x, y, n_accept, next_token, committed, stream);
 }
 
+static size_t commit_ws_bytes(const vc_attn_shape& sh) { return ((size_t)sh.batch * 4 + 255) / 256 * 256; }
+
 vc_status vc_commit_workspace_bytes(const vc_attn_shape* shape, size_t* bytes) {
   TimingClear timing_clear;
   vc_status st;
   if ((st = check_shape(shape)) != VC_OK) return st;
   if (bytes == nullptr) return fail(VC_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = ((size_t)shape->batch * 4 + 255) / 256 * 256;
+  *bytes = commit_ws_bytes(*shape);
   return VC_OK;
 }
 
@@ -317,18 +323,11 @@ vc_status vc_commit_round(const vc_attn_shape* shape, int32_t k, const int32_t* 
     if (draft->body_cap % 32) return fail(VC_ERR_INVALID_ARG, "body_cap %d", draft->body_cap);
     if (draft->residual < 0 || draft->residual % 32)
       return fail(VC_ERR_INVALID_ARG, "residual %d must be a non-negative multiple of 32", draft->residual);
-    VC_REQ(draft->k_codes, 16, "draft.k_codes");
-    VC_REQ(draft->v_codes, 16, "draft.v_codes");
-    VC_REQ(draft->k_scale, 16, "draft.k_scale");
-    VC_REQ(draft->k_zero, 16, "draft.k_zero");
-    VC_REQ(draft->v_scale, 16, "draft.v_scale");
-    VC_REQ(draft->v_zero, 16, "draft.v_zero");
+    VC_REQ(draft->kivi_blocks, 256, "draft.kivi_blocks");
   } else if (draft->kind != VC_DRAFT_TOKDROP && draft->kind != VC_DRAFT_DENSE) {
     return fail(VC_ERR_UNSUPPORTED, "draft kind %d", draft->kind);
   }
-  size_t need = 0;
-  vc_commit_workspace_bytes(shape, &need);
-  if ((st = check_ws(ws, ws_bytes, need)) != VC_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, commit_ws_bytes(*shape))) != VC_OK) return st;
   return vc::commit_launch(*shape, k, n_accept, k_new, v_new, full_k, full_v, full_t_cap, ctx_len, *draft, status_flags,
                            static_cast<int32_t*>(ws), stream);
 }
@@ -349,12 +348,7 @@ vc_status vc_kivi_quantize(const vc_attn_shape* shape, const void* src_k, const 
   VC_REQ(src_v, 16, "src_v");
   VC_REQ(draft->body_len, 4, "draft.body_len");
   VC_REQ(draft->tail_len, 4, "draft.tail_len");
-  VC_REQ(draft->k_codes, 16, "draft.k_codes");
-  VC_REQ(draft->v_codes, 16, "draft.v_codes");
-  VC_REQ(draft->k_scale, 16, "draft.k_scale");
-  VC_REQ(draft->k_zero, 16, "draft.k_zero");
-  VC_REQ(draft->v_scale, 16, "draft.v_scale");
-  VC_REQ(draft->v_zero, 16, "draft.v_zero");
+  VC_REQ(draft->kivi_blocks, 256, "draft.kivi_blocks");
   if (n_tail > 0) {
     VC_REQ(draft->tail_k, 16, "draft.tail_k");
     VC_REQ(draft->tail_v, 16, "draft.tail_v");

@@ -59,12 +59,7 @@ struct DraftParams {
   int body_cap, tail_cap, src_t_cap;
   const int32_t* body_len;
   const int32_t* tail_len;
-  const uint32_t* k_codes;
-  const uint16_t* k_scale;
-  const uint16_t* k_zero;
-  const uint32_t* v_codes;
-  const uint16_t* v_scale;
-  const uint16_t* v_zero;
+  const char* kivi_blocks;  // KIVI body records [u][body_cap/32][BlockLayout::BYTES]
   const int32_t* kept_idx;
   const uint16_t* src_k;
   const uint16_t* src_v;
@@ -259,9 +254,10 @@ __device__ __forceinline__ void row_scores(const f32x4 (&c)[2], float scale, flo
 }
 
 // ------------------------------------------------------- KIVI body block ----
-// Each wave streams its own 32-token blocks into a private 3-stage LDS ring
-// with direct-to-LDS buffer loads issued two blocks ahead, then reads its
-// operands from LDS. One stage holds a block's six pieces back to back.
+// Each wave streams its own 32-token blocks into a private LDS ring with
+// direct-to-LDS buffer loads issued ahead, then reads its operands from LDS.
+// A block's record in memory has the same layout as its ring stage, so one
+// block is one contiguous copy (1 KB per load instruction where it can).
 template <int D, int BITS>
 struct BlockLayout {
   static constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64;
@@ -272,10 +268,11 @@ struct BlockLayout {
   static constexpr int VS = KZ + KS_B, VS_B = NG * 32 * 2;  // value scales / zeros
   static constexpr int VZ = VS + VS_B;
   static constexpr int BYTES = VZ + VS_B;
-  // direct-to-LDS instructions per piece: 1 KB (16 B per lane), then 256 B
+  static_assert(BYTES == 8 * D * (BITS + 1), "record size");
+  // direct-to-LDS instructions per block: 1 KB (16 B per lane), then 256 B
   // (4 B per lane), then a 128 B rest (4 B for half the lanes)
   static constexpr int pieces(int b) { return b / 1024 + (b % 1024) / 256 + ((b % 256) ? 1 : 0); }
-  static constexpr int NI = pieces(KC_B) + pieces(VC_B) + 2 * pieces(KS_B) + 2 * pieces(VS_B);
+  static constexpr int NI = pieces(BYTES);
   static_assert(KC_B % 128 == 0 && VC_B % 128 == 0 && KS_B % 128 == 0 && VS_B % 128 == 0, "128-byte pieces");
 };
 
@@ -312,19 +309,14 @@ __device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* dst, i
 
 // The unit's six arrays.
 struct KiviRes {
-  __amdgpu_buffer_rsrc_t kc, ks, kz, vc, vs, vz;
+  __amdgpu_buffer_rsrc_t blocks;  // the unit's block records
 };
 
 template <int D, int BITS>
 __device__ __forceinline__ void issue_block(char* dst, const KiviRes& res, int blk, int lane) {
   using BL = BlockLayout<D, BITS>;
   blk = __builtin_amdgcn_readfirstlane(blk);
-  dma_piece<BL::KC_B>(res.kc, dst + BL::KC, blk * BL::KC_B, lane);
-  dma_piece<BL::VC_B>(res.vc, dst + BL::VC, blk * BL::VC_B, lane);
-  dma_piece<BL::KS_B>(res.ks, dst + BL::KS, blk * BL::KS_B, lane);
-  dma_piece<BL::KS_B>(res.kz, dst + BL::KZ, blk * BL::KS_B, lane);
-  dma_piece<BL::VS_B>(res.vs, dst + BL::VS, blk * BL::VS_B, lane);
-  dma_piece<BL::VS_B>(res.vz, dst + BL::VZ, blk * BL::VS_B, lane);
+  dma_piece<BL::BYTES>(res.blocks, dst, blk * BL::BYTES, lane);
 }
 
 template <int N>
@@ -781,17 +773,18 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
     KiviQuery<D, W> Q;
     kivi_query<D, W>(P, b, hk, lane, Q);
     const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;
-    const int b0 = (split * kWaves + wave) * P.bpw;
-    const int b1 = min(b0 + P.bpw, nblk);
+    // the workgroup's blocks [g0, g1) are dealt to its waves in turn (wave w
+    // takes g0 + w, g0 + w + kWaves, ...), so the waves of a workgroup read
+    // neighbouring records; i counts this wave's blocks
+    const int g0 = split * kWaves * P.bpw;
+    const int g1 = min(g0 + kWaves * P.bpw, nblk);
+    const int cnt = max(0, (g1 - g0 - wave + kWaves - 1) / kWaves);
+    auto gblk = [&](int i) { return g0 + wave + kWaves * i; };
+    const int b0 = 0, b1 = cnt;
     if (b0 < b1) {
       const size_t nbc = (size_t)(P.body_cap / 32);
       KiviRes res;
-      res.kc = make_rsrc(P.k_codes + unit * P.body_cap * WPT, (size_t)P.body_cap * WPT * 4);
-      res.ks = make_rsrc(P.k_scale + unit * nbc * D, nbc * D * 2);
-      res.kz = make_rsrc(P.k_zero + unit * nbc * D, nbc * D * 2);
-      res.vc = make_rsrc(P.v_codes + unit * nbc * 64 * VWL, nbc * 64 * VWL * 4);
-      res.vs = make_rsrc(P.v_scale + unit * nbc * NG * 32, nbc * NG * 32 * 2);
-      res.vz = make_rsrc(P.v_zero + unit * nbc * NG * 32, nbc * NG * 32 * 2);
+      res.blocks = make_rsrc(P.kivi_blocks + unit * nbc * BL::BYTES, nbc * BL::BYTES);
       constexpr int NS = LL::NS;
       char* const w0 = rs0 + wave * BL::BYTES;
       char* const w1 = rs1 + wave * BL::BYTES;
@@ -806,15 +799,15 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
       KiviRaw<D, BITS, W> ra, rb;
       auto step = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt, char* refill, int refill_blk,
                       const char* next_stage) {
-        issue_block<D, BITS>(refill, res, min(refill_blk, last), lane);
+        issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
         kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
         wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
         kivi_read<D, BITS, W>(nxt, next_stage, lane);
       };
-      issue_block<D, BITS>(w0, res, b0, lane);
-      issue_block<D, BITS>(w1, res, min(b0 + 1, last), lane);
+      issue_block<D, BITS>(w0, res, gblk(b0), lane);
+      issue_block<D, BITS>(w1, res, gblk(min(b0 + 1, last)), lane);
       if constexpr (NS == 4) {
-        issue_block<D, BITS>(w2, res, min(b0 + 2, last), lane);
+        issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
         wait_vm<2 * BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
         for (int blk = b0;; blk += 4) {
@@ -1073,12 +1066,7 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
   P.src_t_cap = kv.src_t_cap;
   P.body_len = kv.body_len;
   P.tail_len = kv.tail_len;
-  P.k_codes = kv.k_codes;
-  P.k_scale = static_cast<const uint16_t*>(kv.k_scale);
-  P.k_zero = static_cast<const uint16_t*>(kv.k_zero);
-  P.v_codes = kv.v_codes;
-  P.v_scale = static_cast<const uint16_t*>(kv.v_scale);
-  P.v_zero = static_cast<const uint16_t*>(kv.v_zero);
+  P.kivi_blocks = static_cast<const char*>(kv.kivi_blocks);
   P.kept_idx = kv.kept_idx;
   P.src_k = static_cast<const uint16_t*>(kv.src_k);
   P.src_v = static_cast<const uint16_t*>(kv.src_v);

@@ -68,12 +68,7 @@ struct QuantParams {
   int nblk_const;
   const int32_t* dst_blk_dev;  // [B] body_len (tokens) or null -> 0
   const int32_t* skip;         // [B] nonzero -> skip sequence (or null)
-  uint32_t* k_codes;
-  uint16_t* k_scale;
-  uint16_t* k_zero;
-  uint32_t* v_codes;
-  uint16_t* v_scale;
-  uint16_t* v_zero;
+  char* blocks;  // block records [u][body_cap/32][8*D*(BITS+1)]
   int Hkv, body_cap;
 };
 
@@ -100,6 +95,13 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
   }
   __syncthreads();
   const size_t nbc = (size_t)P.body_cap / 32;
+  // the block's record: key codes, value codes, key scale / zero, value scale / zero
+  constexpr int KC = 0, VC = 4 * D * BITS, KS = 8 * D * BITS, VS = KS + 4 * D, REC = 8 * D * (BITS + 1);
+  char* const rec = P.blocks + (unit * nbc + dblk) * REC;
+  uint32_t* const rk = reinterpret_cast<uint32_t*>(rec + KC);
+  uint32_t* const rv = reinterpret_cast<uint32_t*>(rec + VC);
+  uint16_t* const rks = reinterpret_cast<uint16_t*>(rec + KS);  // scale [D], then zero [D]
+  uint16_t* const rvs = reinterpret_cast<uint16_t*>(rec + VS);  // scale [D/32][32], then zero
   if (tid < D) {
     // keys: channel tid over 32 tokens
     const int d = tid;
@@ -115,8 +117,8 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
       if (sc != 0.0) c = fmin(fmax(rint((vals_k[t][d] - ze) / sc), 0.0), (double)QMAX);
       ck[t][d] = (uint8_t)c;
     }
-    P.k_scale[(unit * nbc + dblk) * D + d] = sb;
-    P.k_zero[(unit * nbc + dblk) * D + d] = zb;
+    rks[d] = sb;
+    rks[D + d] = zb;
   } else if (tid < D + 32 * NG) {
     // values: token t, channel group j
     const int i = tid - D, t = i / NG, j = i % NG;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
     uint32_t word = 0;
     constexpr int PER = 32 / BITS;
     for (int f = 0; f < PER; ++f) word |= (uint32_t)ck[t][w * PER + f] << (BITS * f);
-    P.k_codes[((unit * P.body_cap) + (size_t)dblk * 32 + t) * WPT + w] = word;
+    rk[t * WPT + w] = word;
   }
   // value words: lane L = 16q + c, word w covers m-tiles [w*4/BITS, (w+1)*4/BITS)
   for (int i = tid; i < 64 * VWL; i += 256) {
@@ -158,13 +160,13 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
         word |= (uint32_t)cv[t][16 * m + c] << bit;
       }
     }
-    P.v_codes[((unit * nbc + dblk) * 64 + L) * VWL + w] = word;
+    rv[L * VWL + w] = word;
   }
   for (int i = tid; i < NG * 32; i += 256) {
     const int j = i / 32, e = i % 32, q = e >> 3, s = e & 7;
     const int t = 4 * q + (s >> 1) + 16 * (s & 1);
-    P.v_scale[((unit * nbc + dblk) * NG + j) * 32 + e] = sv_s[t][j];
-    P.v_zero[((unit * nbc + dblk) * NG + j) * 32 + e] = sv_z[t][j];
+    rvs[j * 32 + e] = sv_s[t][j];
+    rvs[D + j * 32 + e] = sv_z[t][j];
   }
 }
 
@@ -445,12 +447,7 @@ vc_status kivi_quantize_launch(const vc_attn_shape& sh, int bits, const void* sr
   P.nblk_const = nblk_const;
   P.dst_blk_dev = dst_tok_dev;
   P.skip = skip;
-  P.k_codes = dc.k_codes;
-  P.k_scale = static_cast<uint16_t*>(dc.k_scale);
-  P.k_zero = static_cast<uint16_t*>(dc.k_zero);
-  P.v_codes = dc.v_codes;
-  P.v_scale = static_cast<uint16_t*>(dc.v_scale);
-  P.v_zero = static_cast<uint16_t*>(dc.v_zero);
+  P.blocks = static_cast<char*>(dc.kivi_blocks);
   P.Hkv = sh.n_kv_heads;
   P.body_cap = dc.body_cap;
   if (grid_blocks <= 0) return VC_OK;

@@ -171,18 +171,12 @@ class Engine:
         self.body_cap = _round32(n_body + self.rounds_cap * (c.k + 1) + 32)
         nb = self.body_cap // 32
         dev = self.dev
-        self.k_codes = torch.zeros((B, Hkv, self.body_cap, D * bits // 32), dtype=torch.int32, device=dev)
-        self.k_scale = torch.zeros((B, Hkv, nb, D), dtype=torch.float16, device=dev)
-        self.k_zero = torch.zeros_like(self.k_scale)
-        self.v_codes = torch.zeros((B, Hkv, nb, 64, D * bits // 64), dtype=torch.int32, device=dev)
-        self.v_scale = torch.zeros((B, Hkv, nb, D // 32, 32), dtype=torch.float16, device=dev)
-        self.v_zero = torch.zeros_like(self.v_scale)
+        rec = L.vc_kivi_block_bytes(D, bits)
+        self.kivi_blocks = torch.zeros((B, Hkv, nb, rec), dtype=torch.uint8, device=dev)
         for o in (self.kv, self.dc):
             o.bits = bits
             o.body_cap = self.body_cap
-            o.k_codes, o.v_codes = self.k_codes.data_ptr(), self.v_codes.data_ptr()
-            o.k_scale, o.k_zero = self.k_scale.data_ptr(), self.k_zero.data_ptr()
-            o.v_scale, o.v_zero = self.v_scale.data_ptr(), self.v_zero.data_ptr()
+            o.kivi_blocks = self.kivi_blocks.data_ptr()
         if c.staged:
             src_k, src_v = self._big
             t_cap = c.context

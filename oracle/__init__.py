@@ -20,7 +20,8 @@ the pages print none.
 from .attention import attend, attend_masked
 from .kivi import (quantize_keys, quantize_values, dequantize_keys, dequantize_values,
                    pack_key_codes, pack_value_codes, pack_value_side, unpack_key_codes,
-                   unpack_value_codes, unpack_value_side, fp16_round, value_slot_token)
+                   unpack_value_codes, unpack_value_side, fp16_round, value_slot_token, pack_blocks,
+                   unpack_blocks, record_bytes, record_offsets)
 from .tokdrop import select_kept
 from .vocab import to_bf16, logits, argmax_first, tie_bound
 from .accept import greedy_accept
@@ -28,7 +29,8 @@ from .accept import greedy_accept
 __all__ = [
     "attend", "attend_masked", "quantize_keys", "quantize_values", "dequantize_keys",
     "dequantize_values", "pack_key_codes", "pack_value_codes", "pack_value_side",
-    "unpack_key_codes", "unpack_value_codes", "unpack_value_side", "fp16_round",
+    "unpack_key_codes", "unpack_value_codes", "unpack_value_side", "fp16_round", "pack_blocks", "unpack_blocks",
+    "record_bytes", "record_offsets",
     "value_slot_token", "select_kept", "to_bf16", "logits", "argmax_first", "tie_bound",
     "greedy_accept",
 ]

@@ -194,3 +194,63 @@ def unpack_value_side(packed) -> np.ndarray:
     for e in range(GROUP):
         out[:, value_slot_token(e // 8, e % 8), :] = p[:, :, e]
     return out.reshape(nb * GROUP, G)
+
+
+# Block records. The body of one (sequence, KV head) is stored block-major:
+# one record of 8*D*(b + 1) bytes per 32-token block, holding at byte offsets
+#   0          the block's key codes (uint32 [32][D*b/32], as above)
+#   4*D*b      its value codes (uint32 [64][D*b/64], as above)
+#   8*D*b      key scale fp16 [D], then key zero fp16 [D]
+#   8*D*b+4*D  value scale fp16 [D/32][32], then value zero fp16 [D/32][32]
+# (little-endian words), so that one block is one contiguous read.
+
+
+def record_bytes(D: int, bits: int) -> int:
+    return 8 * D * (bits + 1)
+
+
+def record_offsets(D: int, bits: int) -> dict:
+    """Byte offsets of the six pieces inside a record."""
+    return {"key_codes": 0, "value_codes": 4 * D * bits, "key_scale": 8 * D * bits,
+            "key_zero": 8 * D * bits + 2 * D, "value_scale": 8 * D * bits + 4 * D,
+            "value_zero": 8 * D * bits + 6 * D}
+
+
+def pack_blocks(kcodes, kscale, kzero, vcodes, vscale, vzero, bits: int) -> np.ndarray:
+    """Quantised body (codes int [T][D], key scale / zero [T/32][D], value
+    scale / zero [T][D/32]; T a multiple of 32) -> uint8 records [T/32][8*D*(b+1)]."""
+    kcodes = np.asarray(kcodes)
+    T, D = kcodes.shape
+    nb = T // GROUP
+    kw = pack_key_codes(kcodes, bits).reshape(nb, -1).astype("<u4")
+    vw = pack_value_codes(vcodes, bits).reshape(nb, -1).astype("<u4")
+    ks = np.asarray(kscale).astype("<f2").reshape(nb, D)
+    kz = np.asarray(kzero).astype("<f2").reshape(nb, D)
+    vs = pack_value_side(np.asarray(vscale).astype("<f2")).reshape(nb, D)
+    vz = pack_value_side(np.asarray(vzero).astype("<f2")).reshape(nb, D)
+    out = np.zeros((nb, record_bytes(D, bits)), dtype=np.uint8)
+    for j in range(nb):
+        raw = b"".join(a[j].tobytes() for a in (kw, vw, ks, kz, vs, vz))
+        out[j] = np.frombuffer(raw, dtype=np.uint8)
+    return out
+
+
+def unpack_blocks(records, bits: int, D: int):
+    """Inverse of pack_blocks: (key codes, key scale, key zero, value codes,
+    value scale, value zero) with the shapes pack_blocks takes."""
+    r = np.ascontiguousarray(np.asarray(records, dtype=np.uint8))
+    nb = r.shape[0]
+    off = record_offsets(D, bits)
+    nkw = 32 * D * bits // 32
+
+    def piece(name, n, dt):
+        return np.stack([np.frombuffer(r[j, off[name]:off[name] + n * np.dtype(dt).itemsize].tobytes(), dtype=dt)
+                         for j in range(nb)])
+
+    kc = unpack_key_codes(piece("key_codes", nkw, "<u4").reshape(nb * GROUP, D * bits // 32), bits, D)
+    vc = unpack_value_codes(piece("value_codes", 64 * (D * bits // 64), "<u4").reshape(nb, 64, -1), bits, D)
+    ks = piece("key_scale", D, "<f2").astype(np.float16)
+    kz = piece("key_zero", D, "<f2").astype(np.float16)
+    vs = unpack_value_side(piece("value_scale", D, "<f2").reshape(nb, D // GROUP, GROUP)).astype(np.float16)
+    vz = unpack_value_side(piece("value_zero", D, "<f2").reshape(nb, D // GROUP, GROUP)).astype(np.float16)
+    return kc, ks, kz, vc, vs, vz

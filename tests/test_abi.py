@@ -38,9 +38,9 @@ def kivi_kv(**kw):
     kv = L.vc_draft_kv()
     kv.kind, kv.bits, kv.body_cap, kv.tail_cap = L.VC_DRAFT_KIVI, 2, 1024, 64
     fake = 0x10000  # never dereferenced: every test below fails before any launch
-    for f in ("body_len", "tail_len", "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "tail_k",
-              "tail_v"):
+    for f in ("body_len", "tail_len", "tail_k", "tail_v"):
         setattr(kv, f, fake)
+    kv.kivi_blocks = 0x100000
     for k, v in kw.items():
         setattr(kv, k, v)
     return kv
@@ -62,10 +62,10 @@ def test_draft_argument_checks():
     sh = shape()
     out = C.c_size_t()
     assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(bits=3)), C.byref(out)) == L.VC_ERR_UNSUPPORTED
-    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(k_codes=None)), C.byref(out)) == L.VC_ERR_INVALID_ARG
-    assert "k_codes" in L.last_error()
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(kivi_blocks=None)), C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert "kivi_blocks" in L.last_error()
     assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(tail_cap=40)), C.byref(out)) == L.VC_ERR_INVALID_ARG
-    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(k_scale=0x10002)), C.byref(out)) == L.VC_ERR_INVALID_ARG
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(kivi_blocks=0x100010)), C.byref(out)) == L.VC_ERR_INVALID_ARG
     assert "aligned" in L.last_error()
     assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv()), C.byref(out)) == L.VC_OK
     assert out.value > 0
@@ -115,3 +115,12 @@ def test_time_next_call_scope():
     with pytest.raises(L.VCError) as e:
         L.vc_time_next_call(None, None, 7)
     assert e.value.status == L.VC_ERR_INVALID_ARG
+
+
+def test_kivi_block_bytes():
+    assert L.vc_kivi_block_bytes(128, 2) == 3072
+    assert L.vc_kivi_block_bytes(64, 4) == 2560
+    out = C.c_size_t()
+    assert L.lib.vc_kivi_block_bytes(96, 2, C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert L.lib.vc_kivi_block_bytes(128, 3, C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert L.lib.vc_kivi_block_bytes(128, 2, None) == L.VC_ERR_INVALID_ARG

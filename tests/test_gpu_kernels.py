@@ -81,11 +81,7 @@ def build_kivi(B, Hq, Hkv, D, bits, body_lens, tail_lens, seed, outliers=False):
     tail_cap = r32(max(max(tail_lens), 1)) + 32
     nbc = body_cap // 32
     arr = {
-        "k_codes": np.zeros((B, Hkv, body_cap, D * bits // 32), np.uint32),
-        "k_scale": np.zeros((B, Hkv, nbc, D), np.float16), "k_zero": np.zeros((B, Hkv, nbc, D), np.float16),
-        "v_codes": np.zeros((B, Hkv, nbc, 64, D * bits // 64), np.uint32),
-        "v_scale": np.zeros((B, Hkv, nbc, D // 32, 32), np.float16),
-        "v_zero": np.zeros((B, Hkv, nbc, D // 32, 32), np.float16),
+        "kivi_blocks": np.zeros((B, Hkv, nbc, oracle.record_bytes(D, bits)), np.uint8),
         "tail_k": np.zeros((B, Hkv, tail_cap, D), np.float16), "tail_v": np.zeros((B, Hkv, tail_cap, D), np.float16),
     }
     vis = {}
@@ -96,12 +92,7 @@ def build_kivi(B, Hq, Hkv, D, bits, body_lens, tail_lens, seed, outliers=False):
             if nb:
                 kc, ks, kz = oracle.quantize_keys(Kb, bits)
                 vc, vs, vz = oracle.quantize_values(Vb, bits)
-                arr["k_codes"][b, h, :nb] = oracle.pack_key_codes(kc, bits)
-                arr["k_scale"][b, h, :nb // 32] = ks
-                arr["k_zero"][b, h, :nb // 32] = kz
-                arr["v_codes"][b, h, :nb // 32] = oracle.pack_value_codes(vc, bits)
-                arr["v_scale"][b, h, :nb // 32] = oracle.pack_value_side(vs)
-                arr["v_zero"][b, h, :nb // 32] = oracle.pack_value_side(vz)
+                arr["kivi_blocks"][b, h, :nb // 32] = oracle.pack_blocks(kc, ks, kz, vc, vs, vz, bits)
                 kd, vd = oracle.dequantize_keys(kc, ks, kz), oracle.dequantize_values(vc, vs, vz)
             else:
                 kd, vd = np.zeros((0, D)), np.zeros((0, D))
@@ -144,13 +135,13 @@ def test_draft_kivi_parity(L, case):
     log(f"draft kivi {case}")
     seed = 100 + sum(body)
     arr, vis, body_cap, tail_cap = build_kivi(B, Hq, Hkv, D, bits, body, tail, seed, outl)
-    dev = {k: (f16_dev(v) if v.dtype == np.float16 else to_dev(v.view(np.int32))) for k, v in arr.items()}
+    dev = {k: (f16_dev(v) if v.dtype == np.float16 else to_dev(v)) for k, v in arr.items()}
     bl, tl = to_dev(np.array(body, np.int32)), to_dev(np.array(tail, np.int32))
     sh = L.vc_attn_shape(B, Hq, Hkv, D)
     kv = L.vc_draft_kv()
     kv.kind, kv.bits, kv.body_cap, kv.tail_cap = L.VC_DRAFT_KIVI, bits, body_cap, tail_cap
     kv.body_len, kv.tail_len = bl.data_ptr(), tl.data_ptr()
-    for f in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "tail_k", "tail_v"):
+    for f in ("kivi_blocks", "tail_k", "tail_v"):
         setattr(kv, f, dev[f].data_ptr())
     q = draft_queries(seed, B, Hq, D)
     out = run_draft(L, sh, kv, bf16_tensor(q)).cpu().numpy()
@@ -409,13 +400,10 @@ def test_kivi_quantize_matches_oracle(L, D, bits):
     fk[:, :, :T], fv[:, :, :T] = K, V
     body_cap, tail_cap = 128, 32
     nbc = body_cap // 32
+    rec = L.vc_kivi_block_bytes(D, bits)
+    assert rec == oracle.record_bytes(D, bits)
     t = {
-        "k_codes": torch.zeros((B, Hkv, body_cap, D * bits // 32), dtype=torch.int32, device="cuda"),
-        "k_scale": torch.zeros((B, Hkv, nbc, D), dtype=torch.float16, device="cuda"),
-        "k_zero": torch.zeros((B, Hkv, nbc, D), dtype=torch.float16, device="cuda"),
-        "v_codes": torch.zeros((B, Hkv, nbc, 64, D * bits // 64), dtype=torch.int32, device="cuda"),
-        "v_scale": torch.zeros((B, Hkv, nbc, D // 32, 32), dtype=torch.float16, device="cuda"),
-        "v_zero": torch.zeros((B, Hkv, nbc, D // 32, 32), dtype=torch.float16, device="cuda"),
+        "kivi_blocks": torch.zeros((B, Hkv, nbc, rec), dtype=torch.uint8, device="cuda"),
         "tail_k": torch.zeros((B, Hkv, tail_cap, D), dtype=torch.float16, device="cuda"),
         "tail_v": torch.zeros((B, Hkv, tail_cap, D), dtype=torch.float16, device="cuda"),
     }
@@ -437,12 +425,8 @@ def test_kivi_quantize_matches_oracle(L, D, bits):
             kc, ks, kz = oracle.quantize_keys(K[b, h, :n_body], bits)
             vc, vs, vz = oracle.quantize_values(V[b, h, :n_body], bits)
             nb = n_body // 32
-            assert np.array_equal(g["k_codes"][b, h, :n_body].view(np.uint32), oracle.pack_key_codes(kc, bits))
-            assert np.array_equal(g["v_codes"][b, h, :nb].view(np.uint32), oracle.pack_value_codes(vc, bits))
-            for name, ref in (("k_scale", ks), ("k_zero", kz)):
-                assert np.array_equal(g[name][b, h, :nb].view(np.uint16), ref.astype(np.float16).view(np.uint16)), name
-            for name, ref in (("v_scale", vs), ("v_zero", vz)):
-                assert np.array_equal(g[name][b, h, :nb].view(np.uint16),
-                                      oracle.pack_value_side(ref).astype(np.float16).view(np.uint16)), name
+            # the records, byte for byte
+            want = oracle.pack_blocks(kc, ks, kz, vc, vs, vz, bits)
+            assert np.array_equal(g["kivi_blocks"][b, h, :nb], want), (b, h)
             assert np.array_equal(g["tail_k"][b, h, :n_tail].astype(np.float32), K[b, h, n_body:T])
             assert np.array_equal(g["tail_v"][b, h, :n_tail].astype(np.float32), V[b, h, n_body:T])

@@ -70,14 +70,13 @@ def test_draft_call_records_events(L):
     B, Hq, Hkv, D, bits, body, tail = 2, 32, 8, 128, 2, [2048, 1024], [130, 129]
     log("timing draft kivi")
     arr, _, body_cap, tail_cap = build_kivi(B, Hq, Hkv, D, bits, body, tail, 7)
-    dev = {k: (f16_dev(v) if v.dtype == np.float16 else to_dev(v.view(np.int32)))
-           for k, v in arr.items()}
+    dev = {k: (f16_dev(v) if v.dtype == np.float16 else to_dev(v)) for k, v in arr.items()}
     bl, tl = to_dev(np.array(body, np.int32)), to_dev(np.array(tail, np.int32))
     sh = L.vc_attn_shape(B, Hq, Hkv, D)
     kv = L.vc_draft_kv()
     kv.kind, kv.bits, kv.body_cap, kv.tail_cap = L.VC_DRAFT_KIVI, bits, body_cap, tail_cap
     kv.body_len, kv.tail_len = bl.data_ptr(), tl.data_ptr()
-    for f in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "tail_k", "tail_v"):
+    for f in ("kivi_blocks", "tail_k", "tail_v"):
         setattr(kv, f, dev[f].data_ptr())
     q = bf16_tensor(draft_queries(7, B, Hq, D))
     ws = torch.empty(L.vc_draft_workspace_bytes(sh, kv), dtype=torch.uint8, device="cuda")

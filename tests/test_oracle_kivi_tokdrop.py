@@ -5,9 +5,9 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (dequantize_keys, dequantize_values, fp16_round, pack_key_codes,
-                    pack_value_codes, pack_value_side, quantize_keys, quantize_values,
-                    select_kept, unpack_key_codes, unpack_value_codes, unpack_value_side)
+from oracle import (dequantize_keys, dequantize_values, fp16_round, pack_blocks, pack_key_codes,
+                    pack_value_codes, pack_value_side, quantize_keys, quantize_values, record_bytes,
+                    select_kept, unpack_blocks, unpack_key_codes, unpack_value_codes, unpack_value_side)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -99,6 +99,55 @@ def test_layout_golden_positions():
         nz = np.argwhere(vw)
         assert nz.tolist() == [[0, case["value_lane"], case["value_word"]]]
         assert int(vw[0, case["value_lane"], case["value_word"]]) == ((1 << bits) - 1) << case["value_bit"]
+
+
+@pytest.mark.parametrize("bits,D", [(2, 64), (2, 128), (4, 64), (4, 128)])
+def test_block_records_roundtrip(bits, D):
+    rng = np.random.default_rng(7 * bits + D)
+    kc = rng.integers(0, 1 << bits, size=(64, D))
+    vc = rng.integers(0, 1 << bits, size=(64, D))
+    ks, kz = rng.standard_normal((2, D)).astype(np.float16), rng.standard_normal((2, D)).astype(np.float16)
+    vs, vz = (rng.standard_normal((64, D // 32)).astype(np.float16) for _ in range(2))
+    rec = pack_blocks(kc, ks, kz, vc, vs, vz, bits)
+    assert rec.shape == (2, record_bytes(D, bits))
+    for got, want in zip(unpack_blocks(rec, bits, D), (kc, ks, kz, vc, vs, vz)):
+        assert np.array_equal(got, want)
+
+
+def test_block_record_golden_offsets():
+    """Hand-worked record sizes and piece offsets (tests/golden/kivi_layout.json):
+    a value planted in each piece must land at its offset."""
+    with open(os.path.join(GOLDEN, "kivi_layout.json")) as f:
+        cases = json.load(f)["records"]["cases"]
+    for case in cases:
+        bits, D = case["bits"], case["D"]
+        assert record_bytes(D, bits) == case["bytes"]
+        z = np.zeros((32, D), np.int64)
+        one = np.float16(1.0)  # 0x3C00: bytes 00 3C
+        kc = z.copy()
+        kc[0, 0] = 1
+        rec = pack_blocks(kc, np.zeros((1, D), np.float16), np.zeros((1, D), np.float16), z,
+                          np.zeros((32, D // 32), np.float16), np.zeros((32, D // 32), np.float16), bits)[0]
+        assert np.flatnonzero(rec).tolist() == [case["key_codes"]]
+        vc = z.copy()
+        vc[0, 0] = 1  # token 0 = slot 0 of lane 0: lane 0, word 0, bit 0
+        rec = pack_blocks(z, np.zeros((1, D), np.float16), np.zeros((1, D), np.float16), vc,
+                          np.zeros((32, D // 32), np.float16), np.zeros((32, D // 32), np.float16), bits)[0]
+        assert np.flatnonzero(rec).tolist() == [case["value_codes"]]
+        for name in ("key_scale", "key_zero"):
+            p = np.zeros((1, D), np.float16)
+            p[0, 0] = one
+            args = [z, p if name == "key_scale" else 0 * p, p if name == "key_zero" else 0 * p, z,
+                    np.zeros((32, D // 32), np.float16), np.zeros((32, D // 32), np.float16)]
+            rec = pack_blocks(*args, bits)[0]
+            assert np.flatnonzero(rec).tolist() == [case[name] + 1] and rec[case[name] + 1] == 0x3C
+        for name in ("value_scale", "value_zero"):
+            p = np.zeros((32, D // 32), np.float16)
+            p[0, 0] = one  # token 0 = entry 0 of channel group 0
+            args = [z, np.zeros((1, D), np.float16), np.zeros((1, D), np.float16), z,
+                    p if name == "value_scale" else 0 * p, p if name == "value_zero" else 0 * p]
+            rec = pack_blocks(*args, bits)[0]
+            assert np.flatnonzero(rec).tolist() == [case[name] + 1] and rec[case[name] + 1] == 0x3C
 
 
 def _kept_by_rank(scores, n_keep):

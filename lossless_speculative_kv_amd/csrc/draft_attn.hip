@@ -729,28 +729,52 @@ constexpr size_t draft_lds_bytes() {
 }
 
 // ---------------------------------------------------------------- kernels ----
+// This (split, wave)'s share of the 32-token tail blocks when every split
+// also streams body blocks: tail block j goes to split S - 1 - (j mod S)
+// (the last split holds the fewest body blocks), wave (j / S) mod kWaves.
+// BF16 / STAGE as for row_block (fp16 unstaged rows for the KIVI tail).
+template <int D, int NHS, bool BF16, bool STAGE>
+__device__ __forceinline__ void tail_share(const DraftParams& P, int b, int hk, int split, int wave, int lane,
+                                           DState<D, 1, NHS>& st, uint16_t* lds_rows, uint32_t* lds_p) {
+  const size_t unit = (size_t)b * P.Hkv + hk;
+  const int nt = min(max(P.tail_len[b], 0), P.tail_cap);
+  int j = wave * P.S + (P.S - 1 - split);
+  if (j * 32 >= nt) return;
+  uint32_t Aqm[NHS][D / 32][4];
+  row_query<D, NHS, BF16>(P, b, hk, lane, Aqm);
+  const uint16_t* tk = P.tail_k + unit * P.tail_cap * D;
+  const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
+  for (; j * 32 < nt; j += P.S * kWaves) {
+    const PlainRows<D> rows{tk + (size_t)j * 32 * D, tv + (size_t)j * 32 * D};
+    row_block<D, 1, NHS, BF16, STAGE>(rows, min(32, nt - j * 32), lane, P.qscale, Aqm, st, lds_rows, lds_p);
+  }
+}
+
 // LDS of the KIVI kernel: NS ring stages (one per variable, so the compiler
 // can tell which pending direct-to-LDS loads a read depends on; the first
 // also hosts the wave merge at the end), then the probability areas.
 template <int D, int BITS, int W>
 struct KiviLds {
   static constexpr int STAGE = kWaves * BlockLayout<D, BITS>::BYTES;
-  // ring depth: four stages while they fit in 48 KB (three workgroups per
-  // CU) and the rows are one group wide (wider rows need the registers)
-  static constexpr int NS = (W == 1 && 4 * STAGE <= 48 * 1024) ? 4 : 3;
+  // ring depth for one-group rows: six stages while they fit in 72 KB (two
+  // workgroups per CU, four blocks in flight per wave), else four within
+  // 48 KB (three workgroups); wider rows do more work per block and keep
+  // three stages at three workgroups per CU
+  static constexpr int NS = (W == 1 && 6 * STAGE <= 72 * 1024) ? 6 : (W == 1 && 4 * STAGE <= 48 * 1024) ? 4 : 3;
   static constexpr int MERGE = kWaves * Geo<D, W>::HS * (D + 2) * 4;
   static constexpr int STAGE0 = STAGE > MERGE ? STAGE : MERGE;
 };
 
-// Waves per SIMD to plan registers for (wider rows hold more heads per lane).
-template <int D, int W>
+// Waves per SIMD to plan registers for (the six-stage ring allows two
+// workgroups per CU; wider rows hold more heads per lane).
+template <int D, int BITS, int W>
 constexpr int kivi_min_waves() {
-  return W == 1 ? 3 : (Geo<D, W>::NR > 1 ? 2 : 1);
+  return W == 1 ? (KiviLds<D, BITS, W>::NS == 6 ? 2 : 3) : (Geo<D, W>::NR > 1 ? 2 : 1);
 }
 
 // KIVI body + fp16 tail, one head set of HS = 16*W/NG >= g query heads.
 template <int D, int BITS, int W>
-__global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kernel(const DraftParams P) {
+__global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kivi_kernel(const DraftParams P) {
   constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64;
   using BL = BlockLayout<D, BITS>;
   using LL = KiviLds<D, BITS, W>;
@@ -758,6 +782,8 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
   __shared__ __attribute__((aligned(16))) char rs1[LL::STAGE];
   __shared__ __attribute__((aligned(16))) char rs2[LL::STAGE];
   __shared__ __attribute__((aligned(16))) char rs3[LL::NS > 3 ? LL::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char rs4[LL::NS > 4 ? LL::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char rs5[LL::NS > 4 ? LL::STAGE : 16];
   __shared__ __attribute__((aligned(16))) uint32_t parea[kWaves * p_area_words<D, W, 1>()];
   // the wave index is uniform across the wave; saying so keeps the per-block
   // offsets in SGPRs
@@ -768,6 +794,8 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
 
   DState<D, W, 1> st;
   st.init();
+  // the fp16 tail (read without staging) takes a last split of its own, so
+  // that its slower blocks run beside the body instead of after it
   const bool tail_split = (split == P.S - 1);
   if (!tail_split) {
     KiviQuery<D, W> Q;
@@ -790,6 +818,8 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
       char* const w1 = rs1 + wave * BL::BYTES;
       char* const w2 = rs2 + wave * BL::BYTES;
       char* const w3 = rs3 + (NS > 3 ? wave * BL::BYTES : 0);
+      char* const w4 = rs4 + (NS > 4 ? wave * BL::BYTES : 0);
+      char* const w5 = rs5 + (NS > 4 ? wave * BL::BYTES : 0);
       // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of the
       // next block move from LDS to registers at the end of a step, so their
       // latency overlaps the step's last MFMAs. Past the wave's last block
@@ -806,7 +836,38 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, W>())) void draft_kivi_kern
       };
       issue_block<D, BITS>(w0, res, gblk(b0), lane);
       issue_block<D, BITS>(w1, res, gblk(min(b0 + 1, last)), lane);
-      if constexpr (NS == 4) {
+      if constexpr (NS == 6) {
+        // three register sets: the operands of block i + 2 are read while
+        // block i is computed, so the LDS reads have a whole step to land
+        KiviRaw<D, BITS, W> rc;
+        auto step3 = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt2, char* refill, int refill_blk,
+                         const char* stage2) {
+          issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
+          kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
+          wait_vm<3 * BL::NI>();  // block i + 2 has landed
+          kivi_read<D, BITS, W>(nxt2, stage2, lane);
+        };
+        issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
+        issue_block<D, BITS>(w3, res, gblk(min(b0 + 3, last)), lane);
+        issue_block<D, BITS>(w4, res, gblk(min(b0 + 4, last)), lane);
+        wait_vm<3 * BL::NI>();
+        kivi_read<D, BITS, W>(ra, w0, lane);
+        kivi_read<D, BITS, W>(rb, w1, lane);
+        for (int blk = b0;; blk += 6) {
+          step3(ra, rc, w5, blk + 5, w2);
+          if (blk + 1 > last) break;
+          step3(rb, ra, w0, blk + 6, w3);
+          if (blk + 2 > last) break;
+          step3(rc, rb, w1, blk + 7, w4);
+          if (blk + 3 > last) break;
+          step3(ra, rc, w2, blk + 8, w5);
+          if (blk + 4 > last) break;
+          step3(rb, ra, w3, blk + 9, w0);
+          if (blk + 5 > last) break;
+          step3(rc, rb, w4, blk + 10, w1);
+          if (blk + 6 > last) break;
+        }
+      } else if constexpr (NS == 4) {
         issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
         wait_vm<2 * BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
@@ -876,7 +937,8 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
   uint32_t Aqm[NHS][D / 32][4];
   row_query<D, NHS, true>(P, b, hk, lane, Aqm);
   uint16_t* my_lds = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 4);
-  if (split != P.S - 1) {
+  // every split streams its body blocks, then takes its share of the tail
+  {
     const int nb = min(max(P.body_len[b], 0), P.body_cap);
     const int nblk = (nb + 31) / 32;
     const int b0 = (split * kWaves + wave) * P.bpw;
@@ -888,15 +950,8 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
       const SourceRows<D, GATHER> rows{sk, sv, kept, blk * 32, P.src_t_cap};
       row_block<D, 1, NHS, true, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
     }
-  } else {
-    const int nt = min(max(P.tail_len[b], 0), P.tail_cap);
-    const uint16_t* tk = P.tail_k + unit * P.tail_cap * D;
-    const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
-    for (int blk = wave; blk * 32 < nt; blk += kWaves) {
-      const PlainRows<D> rows{tk + (size_t)blk * 32 * D, tv + (size_t)blk * 32 * D};
-      row_block<D, 1, NHS, true, true>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
-    }
   }
+  tail_share<D, NHS, true, true>(P, b, hk, split, wave, lane, st, my_lds, lds_p);
   store_partial<D, 1, NHS>(P, b, hk, split, lane, wave, st, false, reinterpret_cast<float*>(smem));
 }
 
@@ -1021,19 +1076,24 @@ long long resident_wgs(DraftKernel k) {
 // (sequence, KV head)) be resident at once, so the kernel runs in one round.
 struct DraftPlan {
   int bpw;     // body blocks per wave
-  int splits;  // body splits + 1 tail split
+  int splits;  // body splits (+ 1 tail split for KIVI)
 };
 
+// The splits of every (sequence, KV head) fill the resident workgroups once.
+// KIVI keeps its fp16 tail in a last split of its own; the row kernels (token
+// drop, dense) stage the tail like the body, so every split takes body blocks
+// and a share of the tail.
 DraftPlan draft_plan(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   const long long blocks = (kv.body_cap + 31) / 32;
   const long long units = (long long)sh.batch * sh.n_kv_heads;
-  long long body_splits = resident_wgs(pick_kernel(sh, kv)) / units - 1;
+  const bool tail_split = kv.kind == VC_DRAFT_KIVI;
+  long long body_splits = resident_wgs(pick_kernel(sh, kv)) / units - (tail_split ? 1 : 0);
   if (body_splits < 1) body_splits = 1;
   long long bpw = (blocks + body_splits * kWaves - 1) / (body_splits * kWaves);
   if (bpw < 1) bpw = 1;
   body_splits = (blocks + kWaves * bpw - 1) / (kWaves * bpw);
   if (body_splits < 1) body_splits = 1;
-  return DraftPlan{(int)bpw, (int)body_splits + 1};
+  return DraftPlan{(int)bpw, (int)body_splits + (tail_split ? 1 : 0)};
 }
 
 // Workspace: the split partials (unnormalised outputs, then max and sum).

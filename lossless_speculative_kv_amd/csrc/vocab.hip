@@ -4,16 +4,20 @@
 //
 // logits[m][n] = sum_k bf16(h[m][k]) * W[n][k], fp32 accumulation on
 // v_mfma_f32_16x16x32_bf16 with A = 16 vocabulary rows of W and B = 16 hidden
-// rows. Contraction slots are permuted so that each lane reads 64 contiguous
-// bytes of a W row per 128-wide k step: lane group qg takes k = k0 + 32*qg
-// + 8*kk + s in K-step kk (the B operand uses the same permutation).
+// rows. Contraction slots are permuted so that one load instruction reads 64
+// contiguous bytes of each of 16 rows (the four lane groups take consecutive
+// 16-byte pieces): lane group qg takes k = k0 + 32*kk + 8*qg + s in K-step kk
+// (the B operand uses the same permutation).
 //
 // Two kernels share the epilogue:
 //  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
 //    rows; W goes straight from HBM to registers, h (bf16, tiny) from L2.
 //  * vocab_staged: any M. Each wave owns 32 vocab rows and all M rows; the
-//    hidden chunk [M][64] is staged in LDS (double-buffered) and shared by
-//    the 8 waves of the workgroup, so W is read from HBM exactly once.
+//    hidden rows are staged in LDS in 32-wide k chunks (double-buffered) and
+//    shared by the 8 waves of the workgroup, so W is read from HBM exactly
+//    once. Up to 18 row tiles the loads run ahead: the next W chunk and the
+//    hidden chunk after it are in registers while the current one is
+//    multiplied.
 // Argmax: each workgroup reduces (logit, index) to one 64-bit key per row,
 // key = ordered(logit) << 32 | ~index, whose maximum is the largest logit with
 // the lowest index (-0 is folded to +0); a second kernel takes the max over
@@ -128,30 +132,43 @@ __global__ __launch_bounds__(256) void vocab_stream_kernel(const VocabParams P) 
   for (int a = 0; a < NA; ++a) {
     const int v = vbase + 16 * a + n;
     wok[a] = v < P.V;
-    wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K + 32 * qg;
+    wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K + 8 * qg;
   }
   const uint16_t* hrow[MS];
 #pragma unroll
-  for (int t = 0; t < MS; ++t) hrow[t] = P.hb + (size_t)(16 * t + n) * P.K + 32 * qg;
+  for (int t = 0; t < MS; ++t) hrow[t] = P.hb + (size_t)(16 * t + n) * P.K + 8 * qg;
 
-  for (int k0 = 0; k0 < P.K; k0 += 128) {
-    u32x4 A[NA][4];
+  // W k-steps of 128 are double-buffered in registers: the loads of step
+  // i + 1 are in flight while step i is multiplied
+  auto load = [&](u32x4 (&A)[NA][4], int k0) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto compute = [&](const u32x4 (&A)[NA][4], int k0) {
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
       u32x4 B[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) B[kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 8 * kk);
+      for (int kk = 0; kk < 4; ++kk) B[kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 32 * kk);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B[kk], acc[a][t]);
     }
+  };
+  u32x4 Aa[NA][4], Ab[NA][4];
+  load(Aa, 0);
+  int k0 = 0;
+  for (; k0 + 256 <= P.K; k0 += 256) {
+    load(Ab, k0 + 128);
+    compute(Aa, k0);
+    if (k0 + 256 < P.K) load(Aa, k0 + 256);
+    compute(Ab, k0 + 128);
   }
+  if (k0 < P.K) compute(Aa, k0);  // K / 128 odd: the last step is already loaded
   int mrow[MS];
 #pragma unroll
   for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(256) void vocab_stream_kernel(const VocabParams P) 
 
 // Staged kernel: 8 waves x 32 vocab rows; all m-tiles (NMT >= ceil(M/16)).
 constexpr int kStagedWaves = 8;
-constexpr int kKC = 64;  // k per LDS stage
+constexpr int kKC = 32;  // k per LDS stage (one MFMA K-step)
 
 template <int NMT>
 __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) {
@@ -207,33 +224,89 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
           *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x);
     }
   };
-  stage(0, 0);
-  __syncthreads();
-  const int nk = P.K / kKC;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int k0 = kc * kKC;
-    // W for this chunk: 2 K-steps; lane group qg reads k0 + 16*qg + 8*kk (32 contiguous bytes)
-    u32x4 A[NA][2];
+  // W for one chunk: lane group qg of K-step kk reads k0 + 32*kk + 8*qg (with the other lane
+  // groups, 64 contiguous bytes of each row per instruction)
+  constexpr int KS = kKC / 32;  // K-steps per chunk
+  auto load_w = [&](u32x4 (&A)[NA][KS], int k0) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 16 * qg + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
-    if (kc + 1 < nk) stage(k0 + kKC, (kc + 1) & 1);
-    const uint16_t* cur = hs + (kc & 1) * stage_halfs;
+      for (int kk = 0; kk < KS; ++kk)
+        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk + 8 * qg) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto compute = [&](const u32x4 (&A)[NA][KS], const uint16_t* cur) {
 #pragma unroll
     for (int t = 0; t < NMT; ++t) {
       if (t < mtiles) {
-        const uint16_t* hr = cur + (16 * t + n) * HSTR + 16 * qg;
+        const uint16_t* hr = cur + (16 * t + n) * HSTR + 8 * qg;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 B = *reinterpret_cast<const u32x4*>(hr + 8 * kk);
+        for (int kk = 0; kk < KS; ++kk) {
+          const u32x4 B = *reinterpret_cast<const u32x4*>(hr + 32 * kk);
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B, acc[a][t]);
         }
       }
     }
+  };
+  const int nk = P.K / kKC;
+  if constexpr (NMT <= 18) {
+    // Pipelined: W chunks double-buffered in registers, and the hidden chunk
+    // two ahead loaded into registers while the current one is multiplied,
+    // then written to its LDS buffer one iteration later (so neither load's
+    // latency sits between two barriers).
+    constexpr int HPT = (16 * NMT * (kKC / 8) + 64 * kStagedWaves - 1) / (64 * kStagedWaves);
+    u32x4 hreg[HPT];
+    const int chunks = P.Mp * (kKC / 8);
+    auto hload = [&](int k0) {
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int c = threadIdx.x + i * 64 * kStagedWaves;
+        const int m = c / (kKC / 8), x = c % (kKC / 8);
+        hreg[i] = c < chunks ? *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x)
+                             : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto hstore = [&](int buf) {
+      uint16_t* dst = hs + buf * stage_halfs;
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int c = threadIdx.x + i * 64 * kStagedWaves;
+        const int m = c / (kKC / 8), x = c % (kKC / 8);
+        if (c < chunks) *reinterpret_cast<u32x4*>(dst + m * HSTR + 8 * x) = hreg[i];
+      }
+    };
+    u32x4 Aa[NA][KS], Ab[NA][KS];
+    hload(0);
+    hstore(0);
+    if (nk > 1) hload(kKC);
+    load_w(Aa, 0);
     __syncthreads();
+    // iteration kc: W of kc + 1 in flight, hidden kc + 1 -> LDS, hidden kc + 2 in flight
+    auto iter = [&](const u32x4 (&Acur)[NA][KS], u32x4 (&Anext)[NA][KS], int kc) {
+      if (kc + 1 < nk) {
+        load_w(Anext, (kc + 1) * kKC);
+        hstore((kc + 1) & 1);
+        if (kc + 2 < nk) hload((kc + 2) * kKC);
+      }
+      compute(Acur, hs + (kc & 1) * stage_halfs);
+      __syncthreads();
+    };
+    int kc = 0;
+    for (; kc + 2 <= nk; kc += 2) {
+      iter(Aa, Ab, kc);
+      iter(Ab, Aa, kc + 1);
+    }
+    if (kc < nk) iter(Aa, Ab, kc);
+  } else {
+    stage(0, 0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+      u32x4 A[NA][KS];
+      load_w(A, kc * kKC);
+      if (kc + 1 < nk) stage((kc + 1) * kKC, (kc + 1) & 1);
+      compute(A, hs + (kc & 1) * stage_halfs);
+      __syncthreads();
+    }
   }
   int mrow[NMT];
 #pragma unroll

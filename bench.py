@@ -279,6 +279,12 @@ def main():
                         "bytes_per_launch": verify_bytes, "avg_launch_us": t_vmain * 1e6,
                         "call_us": t_verify_avg * 1e6},
         "mfma": mfma,
+        **({"staging": {"host_resident_full_cache": True, "chunk_tokens": cfg.chunk,
+                        "device_chunk_buffers": cfg.stage_buffers,
+                        "verify_host_link_GBs": verify_gbs,
+                        "note": "verify time covers the whole chunked pass with its host-to-device copies "
+                                "(PCIe-inclusive); the first chunks are copied while the round drafts"}}
+           if cfg.staged else {}),
         "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": accepted / args.steps,
                    "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
         "round_tok_s": accepted / wall,

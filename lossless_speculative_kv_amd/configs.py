@@ -24,6 +24,7 @@ class RoundConfig:
     outliers: bool = False
     staged: bool = False      # full cache in pinned host memory, streamed in chunks
     chunk: int = 65536
+    stage_buffers: int = 4    # device chunk buffers; the first ones fill while the round drafts
     seed: int = 1
 
     @property

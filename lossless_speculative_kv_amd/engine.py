@@ -158,9 +158,11 @@ class Engine:
         self.full_v[:, :, :T].copy_(big_v)
         torch.cuda.synchronize(self.dev)
         self._big = (big_k, big_v)
-        self.chunk_k = [torch.empty((B, Hkv, c.chunk, D), dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
-        self.chunk_v = [torch.empty_like(self.chunk_k[0]) for _ in range(2)]
+        nbuf = max(2, c.stage_buffers)
+        self.chunk_k = [torch.empty((B, Hkv, c.chunk, D), dtype=torch.bfloat16, device=self.dev) for _ in range(nbuf)]
+        self.chunk_v = [torch.empty_like(self.chunk_k[0]) for _ in range(nbuf)]
         self.copy_stream = torch.cuda.Stream(self.dev)
+        self._staged_ready = {}
 
     def _init_kivi(self):
         c = self.cfg
@@ -283,17 +285,41 @@ class Engine:
         upper = min(self.full_cap, c.context + self.round_idx * (c.k + 1))
         return [(t0, min(c.chunk, upper - t0)) for t0 in range(0, upper, c.chunk)]
 
+    def stage_ahead(self):
+        """P1 staggering ("P1 cross-resource staggering"): copy the first chunks
+        of the host-resident full cache into the device chunk buffers on the
+        side stream at the start of the round, so the transfer runs while the
+        compute stream drafts (HBM-bound) instead of after it."""
+        cs, comp = self.copy_stream, self.stream
+        cs.wait_stream(comp)  # the previous round's commit wrote the host cache
+        plan = self.stage_plan()
+        self._staged_ready = {}
+        for i, (t0, n) in enumerate(plan[:len(self.chunk_k)]):
+            self._stage_chunk(i, t0, n)
+
+    def _stage_chunk(self, i, t0, n):
+        cs = self.copy_stream
+        buf = i % len(self.chunk_k)
+        L.vc_stage_full_kv(self.shape, self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, t0, n,
+                           self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), self.cfg.chunk,
+                           cs.cuda_stream, None)
+        ev = torch.cuda.Event()
+        ev.record(cs)
+        self._staged_ready[i] = ev
+
     def verify_staged(self):
-        """Stream the host-resident full cache through two device chunk buffers:
-        the copy of chunk i+1 (side stream) overlaps the verification of chunk
-        i (compute stream)."""
+        """Stream the host-resident full cache through the device chunk buffers:
+        chunks not already staged ahead are copied on the side stream once
+        their buffer is free, overlapping the verification of earlier chunks
+        on the compute stream."""
         c = self.cfg
         comp = self.stream
         cs = self.copy_stream
         plan = self.stage_plan()
-        ready = [torch.cuda.Event() for _ in plan]
-        free = [torch.cuda.Event() for _ in range(2)]
-        cs.wait_stream(comp)  # committed rows of the previous round are in host memory
+        nbuf = len(self.chunk_k)
+        free = [None] * nbuf
+        if not self._staged_ready:
+            cs.wait_stream(comp)  # committed rows of the previous round are in host memory
         # timed: from the first chunk's verify kernel start to the last chunk's end
         timing = None
         if self.events is not None:
@@ -302,14 +328,12 @@ class Engine:
             timing = self._ev_pool.pop()
             self.events.append(("verify_attn",) + timing)
         for i, (t0, n) in enumerate(plan):
-            buf = i % 2
-            if i >= 2:
-                cs.wait_event(free[buf])
-            L.vc_stage_full_kv(self.shape, self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, t0, n,
-                               self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), c.chunk, cs.cuda_stream,
-                               None)
-            ready[i].record(cs)
-            comp.wait_event(ready[i])
+            buf = i % nbuf
+            if i not in self._staged_ready:
+                if free[buf] is not None:
+                    cs.wait_event(free[buf])
+                self._stage_chunk(i, t0, n)
+            comp.wait_event(self._staged_ready[i])
             flags = (L.VC_VERIFY_BEGIN if i == 0 else 0) | (L.VC_VERIFY_END if i == len(plan) - 1 else 0)
             ctx = L.vc_kv_chunk(self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), c.chunk, t0, n)
             if timing is not None and (i == 0 or i == len(plan) - 1):
@@ -318,7 +342,9 @@ class Engine:
             L.vc_verify_attn(self.shape, c.k + 1, self.qv.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), ctx,
                              self.ctx_len.data_ptr(), flags, self.o_ver.data_ptr(), self.ws_verify.data_ptr(),
                              self.ws_verify.numel(), comp.cuda_stream)
+            free[buf] = torch.cuda.Event()
             free[buf].record(comp)
+        self._staged_ready = {}
 
     def verify_vocab(self):
         c = self.cfg
@@ -344,7 +370,13 @@ class Engine:
                           self.ws_commit.data_ptr(), self.ws_commit.numel(), s)
         self.round_idx += 1
 
+    def begin_round(self):
+        """Work issued before the draft steps (the staged cache's first chunk copies)."""
+        if self.cfg.staged:
+            self.stage_ahead()
+
     def round(self):
+        self.begin_round()
         for j in range(self.cfg.k):
             self.draft_step(j)
         self.embed_block()

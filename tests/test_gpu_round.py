@@ -84,6 +84,7 @@ def run_case(configs, engine, cfg, rounds):
         log(f"{cfg.name} round {r}")
         tail_start = [st.tail_k.shape[1] for st in states]
         rec = {"draft": [], "draft_ref": []}
+        eng.begin_round()
         for j in range(k):
             eng.draft_step(j)
             torch.cuda.synchronize()

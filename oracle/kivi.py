@@ -7,11 +7,19 @@ scheme written out here is the plain min/max one:
 
 * keys are quantised per channel over groups of 32 consecutive tokens,
   values per token over groups of 32 consecutive channels;
-* for each group: mn, mx = min, max; scale = fp16(round-nearest-even of
-  (mx - mn) / (2**b - 1)); zero = fp16(mn); code = clamp(rint((x - zero) /
-  scale), 0, 2**b - 1) computed in fp64 with the fp16-rounded scale and
-  zero (code 0 when scale == 0); dequantised value = code * scale + zero;
+* for each group: mn, mx = min, max; zero = fp16(mn); the value scale is
+  fp16(round-nearest-even of (mx - mn) / (2**b - 1)); the key scale is
+  (mx - mn) / (2**b - 1) rounded UP to three significant bits (a mini-float
+  scale, then stored as fp16, exact in its normal range); code =
+  clamp(rint((x - zero) / scale), 0, 2**b - 1) computed in fp64 with the
+  stored scale and zero (code 0 when scale == 0); dequantised value =
+  code * scale + zero;
 * b is 2 or 4.
+
+The key scale has three significant bits so that a bf16 query value (eight)
+times a key scale fits the eleven of an fp16 exactly: a GPU can then fold the
+scale into the query in fp16 without rounding. Rounding up keeps every code
+inside [0, 2**b - 1].
 
 The layout functions at the bottom define how codes and per-group
 parameters are stored for the GPU. They are pure index arithmetic.
@@ -28,14 +36,25 @@ def fp16_round(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
-def _quantize_groups(x, bits: int, axis: int):
+def round_up_3sig(x) -> np.ndarray:
+    """Smallest value with at most three significant bits that is >= x
+    (x >= 0; 0 stays 0), returned as its fp16 rounding (fp64 values)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    pos = x > 0
+    m, e = np.frexp(x[pos])  # x = m * 2**e, m in [0.5, 1)
+    out[pos] = np.ldexp(np.ceil(m * 8.0) / 8.0, e)
+    return fp16_round(out)
+
+
+def _quantize_groups(x, bits: int, axis: int, key_scale: bool = False):
     """Quantise along ``axis`` (the group axis). Returns codes, scale, zero
     (scale and zero keep the reduced axis with length 1)."""
     qmax = float((1 << bits) - 1)
     x = np.asarray(x, dtype=np.float64)
     mn = x.min(axis=axis, keepdims=True)
     mx = x.max(axis=axis, keepdims=True)
-    scale = fp16_round((mx - mn) / qmax)
+    scale = round_up_3sig((mx - mn) / qmax) if key_scale else fp16_round((mx - mn) / qmax)
     zero = fp16_round(mn)
     safe = np.where(scale == 0.0, 1.0, scale)
     codes = np.clip(np.rint((x - zero) / safe), 0.0, qmax)
@@ -53,7 +72,7 @@ def quantize_keys(K, bits: int):
     if T % GROUP:
         raise ValueError("key token count must be a multiple of 32")
     g = K.reshape(T // GROUP, GROUP, D)
-    codes, scale, zero = _quantize_groups(g, bits, axis=1)
+    codes, scale, zero = _quantize_groups(g, bits, axis=1, key_scale=True)
     return codes.reshape(T, D), scale[:, 0, :], zero[:, 0, :]
 
 

@@ -177,3 +177,33 @@ def test_dropper_brute_force(seed):
 def test_dropper_keep_all_is_identity():
     s = np.random.default_rng(0).random(77).astype(np.float32)
     assert select_kept(s, 1.0).tolist() == list(range(77))
+
+
+def test_key_scale_rounds_up_to_three_significant_bits():
+    """Hand-worked values, then brute force: the smallest value with at most
+    three significant bits that is >= x."""
+    from oracle.kivi import round_up_3sig
+    hand = {1.0: 1.0, 1.1: 1.25, 1.3: 1.5, 1.76: 2.0, 0.3: 0.3125, 3.0: 3.0, 5.5: 6.0, 0.0: 0.0}
+    for x, want in hand.items():
+        assert round_up_3sig(np.array([x]))[0] == want, x
+    cands = np.array(sorted({m * 2.0 ** e for m in (4, 5, 6, 7) for e in range(-16, 8)}))
+    rng = np.random.default_rng(11)
+    xs = np.exp(rng.uniform(np.log(1e-4), np.log(100.0), 2000))
+    got = round_up_3sig(xs)
+    for x, r in zip(xs, got):
+        assert r == cands[np.searchsorted(cands, x)], (x, r)
+
+
+def test_key_scale_times_bf16_query_is_exact_in_fp16():
+    """The property the key-scale rule exists for: a bf16 query value times a
+    stored key scale is an fp16 value (inside fp16's normal range)."""
+    from oracle import to_bf16
+    rng = np.random.default_rng(12)
+    K = rng.standard_normal((256, 64)) * np.where(rng.random(64) < 0.1, 8.0, 1.0)
+    for bits in (2, 4):
+        _, scale, _ = quantize_keys(K, bits)
+        q = to_bf16(rng.standard_normal((scale.shape[0], 64)))
+        prod = q * scale.astype(np.float64)
+        normal = np.abs(prod) >= 2.0 ** -14
+        assert normal.mean() > 0.9
+        assert np.array_equal(fp16_round(prod[normal]), prod[normal])

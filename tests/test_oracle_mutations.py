@@ -53,11 +53,12 @@ def test_accept_off_by_one_is_caught(monkeypatch):
 
 
 def test_floor_instead_of_round_is_caught(monkeypatch):
-    def bad_groups(x, bits, axis):
+    def bad_groups(x, bits, axis, key_scale=False):
         qmax = float((1 << bits) - 1)
         mn = x.min(axis=axis, keepdims=True)
         mx = x.max(axis=axis, keepdims=True)
-        scale = oracle.kivi.fp16_round((mx - mn) / qmax)
+        raw = (mx - mn) / qmax
+        scale = oracle.kivi.round_up_3sig(raw) if key_scale else oracle.kivi.fp16_round(raw)
         zero = oracle.kivi.fp16_round(mn)
         safe = np.where(scale == 0.0, 1.0, scale)
         codes = np.clip(np.floor((x - zero) / safe), 0.0, qmax)

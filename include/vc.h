@@ -246,7 +246,9 @@ vc_status vc_commit_round(const vc_attn_shape *shape, int32_t k, const int32_t *
 /* ------------------------------------------------------------------------- */
 /* KIVI compression of a context: rows [0, n_body) of bf16 src_k / src_v
  * [u][src_t_cap][D] become body blocks [0, n_body/32) with the min/max rule
- * scale = fp16(rne((max - min) / (2^bits - 1))), zero = fp16(min),
+ * zero = fp16(min); value scale = fp16(rne((max - min) / (2^bits - 1)));
+ * key scale = (max - min) / (2^bits - 1) rounded up to three significant
+ * bits (stored as fp16: a bf16 query value times it is exact in fp16),
  * code = clamp(rint((x - zero) / scale), 0, 2^bits - 1) in fp64 (0 when
  * scale == 0); rows [n_body, n_body + n_tail) become the fp16 tail (the
  * recent-token residual). Sets body_len[b] = n_body, tail_len[b] = n_tail. */

@@ -373,15 +373,16 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
 
 // Query data of one wave, fixed over the body (one head set, g <= HS).
 //   qp: A layout, lane (q, (hl, jr)), run w = K-step W*jr + w: fp16 pairs
-//       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)] *
-//       log2(e)/sqrt(D), zero for padding heads;
-//   qz: score layout, lane (q, t): the same scaled query of head HPL*q + u
-//       at channels CPL*t + e, in fp32.
+//       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)], zero for
+//       padding heads (the scores are scaled after the MFMA);
+//   qz: score layout, lane (q, t): the query of head HPL*q + u at channels
+//       CPL*t + e times log2(e)/sqrt(D), in fp32.
 template <int D, int W>
 struct KiviQuery {
   static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL;
   uint32_t qp[W][4];
   float qz[HPL][CPL];
+  float qscale;  // log2(e)/sqrt(D), applied to the fp32 scores
 };
 
 template <int D, int W>
@@ -398,10 +399,12 @@ __device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, 
       float x[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        x[e] = ok ? bf16_bits_to_f32(qb[(size_t)hl * D + 8 * (qg * NG + W * jr + w) + kperm(2 * r + e)]) * P.qscale
-                  : 0.f;
+        x[e] = ok ? bf16_bits_to_f32(qb[(size_t)hl * D + 8 * (qg * NG + W * jr + w) + kperm(2 * r + e)]) : 0.f;
+      // unscaled: a bf16 query value is an fp16 value (above 2^-14), so the
+      // only rounding left before the MFMA is that of q * key scale
       Q.qp[w][r] = pack_f16(x[0], x[1]);
     }
+  Q.qscale = P.qscale;
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
     const int hb = HPL * qg + u;
@@ -429,7 +432,9 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
 
   // query with the key scales of this lane's runs folded in: register r of
   // run w pairs run channels kperm(2r), kperm(2r + 1), i.e. the low (r even)
-  // or high (r odd) halves of scale words 4w + 2(r >> 1) and the next one
+  // or high (r odd) halves of scale words 4w + 2(r >> 1) and the next one.
+  // The products are exact: a key scale has at most three significant bits
+  // and a bf16 query value eight, within fp16's eleven.
   uint32_t Aq[W][4];
 #pragma unroll
   for (int w = 0; w < W; ++w)
@@ -466,7 +471,7 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
     }
   }
   float s[HPL][2];
-  row_scores<D, W>(c, 1.f, s);
+  row_scores<D, W>(c, Q.qscale, s);
   uint32_t Pp[4];
   soft_block<D, W, 1, false>(st, 0, s, bias, lane, lds_p, Pp);
   // value scales into P~ (one per channel group of the column), value zero

@@ -72,6 +72,18 @@ struct QuantParams {
   int Hkv, body_cap;
 };
 
+// Key scales: the smallest value with at most three significant bits that is
+// >= x (then fp16; exact in fp16's normal range). A bf16 query value times
+// such a scale needs at most 8 + 3 significant bits, so the draft kernel's
+// fp16 fold of the scale into the query is exact; rounding up keeps every
+// code in range.
+__device__ __forceinline__ double round_up_3sig(double x) {
+  if (!(x > 0.0)) return 0.0;
+  int e;
+  const double m = frexp(x, &e);  // x = m * 2^e, m in [0.5, 1)
+  return ldexp(ceil(m * 8.0) / 8.0, e);
+}
+
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P) {
   constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64, QMAX = (1 << BITS) - 1;
@@ -110,7 +122,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
       mn = fmin(mn, vals_k[t][d]);
       mx = fmax(mx, vals_k[t][d]);
     }
-    const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)QMAX), zb = f64_to_f16_bits(mn);
+    const uint16_t sb = f64_to_f16_bits(round_up_3sig((mx - mn) / (double)QMAX)), zb = f64_to_f16_bits(mn);
     const double sc = f16_bits_to_f64(sb), ze = f16_bits_to_f64(zb);
     for (int t = 0; t < 32; ++t) {
       double c = 0.0;

@@ -326,6 +326,148 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
   }
 }
 
+// Tiled kernel (up to 18 row tiles): 8 waves = 2 row groups x 4 vocab
+// groups; a workgroup covers 256 vocab rows and all rows of the hidden
+// matrix. W and hidden rows move in 32-wide k slices through a 4-stage LDS
+// ring of direct-to-LDS loads (1 KB each: 16 rows x 64 bytes), issued by all
+// waves three stages ahead; one workgroup barrier per stage. Each wave
+// multiplies its 4 vocab tiles by its NMT2 row tiles from LDS (A and B
+// operands are 16-byte reads of one row each, conflict-free), so W is read
+// from HBM once at full rate while the MFMA work per byte of LDS stays high.
+// Switched off: on its first run (M = 33, three row tiles) this kernel made
+// the GPU report an illegal memory access, and again after the reads of
+// rows-less waves were removed; the cause is not found yet, so the plan never
+// selects it and the staged kernel serves every M above 32.
+constexpr bool kTiledEnabled = false;
+constexpr int kTiledWaves = 8;
+constexpr int kTVG = 4;              // vocab groups of 64 rows
+constexpr int kTRows = kTVG * 64;    // vocab rows per workgroup
+constexpr int kTStages = 4;
+constexpr int kTWBytes = kTRows * 64;  // W slice of a stage: 256 rows x 32 k (bf16)
+
+template <int NMT2>
+struct TiledGeo {
+  static constexpr int HCH = 2 * NMT2;                               // hidden 1 KB chunks of a stage
+  static constexpr int HPW = (HCH + kTiledWaves - 1) / kTiledWaves;  // hidden chunks issued per wave
+  static constexpr int NI = 2 + HPW;                                 // loads per wave per stage
+  static constexpr int SB = kTWBytes + HCH * 1024;                   // bytes per stage
+};
+
+__device__ __forceinline__ uint32_t lds_addr32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+// 16-byte LDS read the compiler does not track (it would otherwise wait for
+// every pending direct-to-LDS load before it); ordered by the ring's waits.
+__device__ __forceinline__ u32x4 lds_read16(const char* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(lds_addr32(p)) : "memory");
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+template <int NMT2>
+__global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P) {
+  using G = TiledGeo<NMT2>;
+  constexpr int NA = 4;
+  __shared__ __attribute__((aligned(16))) char ring[kTStages * G::SB];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, qg = lane >> 4;
+  const int vg = wave % kTVG, mg = wave / kTVG;
+  const int vwg = blockIdx.x * kTRows;
+  const int mtiles = P.Mp / 16, hch = P.Mp / 16;  // valid hidden chunks per stage
+  const bool active = mg * NMT2 < mtiles;           // this wave's row group holds rows
+  const int nk = P.K / 32;
+  // buffer resources: this workgroup's W rows, and the padded hidden rows
+  const uint64_t wb = reinterpret_cast<uint64_t>(P.w + (size_t)vwg * P.K);
+  const uint32_t wrows = (uint32_t)max(0, min(kTRows, P.V - vwg));
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(wb >> 32)) << 32) |
+                              __builtin_amdgcn_readfirstlane((uint32_t)wb)),
+      (short)0, (int)__builtin_amdgcn_readfirstlane(wrows * (uint32_t)P.K * 2u), 0x00020000);
+  const uint64_t hbb = reinterpret_cast<uint64_t>(P.hb);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(hbb >> 32)) << 32) |
+                              __builtin_amdgcn_readfirstlane((uint32_t)hbb)),
+      (short)0, (int)__builtin_amdgcn_readfirstlane((uint32_t)P.Mp * (uint32_t)P.K * 2u), 0x00020000);
+  // lane l of a 1 KB chunk: row 16c + l/4, 16-byte piece l%4 of the 64-byte k slice
+  const int lrow = lane >> 2, lpiece = lane & 3;
+  auto issue = [&](int st) {
+    char* stage = ring + (st % kTStages) * G::SB;
+    const int k0 = min(st, nk - 1) * 32;  // past the end: reload the last slice into an unused stage
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = wave + kTiledWaves * j;  // W chunks 0..15
+      const int voff = ((16 * c + lrow) * P.K + k0) * 2 + 16 * lpiece;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(stage + c * 1024), 16,
+                                               voff, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < G::HPW; ++j) {
+      const int c = min(wave + kTiledWaves * j, hch - 1);  // beyond the rows: the last chunk again
+      const int voff = ((16 * c + lrow) * P.K + k0) * 2 + 16 * lpiece;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rh, (__attribute__((address_space(3))) void*)(stage + kTWBytes + c * 1024), 16, voff, 0, 0, 0);
+    }
+  };
+  f32x4 acc[NA][NMT2];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NMT2; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int st = 0; st < nk; ++st) {
+    wait_vmcnt<2 * G::NI>();  // this wave's loads of stage st have landed
+    __builtin_amdgcn_s_barrier();  // everyone's have, and stage st - 1 is read
+    issue(st + 3);
+    // The reads are asynchronous and the compiler does not know it: every
+    // path that issues one waits for it (lgkmcnt(0)) before anything else can
+    // be given its registers, so a wave without row tiles issues none.
+    if (active) {
+      const char* stage = ring + (st % kTStages) * G::SB;
+      u32x4 A[NA], B[NMT2];
+#pragma unroll
+      for (int a = 0; a < NA; ++a) A[a] = lds_read16(stage + (64 * vg + 16 * a + n) * 64 + 16 * qg);
+#pragma unroll
+      for (int t = 0; t < NMT2; ++t)
+        B[t] = (mg * NMT2 + t < mtiles) ? lds_read16(stage + kTWBytes + (16 * (mg * NMT2 + t) + n) * 64 + 16 * qg)
+                                        : u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every read above has returned
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NMT2; ++t)
+        if (mg * NMT2 + t < mtiles)
+#pragma unroll
+          for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a], B[t], acc[a][t]);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  int mrow[NMT2];
+#pragma unroll
+  for (int t = 0; t < NMT2; ++t) mrow[t] = 16 * (mg * NMT2 + t);
+  uint64_t best[NMT2];
+  epilogue<NA, NMT2>(P, acc, vwg + 64 * vg, mrow, lane, best);
+  // reduce over the 4 vocab groups of each row through LDS (the ring is idle)
+  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [kTVG][Mp]
+#pragma unroll
+  for (int t = 0; t < NMT2; ++t)
+    if (qg == 0 && mg * NMT2 + t < mtiles) red[vg * P.Mp + 16 * (mg * NMT2 + t) + n] = best[t];
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 64 * kTiledWaves) {
+    uint64_t k = red[m];
+#pragma unroll
+    for (int w = 1; w < kTVG; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+  }
+}
+
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
   const int m = blockIdx.x;
   uint64_t k = 0;
@@ -360,8 +502,9 @@ void launch_staged(const VocabParams& P, hipStream_t s, hipEvent_t start, hipEve
 
 struct VocabPlan {
   bool stream;
-  int ms;  // stream: m-tiles
-  int nmt; // staged: m-tiles template bound
+  int ms;     // stream: m-tiles
+  int nmt;    // staged: m-tiles template bound
+  int tiled;  // tiled: m-tiles per wave (0 = not tiled)
   int nwg;
   int Mp;
 };
@@ -375,6 +518,10 @@ VocabPlan vocab_plan(int M, int K, int V) {
     p.stream = true;
     p.ms = mt;
     p.nwg = (V + 255) / 256;
+  } else if (kTiledEnabled && mt <= 18) {
+    p.stream = false;
+    p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
+    p.nwg = (V + kTRows - 1) / kTRows;
   } else {
     p.stream = false;
     p.nmt = mt <= 4 ? 4 : mt <= 8 ? 8 : mt <= 12 ? 12 : mt <= 18 ? 18 : mt <= 24 ? 24 : 28;
@@ -417,6 +564,11 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   if (plan.stream) {
     if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
     else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
+  } else if (plan.tiled) {
+    const dim3 grid(plan.nwg), block(64 * kTiledWaves);
+    if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);
+    else if (plan.tiled == 6) launch_ev(vocab_tiled_kernel<6>, grid, block, 0, stream, mstart, mstop, P);
+    else launch_ev(vocab_tiled_kernel<9>, grid, block, 0, stream, mstart, mstop, P);
   } else {
     switch (plan.nmt) {
       case 4: launch_staged<4>(P, stream, mstart, mstop); break;

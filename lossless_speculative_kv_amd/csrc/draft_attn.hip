@@ -3,12 +3,14 @@
 // bound by HBM bandwidth, so the kernel streams the compressed bytes once and
 // dequantises in registers).
 //
-// Work decomposition: one workgroup (4 waves) per (body split, KV head,
-// sequence), plus one extra split per (KV head, sequence) for the
-// unquantised tail. Each wave owns a contiguous run of 32-token blocks and
-// keeps an online-softmax state for all g query heads of the KV head; the 4
-// wave states are merged through LDS, and the per-split partials (max, sum,
-// unnormalised output) are merged in split order by draft_merge_kernel.
+// Work decomposition: one workgroup per (split, KV head, sequence). A KIVI
+// workgroup has NW body waves, which are dealt the split's quantised 32-token
+// blocks in turn, and one wave for the split's share of the fp16 tail; a row
+// workgroup (token drop, dense) has 4 waves that each own a contiguous run of
+// blocks and then a share of the tail. Every wave keeps an online-softmax
+// state for all g query heads of the KV head; the wave states are merged
+// through LDS, and the per-split partials (max, sum, unnormalised output) are
+// merged in split order by draft_merge_kernel.
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
 // for bf16 rows). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
@@ -284,6 +286,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) int lds_int;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -625,26 +628,23 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
   }
 }
 
-// Merge the 4 wave states of the workgroup and store the split's partial
-// (running max, sum and unnormalised output per query head). lds must hold
-// kWaves * NH * (D + 2) floats; it may alias the row staging area (the
-// leading barrier orders the reuse). The splits are merged by a second
-// kernel: a merge by the last workgroup to finish would need a device-scope
-// release and acquire in every workgroup, which on a part whose L2 is split
-// per XCD means an L2 writeback and invalidate each.
+// The wave merge at the end of a workgroup. Each wave first writes its state
+// in one layout for every state type: per query head of the unit, the
+// unnormalised output row (D floats, the value zero-point term added) and
+// (running max, sum). Then all threads merge the waves and store the split's
+// partial. The splits are merged by a second kernel: a merge by the last
+// workgroup to finish would need a device-scope release and acquire in every
+// workgroup, which on a part whose L2 is split per XCD means an L2 writeback
+// and invalidate each.
+//   o: [NH][D] floats of this wave; ml: [NH][2] floats of this wave.
 template <int D, int W, int NHS>
-__device__ __forceinline__ void store_partial(const DraftParams& P, int b, int hk, int split, int lane, int wave,
-                                              DState<D, W, NHS>& st, bool has_zero, float* lds) {
+__device__ __forceinline__ void dump_state(int lane, DState<D, W, NHS>& st, bool has_zero, float* o, float* ml) {
   using G = Geo<D, W>;
-  constexpr int NR = G::NR, HS = G::HS, HPL = G::HPL, NH = NHS * HS;
+  constexpr int NR = G::NR, HS = G::HS, HPL = G::HPL;
   const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
-  float* lds_o = lds;
-  float* lds_ml = lds + kWaves * NH * D;
-  __syncthreads();
 #pragma unroll
   for (int h = 0; h < NHS; ++h) {
-    const int head = h * HS + hl;
-    float* o = lds_o + ((size_t)wave * NH + head) * D;
+    float* oh = o + (size_t)(h * HS + hl) * D;
     // column (hl, jr) is valid for the 2W channel tiles of row group jr. The
     // tile index is lane-dependent, so the values are picked with selects:
     // an indexed access (or branches the compiler folds into one) would move
@@ -660,7 +660,7 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
           const float x = st.acc[h][2 * W * jj + mm][r];
           v = (jr == jj) ? x : v;
         }
-        o[16 * (2 * W * jr + mm) + 4 * qg + r] = v + zt;
+        oh[16 * (2 * W * jr + mm) + 4 * qg + r] = v + zt;
       }
     }
 #pragma unroll
@@ -668,26 +668,31 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
       const float l = row_sum16(st.l[h][u]);
       const int hb = h * HS + HPL * qg + u;
       if (n == 0) {
-        lds_ml[(wave * NH + hb) * 2] = st.m[h][u];
-        lds_ml[(wave * NH + hb) * 2 + 1] = l;
+        ml[hb * 2] = st.m[h][u];
+        ml[hb * 2 + 1] = l;
       }
     }
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < P.g * D; idx += 64 * kWaves) {
+}
+
+// Merge NWV wave states (written by dump_state; wave w's at o_of(w), ml_of(w))
+// and store the split's partial (running max, sum and unnormalised output per
+// query head of the unit). Called by all threads of the workgroup (nthreads).
+template <int D, typename OFn, typename MLFn>
+__device__ __forceinline__ void merge_waves(const DraftParams& P, int b, int hk, int split, int nwv, int nthreads,
+                                            const OFn& o_of, const MLFn& ml_of) {
+  for (int idx = threadIdx.x; idx < P.g * D; idx += nthreads) {
     const int head = idx / D, c = idx % D;
     float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_ml[(w * NH + head) * 2]);
+    for (int w = 0; w < nwv; ++w) M = fmaxf(M, ml_of(w)[head * 2]);
     float O = 0.f, L = 0.f;
     if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = lds_ml[(w * NH + head) * 2];
+      for (int w = 0; w < nwv; ++w) {
+        const float mw = ml_of(w)[head * 2];
         if (mw != kNegInf) {
           const float a = fast_exp2(mw - M);
-          O += lds_o[((size_t)w * NH + head) * D + c] * a;
-          L += lds_ml[(w * NH + head) * 2 + 1] * a;
+          O += o_of(w)[(size_t)head * D + c] * a;
+          L += ml_of(w)[head * 2 + 1] * a;
         }
       }
     }
@@ -698,6 +703,23 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
       P.part_ml[row * 2 + 1] = L;
     }
   }
+}
+
+// Merge the kWaves wave states of a row-kernel workgroup and store the
+// split's partial. lds must hold kWaves * NH * (D + 2) floats; it may alias
+// the row staging area (the leading barrier orders the reuse).
+template <int D, int W, int NHS>
+__device__ __forceinline__ void store_partial(const DraftParams& P, int b, int hk, int split, int lane, int wave,
+                                              DState<D, W, NHS>& st, bool has_zero, float* lds) {
+  constexpr int NH = NHS * Geo<D, W>::HS;
+  float* lds_o = lds;
+  float* lds_ml = lds + kWaves * NH * D;
+  __syncthreads();
+  dump_state<D, W, NHS>(lane, st, has_zero, lds_o + (size_t)wave * NH * D, lds_ml + wave * NH * 2);
+  __syncthreads();
+  merge_waves<D>(
+      P, b, hk, split, kWaves, 64 * kWaves, [&](int w) { return lds_o + (size_t)w * NH * D; },
+      [&](int w) { return lds_ml + w * NH * 2; });
 }
 
 template <int D>
@@ -755,64 +777,126 @@ __device__ __forceinline__ void tail_share(const DraftParams& P, int b, int hk, 
   }
 }
 
-// LDS of the KIVI kernel: NS ring stages (one per variable, so the compiler
-// can tell which pending direct-to-LDS loads a read depends on; the first
-// also hosts the wave merge at the end), then the probability areas.
+// Waves of a KIVI workgroup: NW body waves stream the quantised blocks, one
+// more wave takes the fp16 tail. A workgroup holds a whole CU (its LDS ring
+// or its registers leave no room for a second): a CU running two workgroups
+// serves the older one first, so its younger one ends long after the older
+// and the last part of the launch runs on half the waves. NW is eight where
+// three waves of the kernel fit one SIMD's registers, three where only one
+// does (four channel groups per MFMA row).
 template <int D, int BITS, int W>
-struct KiviLds {
-  static constexpr int STAGE = kWaves * BlockLayout<D, BITS>::BYTES;
-  // ring depth for one-group rows: six stages while they fit in 72 KB (two
-  // workgroups per CU, four blocks in flight per wave), else four within
-  // 48 KB (three workgroups); wider rows do more work per block and keep
-  // three stages at three workgroups per CU
-  static constexpr int NS = (W == 1 && 6 * STAGE <= 72 * 1024) ? 6 : (W == 1 && 4 * STAGE <= 48 * 1024) ? 4 : 3;
-  static constexpr int MERGE = kWaves * Geo<D, W>::HS * (D + 2) * 4;
-  static constexpr int STAGE0 = STAGE > MERGE ? STAGE : MERGE;
+struct KiviShape {
+  static constexpr int NW = (D == 128 && W == 4) ? 3 : 8;
+  static_assert(NW <= 8, "progress slots");
+  static constexpr int THREADS = 64 * (NW + 1);
+  static constexpr int MIN_WAVES = (NW + 1 + 3) / 4;  // waves per SIMD the registers must allow
+  // heads of the wave-merge layout: the body head set, which the tail's
+  // one-group head sets cover exactly
+  static constexpr int NHS1 = (Geo<D, W>::HS + Geo<D, 1>::HS - 1) / Geo<D, 1>::HS;
+  static constexpr int NH = Geo<D, W>::HS;
+  static_assert(NHS1 * Geo<D, 1>::HS == NH, "tail head sets");
 };
 
-// Waves per SIMD to plan registers for (the six-stage ring allows two
-// workgroups per CU; wider rows hold more heads per lane).
+// LDS of the KIVI kernel: NS ring stages (one per variable, so the compiler
+// can tell which pending direct-to-LDS loads a read depends on; the first
+// also hosts the body waves' merge layout at the end), the tail wave's merge
+// layout and row staging, then the probability areas.
 template <int D, int BITS, int W>
-constexpr int kivi_min_waves() {
-  return W == 1 ? (KiviLds<D, BITS, W>::NS == 6 ? 2 : 3) : (Geo<D, W>::NR > 1 ? 2 : 1);
-}
+struct KiviLds {
+  static constexpr int NW = KiviShape<D, BITS, W>::NW, NH = KiviShape<D, BITS, W>::NH;
+  static constexpr int STAGE = NW * BlockLayout<D, BITS>::BYTES;
+  // ring depth for one-group rows: six stages (four blocks in flight per
+  // wave) while they fit in 150 KB; wider rows do more work per block and
+  // keep three stages
+  static constexpr int NS = (W == 1 && 6 * STAGE <= 150 * 1024) ? 6 : 3;
+  static constexpr int MERGE = NW * NH * (D + 2) * 4;
+  static constexpr int STAGE0 = STAGE > MERGE ? STAGE : MERGE;
+  static constexpr int TAIL = NH * (D + 2) * 4;
+  static constexpr int PAREA = p_area_words<D, W, 1>();  // per wave, words
+  static_assert(p_area_words<D, 1, KiviShape<D, BITS, W>::NHS1>() == PAREA, "probability area");
+};
 
-// KIVI body + fp16 tail, one head set of HS = 16*W/NG >= g query heads.
+// KIVI body + fp16 tail, one head set of HS = 16*W/NG >= g query heads. The
+// body blocks of a (sequence, KV head) are cut into P.S ranges of NW * P.bpw
+// blocks, one per workgroup; tail block j goes to the tail wave of workgroup
+// j mod P.S.
 template <int D, int BITS, int W>
-__global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kivi_kernel(const DraftParams P) {
-  constexpr int NG = D / 32, WPT = D * BITS / 32, VWL = D * BITS / 64;
+__global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BITS, W>::MIN_WAVES)) void draft_kivi_kernel(
+    const DraftParams P) {
   using BL = BlockLayout<D, BITS>;
   using LL = KiviLds<D, BITS, W>;
+  constexpr int NW = LL::NW, NH = LL::NH, NHS1 = KiviShape<D, BITS, W>::NHS1;
   __shared__ __attribute__((aligned(16))) char rs0[LL::STAGE0];
   __shared__ __attribute__((aligned(16))) char rs1[LL::STAGE];
   __shared__ __attribute__((aligned(16))) char rs2[LL::STAGE];
   __shared__ __attribute__((aligned(16))) char rs3[LL::NS > 3 ? LL::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char rs4[LL::NS > 4 ? LL::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char rs5[LL::NS > 4 ? LL::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) uint32_t parea[kWaves * p_area_words<D, W, 1>()];
+  __shared__ __attribute__((aligned(16))) char rs4[LL::NS > 3 ? LL::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char rs5[LL::NS > 3 ? LL::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float tail_merge[LL::TAIL / 4];
+  __shared__ __attribute__((aligned(16))) uint16_t tail_rows[32 * (D + 4)];
+  __shared__ __attribute__((aligned(16))) uint32_t parea[(NW + 1) * LL::PAREA];
+  __shared__ __attribute__((aligned(16))) int progress[8];  // blocks each body wave has started
   // the wave index is uniform across the wave; saying so keeps the per-block
   // offsets in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
-  uint32_t* lds_p = parea + wave * p_area_words<D, W, 1>();
+  uint32_t* lds_p = parea + wave * LL::PAREA;
+  float* const body_o = reinterpret_cast<float*>(rs0);
+  float* const body_ml = body_o + NW * NH * D;
+
+  if (threadIdx.x < 8) progress[threadIdx.x] = 0;
+  __syncthreads();
 
   DState<D, W, 1> st;
   st.init();
-  // the fp16 tail (read without staging) takes a last split of its own, so
-  // that its slower blocks run beside the body instead of after it
-  const bool tail_split = (split == P.S - 1);
-  if (!tail_split) {
+  if (wave < NW) {
+    // Two body waves share a SIMD, and its issue arbiter prefers the older
+    // one at equal priority, which would finish its blocks well before its
+    // sibling. A wave that has fallen behind the leading wave of the
+    // workgroup raises its priority until it catches up, so the body waves
+    // end together (the block assignment, and with it every result, stays
+    // the same).
+    // The exchange is one asm block that waits for its own LDS accesses: as
+    // plain LDS accesses the compiler would order them after every pending
+    // direct-to-LDS load, and branches around s_setprio would split the
+    // pipelined step.
+    const uint32_t prog_lds = (uint32_t)(uintptr_t)(lds_int*)progress;
+    auto pace = [&](int i) {
+      u32x4 lo, hi;
+      asm volatile(
+          "ds_write_b32 %2, %3\n\t"
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(lo), "=&v"(hi)
+          : "v"(prog_lds + 4 * wave), "v"(i), "v"(prog_lds));
+      int lead = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) lead = max(lead, (int)(w < 4 ? lo[w] : hi[w - 4]));
+      const int lag = __builtin_amdgcn_readfirstlane(lead - i);
+      asm volatile(
+          "s_cmp_gt_i32 %0, 0\n\t"
+          "s_cbranch_scc0 1f\n\t"
+          "s_setprio 1\n\t"
+          "s_branch 2f\n"
+          "1:\n\t"
+          "s_setprio 0\n"
+          "2:"
+          :
+          : "s"(lag)
+          : "scc");
+    };
     KiviQuery<D, W> Q;
     kivi_query<D, W>(P, b, hk, lane, Q);
     const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;
-    // the workgroup's blocks [g0, g1) are dealt to its waves in turn (wave w
-    // takes g0 + w, g0 + w + kWaves, ...), so the waves of a workgroup read
-    // neighbouring records; i counts this wave's blocks
-    const int g0 = split * kWaves * P.bpw;
-    const int g1 = min(g0 + kWaves * P.bpw, nblk);
-    const int cnt = max(0, (g1 - g0 - wave + kWaves - 1) / kWaves);
-    auto gblk = [&](int i) { return g0 + wave + kWaves * i; };
+    // the workgroup's blocks [g0, g1) are dealt to its body waves in turn
+    // (wave w takes g0 + w, g0 + w + NW, ...), so the waves of a workgroup
+    // read neighbouring records; i counts this wave's blocks
+    const int g0 = split * NW * P.bpw;
+    const int g1 = min(g0 + NW * P.bpw, nblk);
+    const int cnt = max(0, (g1 - g0 - wave + NW - 1) / NW);
+    auto gblk = [&](int i) { return g0 + wave + NW * i; };
     const int b0 = 0, b1 = cnt;
     if (b0 < b1) {
       const size_t nbc = (size_t)(P.body_cap / 32);
@@ -823,22 +907,15 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kiv
       char* const w1 = rs1 + wave * BL::BYTES;
       char* const w2 = rs2 + wave * BL::BYTES;
       char* const w3 = rs3 + (NS > 3 ? wave * BL::BYTES : 0);
-      char* const w4 = rs4 + (NS > 4 ? wave * BL::BYTES : 0);
-      char* const w5 = rs5 + (NS > 4 ? wave * BL::BYTES : 0);
-      // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of the
-      // next block move from LDS to registers at the end of a step, so their
+      char* const w4 = rs4 + (NS > 3 ? wave * BL::BYTES : 0);
+      char* const w5 = rs5 + (NS > 3 ? wave * BL::BYTES : 0);
+      // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of a
+      // later block move from LDS to registers at the end of a step, so their
       // latency overlaps the step's last MFMAs. Past the wave's last block
       // the last one is loaded again (into a stage that is not read), which
       // keeps every wait count constant.
       const int last = b1 - 1;
       KiviRaw<D, BITS, W> ra, rb;
-      auto step = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt, char* refill, int refill_blk,
-                      const char* next_stage) {
-        issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
-        kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
-        wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
-        kivi_read<D, BITS, W>(nxt, next_stage, lane);
-      };
       issue_block<D, BITS>(w0, res, gblk(b0), lane);
       issue_block<D, BITS>(w1, res, gblk(min(b0 + 1, last)), lane);
       if constexpr (NS == 6) {
@@ -848,6 +925,7 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kiv
         auto step3 = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt2, char* refill, int refill_blk,
                          const char* stage2) {
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
+          pace(refill_blk - 5);
           kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
           wait_vm<3 * BL::NI>();  // block i + 2 has landed
           kivi_read<D, BITS, W>(nxt2, stage2, lane);
@@ -872,21 +950,15 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kiv
           step3(rc, rb, w4, blk + 10, w1);
           if (blk + 6 > last) break;
         }
-      } else if constexpr (NS == 4) {
-        issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
-        wait_vm<2 * BL::NI>();
-        kivi_read<D, BITS, W>(ra, w0, lane);
-        for (int blk = b0;; blk += 4) {
-          step(ra, rb, w3, blk + 3, w1);
-          if (blk + 1 > last) break;
-          step(rb, ra, w0, blk + 4, w2);
-          if (blk + 2 > last) break;
-          step(ra, rb, w1, blk + 5, w3);
-          if (blk + 3 > last) break;
-          step(rb, ra, w2, blk + 6, w0);
-          if (blk + 4 > last) break;
-        }
       } else {
+        auto step = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt, char* refill, int refill_blk,
+                        const char* next_stage) {
+          issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
+          pace(refill_blk - 2);
+          kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
+          wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
+          kivi_read<D, BITS, W>(nxt, next_stage, lane);
+        };
         wait_vm<BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
         for (int blk = b0;; blk += 6) {
@@ -907,9 +979,9 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kiv
       wait_vm<0>();
     }
   } else {
-    // the fp16 tail with one-group rows: a separate state whose head set
-    // covers the same heads, folded into st below
-    constexpr int NHS1 = (Geo<D, W>::HS + Geo<D, 1>::HS - 1) / Geo<D, 1>::HS;
+    // the tail wave: fp16 rows with the values staged in LDS (so a block
+    // takes one trip to memory), one-group rows (a separate state whose head
+    // sets cover the body head set), written to its own merge area at once
     DState<D, 1, NHS1> st1;
     st1.init();
     uint32_t Aqm[NHS1][D / 32][4];
@@ -917,14 +989,21 @@ __global__ __launch_bounds__(256, (kivi_min_waves<D, BITS, W>())) void draft_kiv
     const int nt = min(max(P.tail_len[b], 0), P.tail_cap);
     const uint16_t* tk = P.tail_k + unit * P.tail_cap * D;
     const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
-    for (int blk = wave; blk * 32 < nt; blk += kWaves) {
+    for (int blk = split; blk * 32 < nt; blk += P.S) {
       const PlainRows<D> rows{tk + (size_t)blk * 32 * D, tv + (size_t)blk * 32 * D};
-      row_block<D, 1, NHS1, false, false>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, nullptr, lds_p);
+      row_block<D, 1, NHS1, false, true>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, tail_rows, lds_p);
     }
-    store_partial<D, 1, NHS1>(P, b, hk, split, lane, wave, st1, false, reinterpret_cast<float*>(rs0));
-    return;
+    dump_state<D, 1, NHS1>(lane, st1, false, tail_merge, tail_merge + NH * D);
   }
-  store_partial<D, W, 1>(P, b, hk, split, lane, wave, st, true, reinterpret_cast<float*>(rs0));
+  // the ring (and with it the body waves' merge area) is free once every body
+  // wave has left its loop
+  __syncthreads();
+  if (wave < NW) dump_state<D, W, 1>(lane, st, true, body_o + (size_t)wave * NH * D, body_ml + wave * NH * 2);
+  __syncthreads();
+  merge_waves<D>(
+      P, b, hk, split, NW + 1, LL::NW * 64 + 64,
+      [&](int w) { return w < NW ? body_o + (size_t)w * NH * D : tail_merge; },
+      [&](int w) { return w < NW ? body_ml + w * NH * 2 : tail_merge + NH * D; });
 }
 
 // Token-drop (GATHER) and dense draft caches: bf16 rows everywhere.
@@ -1013,29 +1092,42 @@ int pick_w(int g) {
 
 using DraftKernel = void (*)(DraftParams);
 
+// A kernel with its workgroup shape: waves that stream body blocks (nw) and
+// threads per workgroup.
+struct DraftKernelPick {
+  DraftKernel fn;
+  int nw, threads;
+};
+
+template <int D, int BITS, int W>
+DraftKernelPick kivi_pick() {
+  return DraftKernelPick{draft_kivi_kernel<D, BITS, W>, KiviShape<D, BITS, W>::NW, KiviShape<D, BITS, W>::THREADS};
+}
 template <int D, int BITS>
-DraftKernel kivi_kernel_for(int w) {
+DraftKernelPick kivi_kernel_for(int w) {
   if constexpr (D == 128) {
     switch (w) {
-      case 1: return draft_kivi_kernel<D, BITS, 1>;
-      case 2: return draft_kivi_kernel<D, BITS, 2>;
-      default: return draft_kivi_kernel<D, BITS, 4>;
+      case 1: return kivi_pick<D, BITS, 1>();
+      case 2: return kivi_pick<D, BITS, 2>();
+      default: return kivi_pick<D, BITS, 4>();
     }
   } else {
-    return w == 1 ? draft_kivi_kernel<D, BITS, 1> : draft_kivi_kernel<D, BITS, 2>;
+    return w == 1 ? kivi_pick<D, BITS, 1>() : kivi_pick<D, BITS, 2>();
   }
 }
 template <int D, bool GATHER>
-DraftKernel rows_kernel_for(int nhs) {
+DraftKernelPick rows_kernel_for(int nhs) {
+  DraftKernel k;
   switch (nhs) {
-    case 1: return draft_rows_kernel<D, 1, GATHER>;
-    case 2: return draft_rows_kernel<D, 2, GATHER>;
-    case 3: return draft_rows_kernel<D, 3, GATHER>;
-    default: return draft_rows_kernel<D, 4, GATHER>;
+    case 1: k = draft_rows_kernel<D, 1, GATHER>; break;
+    case 2: k = draft_rows_kernel<D, 2, GATHER>; break;
+    case 3: k = draft_rows_kernel<D, 3, GATHER>; break;
+    default: k = draft_rows_kernel<D, 4, GATHER>; break;
   }
+  return DraftKernelPick{k, kWaves, 64 * kWaves};
 }
 
-DraftKernel pick_kernel(const vc_attn_shape& sh, const vc_draft_kv& kv) {
+DraftKernelPick pick_kernel(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   const int D = sh.head_dim, g = sh.n_q_heads / sh.n_kv_heads;
   if (kv.kind == VC_DRAFT_KIVI) {
     const int w = D == 128 ? pick_w<128>(g) : pick_w<64>(g);
@@ -1049,8 +1141,10 @@ DraftKernel pick_kernel(const vc_attn_shape& sh, const vc_draft_kv& kv) {
 
 // Workgroups of kernel k that the current device holds at once (CUs times
 // workgroups per CU), cached per (device, kernel). Without a device (a
-// workspace query on a host with no GPU) the 256-CU part is assumed.
-long long resident_wgs(DraftKernel k) {
+// workspace query on a host with no GPU) four per CU of a 256-CU part are
+// assumed, which is at least what any draft kernel holds, so such a
+// workspace is large enough.
+long long resident_wgs(const DraftKernelPick& k) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, long long> cache;
   int dev = -1;
@@ -1059,11 +1153,11 @@ long long resident_wgs(DraftKernel k) {
     return 256 * 4;
   }
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(k));
+  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(k.fn));
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 64 * kWaves, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k.fn), k.threads, 0) !=
           hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -1076,29 +1170,28 @@ long long resident_wgs(DraftKernel k) {
 
 }  // namespace
 
-// Split plan shared by the workspace query and the launch: as many body
-// splits as let every workgroup (body splits plus the tail split of each
-// (sequence, KV head)) be resident at once, so the kernel runs in one round.
+// Split plan shared by the workspace query and the launch: as many splits as
+// let every workgroup be resident at once, so the kernel runs in one round.
 struct DraftPlan {
-  int bpw;     // body blocks per wave
-  int splits;  // body splits (+ 1 tail split for KIVI)
+  int bpw;     // body blocks per body wave
+  int splits;  // workgroups per (sequence, KV head)
 };
 
-// The splits of every (sequence, KV head) fill the resident workgroups once.
-// KIVI keeps its fp16 tail in a last split of its own; the row kernels (token
-// drop, dense) stage the tail like the body, so every split takes body blocks
-// and a share of the tail.
+// The splits of every (sequence, KV head) fill the resident workgroups once;
+// each split takes a range of nw * bpw body blocks and a share of the tail
+// (the KIVI kernel gives its share to a wave of its own, the row kernels
+// stage it like the body).
 DraftPlan draft_plan(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   const long long blocks = (kv.body_cap + 31) / 32;
   const long long units = (long long)sh.batch * sh.n_kv_heads;
-  const bool tail_split = kv.kind == VC_DRAFT_KIVI;
-  long long body_splits = resident_wgs(pick_kernel(sh, kv)) / units - (tail_split ? 1 : 0);
-  if (body_splits < 1) body_splits = 1;
-  long long bpw = (blocks + body_splits * kWaves - 1) / (body_splits * kWaves);
+  const DraftKernelPick k = pick_kernel(sh, kv);
+  long long splits = resident_wgs(k) / units;
+  if (splits < 1) splits = 1;
+  long long bpw = (blocks + splits * k.nw - 1) / (splits * k.nw);
   if (bpw < 1) bpw = 1;
-  body_splits = (blocks + kWaves * bpw - 1) / (kWaves * bpw);
-  if (body_splits < 1) body_splits = 1;
-  return DraftPlan{(int)bpw, (int)body_splits + (tail_split ? 1 : 0)};
+  splits = (blocks + k.nw * bpw - 1) / (k.nw * bpw);
+  if (splits < 1) splits = 1;
+  return DraftPlan{(int)bpw, (int)splits};
 }
 
 // Workspace: the split partials (unnormalised outputs, then max and sum).
@@ -1142,7 +1235,8 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
   const int D = sh.head_dim;
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
-  launch_ev(pick_kernel(sh, kv), grid, dim3(64 * kWaves), 0, stream, tm.start, main_only ? tm.stop : nullptr, P);
+  const DraftKernelPick k = pick_kernel(sh, kv);
+  launch_ev(k.fn, grid, dim3(k.threads), 0, stream, tm.start, main_only ? tm.stop : nullptr, P);
   vc_status st = check_launch("draft attention");
   if (st != VC_OK) return st;
   const dim3 mgrid(sh.n_q_heads, sh.batch);

@@ -286,7 +286,6 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) int lds_int;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -851,42 +850,10 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
   DState<D, W, 1> st;
   st.init();
   if (wave < NW) {
-    // Two body waves share a SIMD, and its issue arbiter prefers the older
-    // one at equal priority, which would finish its blocks well before its
-    // sibling. A wave that has fallen behind the leading wave of the
-    // workgroup raises its priority until it catches up, so the body waves
-    // end together (the block assignment, and with it every result, stays
-    // the same).
-    // The exchange is one asm block that waits for its own LDS accesses: as
-    // plain LDS accesses the compiler would order them after every pending
-    // direct-to-LDS load, and branches around s_setprio would split the
-    // pipelined step.
-    const uint32_t prog_lds = (uint32_t)(uintptr_t)(lds_int*)progress;
-    auto pace = [&](int i) {
-      u32x4 lo, hi;
-      asm volatile(
-          "ds_write_b32 %2, %3\n\t"
-          "ds_read_b128 %0, %4\n\t"
-          "ds_read_b128 %1, %4 offset:16\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(lo), "=&v"(hi)
-          : "v"(prog_lds + 4 * wave), "v"(i), "v"(prog_lds));
-      int lead = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) lead = max(lead, (int)(w < 4 ? lo[w] : hi[w - 4]));
-      const int lag = __builtin_amdgcn_readfirstlane(lead - i);
-      asm volatile(
-          "s_cmp_gt_i32 %0, 0\n\t"
-          "s_cbranch_scc0 1f\n\t"
-          "s_setprio 1\n\t"
-          "s_branch 2f\n"
-          "1:\n\t"
-          "s_setprio 0\n"
-          "2:"
-          :
-          : "s"(lag)
-          : "scc");
-    };
+    // two body waves share each SIMD: the one behind is given the issue
+    // slots first, so the body waves end together
+    const uint32_t prog_lds = lds_addr(progress);
+    auto pace = [&](int i) { pace_waves<NW>(prog_lds, wave, i); };
     KiviQuery<D, W> Q;
     kivi_query<D, W>(P, b, hk, lane, Q);
     const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;

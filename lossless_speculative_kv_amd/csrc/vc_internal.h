@@ -130,6 +130,50 @@ __device__ __forceinline__ float sum_group(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// --------------------------------------------------------- wave pacing ----
+// Waves with equal static shares that share a SIMD do not progress equally:
+// the SIMD's issue arbiter prefers the older wave at equal priority, so the
+// younger ones finish long after. Each wave publishes the step it has
+// reached in an LDS array of 8 ints (zeroed before the first call, address
+// lds_base) and runs at priority 1 while it is behind the workgroup's
+// leading wave, else at 0. Only the timing changes, never the work a wave
+// does. The exchange is one asm block that waits for its own LDS accesses
+// (as plain LDS accesses the compiler would order them after every pending
+// direct-to-LDS load), and the priority is chosen inside asm (branches the
+// compiler sees would split a pipelined loop body).
+template <int NW>
+__device__ __forceinline__ void pace_waves(uint32_t lds_base, int wave, int step) {
+  static_assert(NW >= 1 && NW <= 8, "eight progress slots");
+  u32x4 lo, hi;
+  asm volatile(
+      "ds_write_b32 %2, %3\n\t"
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(lds_base + 4 * wave), "v"(step), "v"(lds_base));
+  int lead = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) lead = max(lead, (int)(w < 4 ? lo[w] : hi[w - 4]));
+  const int lag = __builtin_amdgcn_readfirstlane(lead - step);
+  asm volatile(
+      "s_cmp_gt_i32 %0, 0\n\t"
+      "s_cbranch_scc0 1f\n\t"
+      "s_setprio 1\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "s_setprio 0\n"
+      "2:"
+      :
+      : "s"(lag)
+      : "scc");
+}
+// LDS byte address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
+}
+
 // ------------------------------------------------------------ loads ----
 template <typename T>
 __device__ __forceinline__ T ldg(const void* p) {

@@ -12,6 +12,7 @@
 // Two kernels share the epilogue:
 //  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
 //    rows; W goes straight from HBM to registers, h (bf16, tiny) from L2.
+//    A workgroup of 8 waves fills a CU and its waves are paced.
 //  * vocab_staged: any M. Each wave owns 32 vocab rows and all M rows; the
 //    hidden rows are staged in LDS in 32-wide k chunks (double-buffered) and
 //    shared by the 8 waves of the workgroup, so W is read from HBM exactly
@@ -115,12 +116,21 @@ __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc
   }
 }
 
+// Stream kernel: 8 waves x 64 vocab rows. Its registers hold two waves per
+// SIMD, so a workgroup fills a CU (a CU with two workgroups would serve the
+// older first and finish the younger late) and the waves are paced.
+constexpr int kStreamWaves = 8;
+
 template <int MS>
-__global__ __launch_bounds__(256) void vocab_stream_kernel(const VocabParams P) {
+__global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(const VocabParams P) {
   constexpr int NA = 4;  // vocab tiles per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
-  const int vbase = (blockIdx.x * 4 + wave) * 64;
+  const int vbase = (blockIdx.x * kStreamWaves + wave) * 64;
+  __shared__ __attribute__((aligned(16))) int progress[8];  // k-steps of 256 each wave has started
+  if (threadIdx.x < 8) progress[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t prog_lds = lds_addr(progress);
   f32x4 acc[NA][MS];
 #pragma unroll
   for (int a = 0; a < NA; ++a)
@@ -160,29 +170,34 @@ __global__ __launch_bounds__(256) void vocab_stream_kernel(const VocabParams P) 
     }
   };
   u32x4 Aa[NA][4], Ab[NA][4];
-  load(Aa, 0);
-  int k0 = 0;
-  for (; k0 + 256 <= P.K; k0 += 256) {
-    load(Ab, k0 + 128);
-    compute(Aa, k0);
-    if (k0 + 256 < P.K) load(Aa, k0 + 256);
-    compute(Ab, k0 + 128);
+  // a wave past the last vocab row has nothing to stream (and must not lead
+  // the pacing)
+  if (vbase < P.V) {
+    load(Aa, 0);
+    int k0 = 0;
+    for (; k0 + 256 <= P.K; k0 += 256) {
+      load(Ab, k0 + 128);
+      pace_waves<kStreamWaves>(prog_lds, wave, k0 >> 8);
+      compute(Aa, k0);
+      if (k0 + 256 < P.K) load(Aa, k0 + 256);
+      compute(Ab, k0 + 128);
+    }
+    if (k0 < P.K) compute(Aa, k0);  // K / 128 odd: the last step is already loaded
   }
-  if (k0 < P.K) compute(Aa, k0);  // K / 128 odd: the last step is already loaded
   int mrow[MS];
 #pragma unroll
   for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
   uint64_t best[MS];
   epilogue<NA, MS>(P, acc, vbase, mrow, lane, best);
-  __shared__ uint64_t red[4][16 * MS];
+  __shared__ uint64_t red[kStreamWaves][16 * MS];
 #pragma unroll
   for (int t = 0; t < MS; ++t)
     if (qg == 0) red[wave][16 * t + n] = best[t];
   __syncthreads();
-  for (int m = threadIdx.x; m < P.M; m += 256) {
+  for (int m = threadIdx.x; m < P.M; m += 64 * kStreamWaves) {
     uint64_t k = red[0][m];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) k = red[w][m] > k ? red[w][m] : k;
+    for (int w = 1; w < kStreamWaves; ++w) k = red[w][m] > k ? red[w][m] : k;
     P.keys[(size_t)blockIdx.x * P.M + m] = k;
   }
 }
@@ -517,7 +532,7 @@ VocabPlan vocab_plan(int M, int K, int V) {
   if (mt <= 2) {
     p.stream = true;
     p.ms = mt;
-    p.nwg = (V + 255) / 256;
+    p.nwg = (V + 64 * kStreamWaves - 1) / (64 * kStreamWaves);
   } else if (kTiledEnabled && mt <= 18) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
@@ -562,8 +577,9 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
     launch_ev(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, main_only ? nullptr : tm.start, nullptr, P);
   }
   if (plan.stream) {
-    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
-    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), dim3(256), 0, stream, mstart, mstop, P);
+    const dim3 block(64 * kStreamWaves);
+    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, mstart, mstop, P);
+    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, mstart, mstop, P);
   } else if (plan.tiled) {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);

@@ -54,9 +54,9 @@ const char *vc_last_error(void);
  * calls). The next call made on this thread has its own kernel dispatches
  * record the given events: with VC_TIME_CALL, start_event when the call's
  * first kernel starts and stop_event when its last kernel ends; with
- * VC_TIME_MAIN_KERNEL, both around the call's main kernel (the attention
+ * VC_TIME_MAIN_KERNEL, both around the call's main kernel (the verification
  * kernel before its split merge, the vocab product before its argmax
- * reduction). Recording events around a call from the host instead adds a
+ * reduction; draft attention is one kernel, so both scopes time it). Recording events around a call from the host instead adds a
  * marker to the queue before and after it, which idles the GPU for a few
  * microseconds each time. Calls that take part: vc_draft_decode_attn,
  * vc_verify_attn, vc_vocab_logits; any other call discards the setting.
@@ -133,7 +133,12 @@ typedef struct {
 /* Bytes of one KIVI block record: 8 * head_dim * (bits + 1). */
 vc_status vc_kivi_block_bytes(int32_t head_dim, int32_t bits, size_t *bytes);
 
-/* Workspace size for vc_draft_decode_attn with this shape and cache. */
+/* Workspace size for vc_draft_decode_attn with this shape and cache. The
+ * workspace starts with one 32-bit split counter per (sequence, KV head): it
+ * must be all zero before its first use (e.g. hipMemset once after
+ * allocation), and every completed call leaves those words zero again, so a
+ * workspace is zeroed once and then reused. Calls that share a workspace
+ * must not run concurrently. */
 vc_status vc_draft_workspace_bytes(const vc_attn_shape *shape, const vc_draft_kv *kv, size_t *bytes);
 
 /* Draft decode attention (VeriCache summary, "Core algorithm", drafting with

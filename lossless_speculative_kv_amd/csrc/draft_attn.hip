@@ -9,8 +9,9 @@
 // workgroup (token drop, dense) has 4 waves that each own a contiguous run of
 // blocks and then a share of the tail. Every wave keeps an online-softmax
 // state for all g query heads of the KV head; the wave states are merged
-// through LDS, and the per-split partials (max, sum, unnormalised output) are
-// merged in split order by draft_merge_kernel.
+// through LDS into a per-split partial (max, sum, unnormalised output), and
+// the last workgroup of a (KV head, sequence) to store its partial merges
+// the partials in split order.
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
 // for bf16 rows). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
@@ -56,6 +57,7 @@ struct DraftParams {
   float* part_o;      // [B][Hq][S][D]
   float* part_ml;     // [B][Hq][S][2]
   float* out;         // [B][Hq][D]
+  uint32_t* counters;  // [B][Hkv] splits stored so far (zero between calls)
   int B, Hq, Hkv, g, S, bpw;
   float qscale;       // log2(e) / sqrt(D)
   int body_cap, tail_cap, src_t_cap;
@@ -631,10 +633,9 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
 // in one layout for every state type: per query head of the unit, the
 // unnormalised output row (D floats, the value zero-point term added) and
 // (running max, sum). Then all threads merge the waves and store the split's
-// partial. The splits are merged by a second kernel: a merge by the last
-// workgroup to finish would need a device-scope release and acquire in every
-// workgroup, which on a part whose L2 is split per XCD means an L2 writeback
-// and invalidate each.
+// partial, with device-coherent stores (they pass the per-XCD L2s), so the
+// workgroup that merges the splits (finish_unit) reads them without an L2
+// writeback or invalidate.
 //   o: [NH][D] floats of this wave; ml: [NH][2] floats of this wave.
 template <int D, int W, int NHS>
 __device__ __forceinline__ void dump_state(int lane, DState<D, W, NHS>& st, bool has_zero, float* o, float* ml) {
@@ -696,16 +697,71 @@ __device__ __forceinline__ void merge_waves(const DraftParams& P, int b, int hk,
       }
     }
     const size_t row = ((size_t)b * P.Hq + (size_t)hk * P.g + head) * P.S + split;
-    P.part_o[row * D + c] = O;
+    __hip_atomic_store(&P.part_o[row * D + c], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c == 0) {
-      P.part_ml[row * 2] = M;
-      P.part_ml[row * 2 + 1] = L;
+      __hip_atomic_store(&P.part_ml[row * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&P.part_ml[row * 2 + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Merge the kWaves wave states of a row-kernel workgroup and store the
-// split's partial. lds must hold kWaves * NH * (D + 2) floats; it may alias
+// Called by every thread after merge_waves. The workgroup's partial stores
+// complete, then one thread counts the split in; the workgroup that brings
+// the count to S merges the S partials of its (sequence, KV head) in split
+// order (so the result does not depend on the order in which workgroups
+// ran), writes the output and sets the count back to zero for the next
+// call. The partials are read with device-coherent loads.
+template <int D>
+__device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk, int nthreads, int* lds_flag) {
+  constexpr int kBatch = 8;  // splits whose loads are issued together
+  const size_t unit = (size_t)b * P.Hkv + hk;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(&P.counters[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = before == (uint32_t)(P.S - 1);
+  }
+  __syncthreads();
+  if (!*lds_flag) return;
+  asm volatile("" ::: "memory");
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  for (int idx = threadIdx.x; idx < P.g * D; idx += nthreads) {
+    const int hq = hk * P.g + idx / D, c = idx % D;
+    const size_t row0 = ((size_t)b * P.Hq + hq) * P.S;
+    float M = kNegInf, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < P.S; s0 += kBatch) {
+      float ms[kBatch], ls[kBatch], os[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const size_t r = row0 + min(s0 + i, P.S - 1);
+        ms[i] = s0 + i < P.S ? ld(&P.part_ml[r * 2]) : kNegInf;
+        ls[i] = ld(&P.part_ml[r * 2 + 1]);
+        os[i] = ld(&P.part_o[r * D + c]);
+      }
+      float mx = M;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
+      if (mx == kNegInf) continue;  // nothing visible so far
+      const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
+      O *= a;
+      L *= a;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const bool ok = ms[i] != kNegInf;
+        const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
+        O = ok ? fmaf(os[i], w, O) : O;
+        L = ok ? fmaf(ls[i], w, L) : L;
+      }
+      M = mx;
+    }
+    P.out[((size_t)b * P.Hq + hq) * D + c] = (L > 0.f) ? O / L : 0.f;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&P.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the kWaves wave states of a row-kernel workgroup, store the split's
+// partial and take part in the split merge. lds must hold kWaves * NH * (D + 2) floats; it may alias
 // the row staging area (the leading barrier orders the reuse).
 template <int D, int W, int NHS>
 __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int hk, int split, int lane, int wave,
@@ -719,6 +775,8 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
   merge_waves<D>(
       P, b, hk, split, kWaves, 64 * kWaves, [&](int w) { return lds_o + (size_t)w * NH * D; },
       [&](int w) { return lds_ml + w * NH * 2; });
+  __shared__ int last;
+  finish_unit<D>(P, b, hk, 64 * kWaves, &last);
 }
 
 template <int D>
@@ -971,6 +1029,8 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
       P, b, hk, split, NW + 1, LL::NW * 64 + 64,
       [&](int w) { return w < NW ? body_o + (size_t)w * NH * D : tail_merge; },
       [&](int w) { return w < NW ? body_ml + w * NH * 2 : tail_merge + NH * D; });
+  __shared__ int last;
+  finish_unit<D>(P, b, hk, LL::NW * 64 + 64, &last);
 }
 
 // Token-drop (GATHER) and dense draft caches: bf16 rows everywhere.
@@ -1004,42 +1064,6 @@ __global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
   }
   tail_share<D, NHS, true, true>(P, b, hk, split, wave, lane, st, my_lds, lds_p);
   store_partial<D, 1, NHS>(P, b, hk, split, lane, wave, st, false, reinterpret_cast<float*>(smem));
-}
-
-// Merge the splits of one (sequence, query head) in split order, so the
-// result does not depend on the order in which workgroups ran.
-template <int D>
-__global__ __launch_bounds__(D) void draft_merge_kernel(const DraftParams P) {
-  constexpr int kBatch = 8;  // splits whose loads are issued together
-  const int c = threadIdx.x, hq = blockIdx.x, b = blockIdx.y;
-  const size_t row0 = ((size_t)b * P.Hq + hq) * P.S;
-  float M = kNegInf, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < P.S; s0 += kBatch) {
-    float ms[kBatch], ls[kBatch], os[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const size_t r = row0 + min(s0 + i, P.S - 1);
-      ms[i] = s0 + i < P.S ? P.part_ml[r * 2] : kNegInf;
-      ls[i] = P.part_ml[r * 2 + 1];
-      os[i] = P.part_o[r * D + c];
-    }
-    float mx = M;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
-    if (mx == kNegInf) continue;  // nothing visible so far
-    const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
-    O *= a;
-    L *= a;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const bool ok = ms[i] != kNegInf;
-      const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
-      O = ok ? fmaf(os[i], w, O) : O;
-      L = ok ? fmaf(ls[i], w, L) : L;
-    }
-    M = mx;
-  }
-  P.out[((size_t)b * P.Hq + hq) * D + c] = (L > 0.f) ? O / L : 0.f;
 }
 
 // Head sets of the row kernel (W = 1).
@@ -1161,11 +1185,17 @@ DraftPlan draft_plan(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   return DraftPlan{(int)bpw, (int)splits};
 }
 
-// Workspace: the split partials (unnormalised outputs, then max and sum).
+// Workspace: the split counters (one 32-bit word per (sequence, KV head),
+// zero between calls), then the split partials (unnormalised outputs, then
+// max and sum).
+size_t draft_counter_bytes(const vc_attn_shape& sh) {
+  return align_up((size_t)sh.batch * sh.n_kv_heads * sizeof(uint32_t), 256);
+}
 size_t draft_ws_bytes(const vc_attn_shape& sh, const vc_draft_kv& kv) {
   const DraftPlan p = draft_plan(sh, kv);
   const size_t rows = (size_t)sh.batch * sh.n_q_heads * p.splits;
-  return align_up(rows * sh.head_dim * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
+  return draft_counter_bytes(sh) + align_up(rows * sh.head_dim * sizeof(float), 256) +
+         align_up(rows * 2 * sizeof(float), 256);
 }
 
 vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out, void* ws,
@@ -1175,6 +1205,8 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
   P.q = static_cast<const uint16_t*>(q);
   const size_t rows = (size_t)sh.batch * sh.n_q_heads * plan.splits;
   char* w = static_cast<char*>(ws);
+  P.counters = reinterpret_cast<uint32_t*>(w);
+  w += draft_counter_bytes(sh);
   P.part_o = reinterpret_cast<float*>(w);
   w += align_up(rows * sh.head_dim * sizeof(float), 256);
   P.part_ml = reinterpret_cast<float*>(w);
@@ -1198,19 +1230,13 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
   P.tail_k = static_cast<const uint16_t*>(kv.tail_k);
   P.tail_v = static_cast<const uint16_t*>(kv.tail_v);
 
+  // one kernel: the split merge happens in its last workgroup per unit, so
+  // both timing scopes cover the same dispatch
   const dim3 grid(plan.splits, sh.n_kv_heads, sh.batch);
-  const int D = sh.head_dim;
   const Timing tm = take_timing();
-  const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
   const DraftKernelPick k = pick_kernel(sh, kv);
-  launch_ev(k.fn, grid, dim3(k.threads), 0, stream, tm.start, main_only ? tm.stop : nullptr, P);
-  vc_status st = check_launch("draft attention");
-  if (st != VC_OK) return st;
-  const dim3 mgrid(sh.n_q_heads, sh.batch);
-  hipEvent_t mstop = main_only ? nullptr : tm.stop;
-  if (D == 128) launch_ev(draft_merge_kernel<128>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
-  else launch_ev(draft_merge_kernel<64>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
-  return check_launch("draft merge");
+  launch_ev(k.fn, grid, dim3(k.threads), 0, stream, tm.start, tm.stop, P);
+  return check_launch("draft attention");
 }
 
 }  // namespace vc

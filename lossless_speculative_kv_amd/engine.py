@@ -123,7 +123,9 @@ class Engine:
         self.o_ver = torch.empty((k + 1, B, Hq, D), dtype=torch.float32, device=self.dev)
 
         # workspaces
-        self.ws_draft = self._ws(L.vc_draft_workspace_bytes(sh, self.kv))
+        # the draft workspace starts with split counters that must be zero
+        # before the first call (every call leaves them zero)
+        self.ws_draft = self._ws(L.vc_draft_workspace_bytes(sh, self.kv)).zero_()
         max_chunk = c.chunk if c.staged else self.full_cap
         self.ws_verify = self._ws(L.vc_verify_workspace_bytes(sh, k + 1, max_chunk))
         self.ws_vocab_d = self._ws(L.vc_vocab_workspace_bytes(B, c.hidden, c.vocab))

@@ -108,7 +108,7 @@ def draft_queries(seed, B, Hq, D, token0=11):
 
 
 def run_draft(L, sh, kv, q_dev):
-    ws = torch.empty(L.vc_draft_workspace_bytes(sh, kv), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(L.vc_draft_workspace_bytes(sh, kv), dtype=torch.uint8, device="cuda")
     out = torch.full((sh.batch, sh.n_q_heads, sh.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     L.vc_draft_decode_attn(sh, q_dev.data_ptr(), kv, out.data_ptr(), ws.data_ptr(), ws.numel(), stream())
     torch.cuda.synchronize()
@@ -151,6 +151,35 @@ def test_draft_kivi_parity(L, case):
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
     out2 = run_draft(L, sh, kv, bf16_tensor(q)).cpu().numpy()
     assert np.array_equal(out, out2), "draft attention is not deterministic"
+
+
+def test_draft_workspace_reuse(L):
+    """One zeroed workspace serves consecutive calls: the split counters at its
+    start are zero again after every call, and each call's output matches the
+    oracle (a counter left behind would make the next call skip its merge)."""
+    B, Hq, Hkv, D, bits = 2, 32, 8, 128, 2
+    body, tail = [2048, 1024], [130, 129]
+    arr, vis, body_cap, tail_cap = build_kivi(B, Hq, Hkv, D, bits, body, tail, 321, True)
+    dev = {k: (f16_dev(v) if v.dtype == np.float16 else to_dev(v)) for k, v in arr.items()}
+    bl, tl = to_dev(np.array(body, np.int32)), to_dev(np.array(tail, np.int32))
+    sh = L.vc_attn_shape(B, Hq, Hkv, D)
+    kv = L.vc_draft_kv()
+    kv.kind, kv.bits, kv.body_cap, kv.tail_cap = L.VC_DRAFT_KIVI, bits, body_cap, tail_cap
+    kv.body_len, kv.tail_len = bl.data_ptr(), tl.data_ptr()
+    for f in ("kivi_blocks", "tail_k", "tail_v"):
+        setattr(kv, f, dev[f].data_ptr())
+    ws = torch.zeros(L.vc_draft_workspace_bytes(sh, kv), dtype=torch.uint8, device="cuda")
+    g = Hq // Hkv
+    for call, token0 in enumerate((11, 500, 77)):
+        log(f"draft workspace reuse: call {call}")
+        q = draft_queries(321, B, Hq, D, token0=token0)
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        L.vc_draft_decode_attn(sh, bf16_tensor(q).data_ptr(), kv, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                               stream())
+        torch.cuda.synchronize()
+        assert not ws[:4 * B * Hkv].any().item(), f"split counters not zero after call {call}"
+        ref = np.stack([np.stack([oracle.attend(q[b, h], *vis[b, h // g]) for h in range(Hq)]) for b in range(B)])
+        assert_attention_close(out.cpu().numpy(), ref, f"reuse call {call}")
 
 
 ROW_CASES = [

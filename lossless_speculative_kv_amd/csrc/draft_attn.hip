@@ -6,12 +6,14 @@
 // Work decomposition: one workgroup per (split, KV head, sequence). A KIVI
 // workgroup has NW body waves, which are dealt the split's quantised 32-token
 // blocks in turn, and one wave for the split's share of the fp16 tail; a row
-// workgroup (token drop, dense) has 4 waves that each own a contiguous run of
-// blocks and then a share of the tail. Every wave keeps an online-softmax
-// state for all g query heads of the KV head; the wave states are merged
-// through LDS into a per-split partial (max, sum, unnormalised output), and
-// the last workgroup of a (KV head, sequence) to store its partial merges
-// the partials in split order.
+// workgroup (token drop, dense) has as many waves as its registers allow on a
+// CU, dealt the split's blocks in turn, each then taking a share of the tail.
+// Every workgroup fills its CU, and waves that share a SIMD are paced (see
+// pace_waves). Every wave keeps an online-softmax state for all g query heads
+// of the KV head; the wave states are merged through LDS into a per-split
+// partial (max, sum, unnormalised output), and the last workgroup of a
+// (KV head, sequence) to store its partial merges the partials in split
+// order.
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
 // for bf16 rows). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
@@ -50,7 +52,6 @@ namespace vc {
 
 namespace {
 
-constexpr int kWaves = 4;
 
 struct DraftParams {
   const uint16_t* q;  // bf16 [B][Hq][D]
@@ -506,10 +507,10 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
 // token t < nvalid. Aqm[h][kk] is the unscaled query operand of K-step kk
 // (exact in fp16 and bf16, zero unless kk is the lane's group); scores are
 // scaled by log2(e)/sqrt(D) after the MFMA.
-// lds: this wave's staging area, 32 rows of D halfs with a stride of D + 4
-// (STAGE); without STAGE the V^T operand is gathered from global memory with
-// 16-bit loads (the short unquantised tail of the KIVI cache).
-template <int D, int W, int NHS, bool BF16, bool STAGE, typename RowFn>
+// lds: this wave's staging area for the value rows, 32 rows of D halfs with
+// a stride of D + 4 (so a block takes one trip to memory: keys and values
+// are loaded together, the V^T operand is then read from LDS).
+template <int D, int W, int NHS, bool BF16, typename RowFn>
 __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lane, float qscale,
                                           const uint32_t (&Aqm)[NHS][D / 32][4], DState<D, W, NHS>& st,
                                           uint16_t* lds, uint32_t* lds_p) {
@@ -520,7 +521,7 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
   // ---- stage V rows in LDS (invalid rows as zeros) ----
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  if constexpr (STAGE) {
+  {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;
 #pragma unroll
@@ -534,16 +535,16 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     }
   }
 
-  // ---- key operands: token 16i + n, channels 8(qg*NG + kk) .. + 7 ----
+  // ---- key operands: token 16i + n, channels 32kk + 8qg .. + 7 ----
   uint32_t Bk[2][NG][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = 16 * i + n;
     if (t < nvalid) {
-      const uint16_t* kp = rows.k(t) + 8 * qg * NG;
+      const uint16_t* kp = rows.k(t) + 8 * qg;
 #pragma unroll
       for (int kk = 0; kk < NG; ++kk) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(kp + 8 * kk);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
         Bk[i][kk][0] = v[0];
         Bk[i][kk][1] = v[1];
         Bk[i][kk][2] = v[2];
@@ -585,15 +586,8 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     uint32_t A[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      uint32_t lo, hi;
-      if constexpr (STAGE) {
-        lo = lds[(4 * qg + r) * LSTR + 16 * m + n];
-        hi = lds[(16 + 4 * qg + r) * LSTR + 16 * m + n];
-      } else {
-        const int t0 = 4 * qg + r, t1 = 16 + 4 * qg + r;
-        lo = t0 < nvalid ? rows.v(t0)[16 * m + n] : 0u;
-        hi = t1 < nvalid ? rows.v(t1)[16 * m + n] : 0u;
-      }
+      const uint32_t lo = lds[(4 * qg + r) * LSTR + 16 * m + n];
+      const uint32_t hi = lds[(16 + 4 * qg + r) * LSTR + 16 * m + n];
       A[r] = lo | (hi << 16);
     }
 #pragma unroll
@@ -604,7 +598,9 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
 }
 
 // Unscaled query operands of the row path (W = 1), one per K-step (zero
-// unless the step is the lane's channel group).
+// unless the step is the lane's channel group). K-step kk covers channels
+// 32kk .. 32kk + 31, lane group qg the eight from 32kk + 8qg, so a key load
+// instruction reads 64 contiguous bytes of each of 16 rows.
 template <int D, int NHS, bool BF16>
 __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, int lane,
                                           uint32_t (&Aqm)[NHS][D / 32][4]) {
@@ -618,7 +614,7 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
     uint32_t a[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint16_t* qp = qb + (size_t)(ok ? head : 0) * D + 8 * (qg * NG + j) + 2 * r;
+      const uint16_t* qp = qb + (size_t)(ok ? head : 0) * D + 32 * j + 8 * qg + 2 * r;
       const float lo = ok ? bf16_bits_to_f32(qp[0]) : 0.f, hi = ok ? bf16_bits_to_f32(qp[1]) : 0.f;
       a[r] = pack16<BF16>(lo, hi);
     }
@@ -760,23 +756,24 @@ __device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk,
   if (threadIdx.x == 0) __hip_atomic_store(&P.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge the kWaves wave states of a row-kernel workgroup, store the split's
-// partial and take part in the split merge. lds must hold kWaves * NH * (D + 2) floats; it may alias
-// the row staging area (the leading barrier orders the reuse).
-template <int D, int W, int NHS>
+// Merge the NW wave states of a row-kernel workgroup, store the split's
+// partial and take part in the split merge. lds must hold NW * NH * (D + 2)
+// floats; it may alias the row staging area (the leading barrier orders the
+// reuse).
+template <int D, int NHS, int NW>
 __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int hk, int split, int lane, int wave,
-                                              DState<D, W, NHS>& st, bool has_zero, float* lds) {
-  constexpr int NH = NHS * Geo<D, W>::HS;
+                                              DState<D, 1, NHS>& st, float* lds) {
+  constexpr int NH = NHS * Geo<D, 1>::HS;
   float* lds_o = lds;
-  float* lds_ml = lds + kWaves * NH * D;
+  float* lds_ml = lds + NW * NH * D;
   __syncthreads();
-  dump_state<D, W, NHS>(lane, st, has_zero, lds_o + (size_t)wave * NH * D, lds_ml + wave * NH * 2);
+  dump_state<D, 1, NHS>(lane, st, false, lds_o + (size_t)wave * NH * D, lds_ml + wave * NH * 2);
   __syncthreads();
   merge_waves<D>(
-      P, b, hk, split, kWaves, 64 * kWaves, [&](int w) { return lds_o + (size_t)w * NH * D; },
+      P, b, hk, split, NW, 64 * NW, [&](int w) { return lds_o + (size_t)w * NH * D; },
       [&](int w) { return lds_ml + w * NH * 2; });
   __shared__ int last;
-  finish_unit<D>(P, b, hk, 64 * kWaves, &last);
+  finish_unit<D>(P, b, hk, 64 * NW, &last);
 }
 
 template <int D>
@@ -798,26 +795,34 @@ struct SourceRows {
   __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)pos(t) * D; }
 };
 
+// Waves of a row-kernel workgroup (token drop, dense): as many as the
+// kernel's registers allow on a CU, so one workgroup fills it (a CU running
+// two workgroups serves the older one first), paced like the KIVI body waves.
+template <int D, int NHS>
+struct RowShape {
+  static constexpr int PER_SIMD = D == 128 ? (NHS == 1 ? 3 : NHS <= 3 ? 2 : 1) : (NHS <= 2 ? 4 : NHS == 3 ? 3 : 2);
+  static constexpr int NW = 4 * PER_SIMD;
+};
+
 // LDS of the row kernel: the row staging area (aliased by the wave merge),
 // then the per-wave probability hand-over areas.
-template <int D, int NHS>
+template <int D, int NHS, int NW>
 constexpr size_t draft_stage_bytes() {
   constexpr int NH = NHS * Geo<D, 1>::HS;
-  constexpr size_t part = (size_t)kWaves * NH * (D + 2) * sizeof(float);
-  constexpr size_t rows = (size_t)kWaves * 32 * (D + 4) * sizeof(uint16_t);
+  constexpr size_t part = (size_t)NW * NH * (D + 2) * sizeof(float);
+  constexpr size_t rows = (size_t)NW * 32 * (D + 4) * sizeof(uint16_t);
   return part > rows ? part : rows;
 }
-template <int D, int NHS>
+template <int D, int NHS, int NW>
 constexpr size_t draft_lds_bytes() {
-  return draft_stage_bytes<D, NHS>() + (size_t)kWaves * p_area_words<D, 1, NHS>() * sizeof(uint32_t);
+  return draft_stage_bytes<D, NHS, NW>() + (size_t)NW * p_area_words<D, 1, NHS>() * sizeof(uint32_t);
 }
 
 // ---------------------------------------------------------------- kernels ----
 // This (split, wave)'s share of the 32-token tail blocks when every split
 // also streams body blocks: tail block j goes to split S - 1 - (j mod S)
-// (the last split holds the fewest body blocks), wave (j / S) mod kWaves.
-// BF16 / STAGE as for row_block (fp16 unstaged rows for the KIVI tail).
-template <int D, int NHS, bool BF16, bool STAGE>
+// (the last split holds the fewest body blocks), wave (j / S) mod NW.
+template <int D, int NHS, int NW>
 __device__ __forceinline__ void tail_share(const DraftParams& P, int b, int hk, int split, int wave, int lane,
                                            DState<D, 1, NHS>& st, uint16_t* lds_rows, uint32_t* lds_p) {
   const size_t unit = (size_t)b * P.Hkv + hk;
@@ -825,12 +830,12 @@ __device__ __forceinline__ void tail_share(const DraftParams& P, int b, int hk, 
   int j = wave * P.S + (P.S - 1 - split);
   if (j * 32 >= nt) return;
   uint32_t Aqm[NHS][D / 32][4];
-  row_query<D, NHS, BF16>(P, b, hk, lane, Aqm);
+  row_query<D, NHS, true>(P, b, hk, lane, Aqm);
   const uint16_t* tk = P.tail_k + unit * P.tail_cap * D;
   const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
-  for (; j * 32 < nt; j += P.S * kWaves) {
+  for (; j * 32 < nt; j += P.S * NW) {
     const PlainRows<D> rows{tk + (size_t)j * 32 * D, tv + (size_t)j * 32 * D};
-    row_block<D, 1, NHS, BF16, STAGE>(rows, min(32, nt - j * 32), lane, P.qscale, Aqm, st, lds_rows, lds_p);
+    row_block<D, 1, NHS, true>(rows, min(32, nt - j * 32), lane, P.qscale, Aqm, st, lds_rows, lds_p);
   }
 }
 
@@ -1016,7 +1021,7 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
     const uint16_t* tv = P.tail_v + unit * P.tail_cap * D;
     for (int blk = split; blk * 32 < nt; blk += P.S) {
       const PlainRows<D> rows{tk + (size_t)blk * 32 * D, tv + (size_t)blk * 32 * D};
-      row_block<D, 1, NHS1, false, true>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, tail_rows, lds_p);
+      row_block<D, 1, NHS1, false>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, tail_rows, lds_p);
     }
     dump_state<D, 1, NHS1>(lane, st1, false, tail_merge, tail_merge + NH * D);
   }
@@ -1033,37 +1038,46 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
   finish_unit<D>(P, b, hk, LL::NW * 64 + 64, &last);
 }
 
-// Token-drop (GATHER) and dense draft caches: bf16 rows everywhere.
+// Token-drop (GATHER) and dense draft caches: bf16 rows everywhere. The
+// split's blocks [g0, g1) are dealt to its NW waves in turn (wave w takes
+// g0 + w, g0 + w + NW, ...), then every wave takes its share of the tail.
 template <int D, int NHS, bool GATHER>
-__global__ __launch_bounds__(256) void draft_rows_kernel(const DraftParams P) {
-  __shared__ __attribute__((aligned(16))) char smem[draft_lds_bytes<D, NHS>()];
+__global__ __launch_bounds__((64 * RowShape<D, NHS>::NW), (RowShape<D, NHS>::PER_SIMD)) void draft_rows_kernel(
+    const DraftParams P) {
+  constexpr int NW = RowShape<D, NHS>::NW;
+  __shared__ __attribute__((aligned(16))) char smem[draft_lds_bytes<D, NHS, NW>()];
+  __shared__ __attribute__((aligned(16))) int progress[16];  // blocks each wave has started
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
   uint32_t* lds_p =
-      reinterpret_cast<uint32_t*>(smem + draft_stage_bytes<D, NHS>()) + wave * p_area_words<D, 1, NHS>();
+      reinterpret_cast<uint32_t*>(smem + draft_stage_bytes<D, NHS, NW>()) + wave * p_area_words<D, 1, NHS>();
+  if (threadIdx.x < 16) progress[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t prog_lds = lds_addr(progress);
 
   DState<D, 1, NHS> st;
   st.init();
   uint32_t Aqm[NHS][D / 32][4];
   row_query<D, NHS, true>(P, b, hk, lane, Aqm);
   uint16_t* my_lds = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 4);
-  // every split streams its body blocks, then takes its share of the tail
   {
     const int nb = min(max(P.body_len[b], 0), P.body_cap);
     const int nblk = (nb + 31) / 32;
-    const int b0 = (split * kWaves + wave) * P.bpw;
-    const int b1 = min(b0 + P.bpw, nblk);
+    const int g0 = split * NW * P.bpw;
+    const int g1 = min(g0 + NW * P.bpw, nblk);
     const uint16_t* sk = P.src_k + unit * (size_t)P.src_t_cap * D;
     const uint16_t* sv = P.src_v + unit * (size_t)P.src_t_cap * D;
     const int32_t* kept = GATHER ? P.kept_idx + unit * (size_t)P.body_cap : nullptr;
-    for (int blk = b0; blk < b1; ++blk) {
+    int i = 0;
+    for (int blk = g0 + wave; blk < g1; blk += NW, ++i) {
+      pace_waves<NW>(prog_lds, wave, i);
       const SourceRows<D, GATHER> rows{sk, sv, kept, blk * 32, P.src_t_cap};
-      row_block<D, 1, NHS, true, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+      row_block<D, 1, NHS, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
     }
   }
-  tail_share<D, NHS, true, true>(P, b, hk, split, wave, lane, st, my_lds, lds_p);
-  store_partial<D, 1, NHS>(P, b, hk, split, lane, wave, st, false, reinterpret_cast<float*>(smem));
+  tail_share<D, NHS, NW>(P, b, hk, split, wave, lane, st, my_lds, lds_p);
+  store_partial<D, NHS, NW>(P, b, hk, split, lane, wave, st, reinterpret_cast<float*>(smem));
 }
 
 // Head sets of the row kernel (W = 1).
@@ -1115,7 +1129,9 @@ DraftKernelPick rows_kernel_for(int nhs) {
     case 3: k = draft_rows_kernel<D, 3, GATHER>; break;
     default: k = draft_rows_kernel<D, 4, GATHER>; break;
   }
-  return DraftKernelPick{k, kWaves, 64 * kWaves};
+  constexpr int NW[5] = {0, RowShape<D, 1>::NW, RowShape<D, 2>::NW, RowShape<D, 3>::NW, RowShape<D, 4>::NW};
+  const int nw = NW[nhs < 1 ? 1 : nhs > 4 ? 4 : nhs];
+  return DraftKernelPick{k, nw, 64 * nw};
 }
 
 DraftKernelPick pick_kernel(const vc_attn_shape& sh, const vc_draft_kv& kv) {

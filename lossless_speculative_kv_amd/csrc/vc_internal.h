@@ -134,27 +134,42 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Waves with equal static shares that share a SIMD do not progress equally:
 // the SIMD's issue arbiter prefers the older wave at equal priority, so the
 // younger ones finish long after. Each wave publishes the step it has
-// reached in an LDS array of 8 ints (zeroed before the first call, address
-// lds_base) and runs at priority 1 while it is behind the workgroup's
-// leading wave, else at 0. Only the timing changes, never the work a wave
+// reached in an LDS array of ints at lds_base (8 for up to eight waves, else
+// 16; zeroed before the first call) and runs at priority 1 while it is
+// behind the workgroup's leading wave, else at 0. Only the timing changes, never the work a wave
 // does. The exchange is one asm block that waits for its own LDS accesses
 // (as plain LDS accesses the compiler would order them after every pending
 // direct-to-LDS load), and the priority is chosen inside asm (branches the
 // compiler sees would split a pipelined loop body).
 template <int NW>
 __device__ __forceinline__ void pace_waves(uint32_t lds_base, int wave, int step) {
-  static_assert(NW >= 1 && NW <= 8, "eight progress slots");
-  u32x4 lo, hi;
-  asm volatile(
-      "ds_write_b32 %2, %3\n\t"
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo), "=&v"(hi)
-      : "v"(lds_base + 4 * wave), "v"(step), "v"(lds_base));
+  static_assert(NW >= 1 && NW <= 16, "sixteen progress slots");
+  u32x4 p0, p1, p2, p3;
+  if constexpr (NW <= 8) {
+    asm volatile(
+        "ds_write_b32 %2, %3\n\t"
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p0), "=&v"(p1)
+        : "v"(lds_base + 4 * wave), "v"(step), "v"(lds_base));
+  } else {
+    asm volatile(
+        "ds_write_b32 %4, %5\n\t"
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:16\n\t"
+        "ds_read_b128 %2, %6 offset:32\n\t"
+        "ds_read_b128 %3, %6 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
+        : "v"(lds_base + 4 * wave), "v"(step), "v"(lds_base));
+  }
   int lead = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) lead = max(lead, (int)(w < 4 ? lo[w] : hi[w - 4]));
+  for (int w = 0; w < NW; ++w) {
+    const u32x4& q = w < 4 ? p0 : w < 8 ? p1 : w < 12 ? p2 : p3;
+    lead = max(lead, (int)q[w & 3]);
+  }
   const int lag = __builtin_amdgcn_readfirstlane(lead - step);
   asm volatile(
       "s_cmp_gt_i32 %0, 0\n\t"

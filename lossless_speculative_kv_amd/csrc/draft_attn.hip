@@ -300,15 +300,16 @@ __device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t r, char* dst, i
   constexpr int N1K = BYTES / 1024, N256 = (BYTES % 1024) / 256, R128 = BYTES % 256;
 #pragma unroll
   for (int i = 0; i < N1K; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, lane * 16, soff + i * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, lane * 16, soff + i * 1024, 0,
+                                             kStreamPolicy);
 #pragma unroll
   for (int i = 0; i < N256; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + N1K * 1024 + i * 256), 4, lane * 4,
-                                             soff + N1K * 1024 + i * 256, 0, 0);
+                                             soff + N1K * 1024 + i * 256, 0, kStreamPolicy);
   if constexpr (R128 != 0) {
     if (lane < 32)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + N1K * 1024 + N256 * 256), 4, lane * 4,
-                                               soff + N1K * 1024 + N256 * 256, 0, 0);
+                                               soff + N1K * 1024 + N256 * 256, 0, kStreamPolicy);
   }
 }
 
@@ -528,7 +529,7 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     for (int u = 0; u < 32 / RPI; ++u) {
       const int t = lane / CPR + RPI * u, c = lane % CPR;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < nvalid) v = *reinterpret_cast<const u32x4*>(rows.v(t) + 8 * c);
+      if (t < nvalid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows.v(t) + 8 * c));
       uint32_t* d = reinterpret_cast<uint32_t*>(lds + t * LSTR + 8 * c);
       *reinterpret_cast<u32x2*>(d) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(d + 2) = u32x2{v[2], v[3]};
@@ -544,7 +545,7 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
       const uint16_t* kp = rows.k(t) + 8 * qg;
 #pragma unroll
       for (int kk = 0; kk < NG; ++kk) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk));
         Bk[i][kk][0] = v[0];
         Bk[i][kk][1] = v[1];
         Bk[i][kk][2] = v[2];

@@ -109,7 +109,7 @@ __device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int t
   for (int c = 0; c < T::CHUNKS; ++c) {
     const int row = T::RPC * c + rl;
     const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, kStreamPolicy);
   }
 }
 

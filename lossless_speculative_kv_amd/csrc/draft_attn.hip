@@ -391,12 +391,59 @@ struct KiviQuery {
   float qscale;  // log2(e)/sqrt(D), applied to the fp32 scores
 };
 
+// Raw bf16 bits of the query values a lane needs (pairs per word, lowest
+// channel in the low half), loaded as whole 16-byte runs from a valid head
+// (head 0 stands in for padding heads, whose values are zeroed on
+// conversion). Unconditional vector loads leave the wave with one trip to
+// memory; loads under a per-lane condition are issued and waited for one by
+// one.
 template <int D, int W>
-__device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, int lane, KiviQuery<D, W>& Q) {
+struct KiviQueryRaw {
+  static constexpr int CPL = Geo<D, W>::CPL, HPL = Geo<D, W>::HPL;
+  uint32_t qp[W][4];          // channels 8(q*NG + W*jr + w) + 0..7 of head hl
+  uint32_t qz[HPL][CPL / 2];  // channels CPL*t + 0..CPL-1 of head HPL*q + u
+};
+
+template <int N>
+__device__ __forceinline__ void global_words(const uint16_t* p, uint32_t* w) {
+  if constexpr (N == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+    static_assert(N == 4, "16-byte runs");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
+  }
+}
+
+__device__ __forceinline__ uint32_t half_of(const uint32_t* w, int i) { return (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu; }
+
+template <int D, int W>
+__device__ __forceinline__ void kivi_query_load(const DraftParams& P, int b, int hk, int lane, KiviQueryRaw<D, W>& R) {
   using G = Geo<D, W>;
   constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, CPL = G::CPL;
   const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
   const uint16_t* qb = P.q + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
+  const int hlc = hl < P.g ? hl : 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) global_words<4>(qb + (size_t)hlc * D + 8 * (qg * NG + W * jr + w), R.qp[w]);
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) {
+    const int hb = HPL * qg + u;
+    global_words<CPL / 2>(qb + (size_t)(hb < P.g ? hb : 0) * D + CPL * n, R.qz[u]);
+  }
+}
+
+template <int D, int W>
+__device__ __forceinline__ void kivi_query_finish(const DraftParams& P, int lane, const KiviQueryRaw<D, W>& R,
+                                                  KiviQuery<D, W>& Q) {
+  using G = Geo<D, W>;
+  constexpr int NR = G::NR, HPL = G::HPL, CPL = G::CPL;
+  const int n = lane & 15, qg = lane >> 4, hl = n / NR;
   const bool ok = hl < P.g;
 #pragma unroll
   for (int w = 0; w < W; ++w)
@@ -404,8 +451,7 @@ __device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, 
     for (int r = 0; r < 4; ++r) {
       float x[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        x[e] = ok ? bf16_bits_to_f32(qb[(size_t)hl * D + 8 * (qg * NG + W * jr + w) + kperm(2 * r + e)]) : 0.f;
+      for (int e = 0; e < 2; ++e) x[e] = ok ? bf16_bits_to_f32(half_of(R.qp[w], kperm(2 * r + e))) : 0.f;
       // unscaled: a bf16 query value is an fp16 value (above 2^-14), so the
       // only rounding left before the MFMA is that of q * key scale
       Q.qp[w][r] = pack_f16(x[0], x[1]);
@@ -413,10 +459,9 @@ __device__ __forceinline__ void kivi_query(const DraftParams& P, int b, int hk, 
   Q.qscale = P.qscale;
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
-    const int hb = HPL * qg + u;
-    const bool okb = hb < P.g;
+    const bool okb = HPL * qg + u < P.g;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(qb[(size_t)hb * D + CPL * n + e]) * P.qscale : 0.f;
+    for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(half_of(R.qz[u], e)) * P.qscale : 0.f;
   }
 }
 
@@ -608,15 +653,22 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
   constexpr int NG = Geo<D, 1>::NG, HS = Geo<D, 1>::HS;
   const int n = lane & 15, qg = lane >> 4, j = n % NG, hl = n / NG;
   const uint16_t* qb = P.q + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
+  // every head set's run is loaded before any is used (one trip to memory);
+  // padding heads read head 0 and are zeroed below
+  uint32_t raw[NHS][4];
 #pragma unroll
   for (int h = 0; h < NHS; ++h) {
     const int head = h * HS + hl;
-    const bool ok = head < P.g;
+    global_words<4>(qb + (size_t)(head < P.g ? head : 0) * D + 32 * j + 8 * qg, raw[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < NHS; ++h) {
+    const bool ok = h * HS + hl < P.g;
     uint32_t a[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint16_t* qp = qb + (size_t)(ok ? head : 0) * D + 32 * j + 8 * qg + 2 * r;
-      const float lo = ok ? bf16_bits_to_f32(qp[0]) : 0.f, hi = ok ? bf16_bits_to_f32(qp[1]) : 0.f;
+      const float lo = ok ? bf16_bits_to_f32(raw[h][r] & 0xFFFFu) : 0.f;
+      const float hi = ok ? bf16_bits_to_f32(raw[h][r] >> 16) : 0.f;
       a[r] = pack16<BF16>(lo, hi);
     }
 #pragma unroll
@@ -918,8 +970,11 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
     // slots first, so the body waves end together
     const uint32_t prog_lds = lds_addr(progress);
     auto pace = [&](int i) { pace_waves<NW>(prog_lds, wave, i); };
+    // the query loads go out first; they are converted once the ring's
+    // first loads are in flight
+    KiviQueryRaw<D, W> qraw;
+    kivi_query_load<D, W>(P, b, hk, lane, qraw);
     KiviQuery<D, W> Q;
-    kivi_query<D, W>(P, b, hk, lane, Q);
     const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;
     // the workgroup's blocks [g0, g1) are dealt to its body waves in turn
     // (wave w takes g0 + w, g0 + w + NW, ...), so the waves of a workgroup
@@ -964,6 +1019,7 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
         issue_block<D, BITS>(w3, res, gblk(min(b0 + 3, last)), lane);
         issue_block<D, BITS>(w4, res, gblk(min(b0 + 4, last)), lane);
+        kivi_query_finish<D, W>(P, lane, qraw, Q);
         wait_vm<3 * BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
         kivi_read<D, BITS, W>(rb, w1, lane);
@@ -990,6 +1046,7 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
           wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
           kivi_read<D, BITS, W>(nxt, next_stage, lane);
         };
+        kivi_query_finish<D, W>(P, lane, qraw, Q);
         wait_vm<BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
         for (int blk = b0;; blk += 6) {

@@ -2,6 +2,7 @@
 // Nothing here allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -110,12 +111,14 @@ vc_status check_draft_kv(const vc_attn_shape* sh, const vc_draft_kv* kv) {
   VC_REQ(kv->tail_len, 4, "tail_len");
   VC_REQ(kv->tail_k, 16, "tail_k");
   VC_REQ(kv->tail_v, 16, "tail_v");
-  (void)sh;
   switch (kv->kind) {
     case VC_DRAFT_KIVI:
       if (kv->bits != 2 && kv->bits != 4) return fail(VC_ERR_UNSUPPORTED, "KIVI bits %d (supported: 2, 4)", kv->bits);
       if (kv->body_cap % 32) return fail(VC_ERR_INVALID_ARG, "KIVI body_cap %d must be a multiple of 32", kv->body_cap);
       VC_REQ(kv->kivi_blocks, 256, "kivi_blocks");
+      // one (sequence, KV head)'s records are addressed with 32-bit byte offsets
+      if (sh != nullptr && (int64_t)(kv->body_cap / 32) * 8 * sh->head_dim * (kv->bits + 1) > INT32_MAX)
+        return fail(VC_ERR_UNSUPPORTED, "KIVI body_cap %d: one KV head's records exceed 2^31 bytes", kv->body_cap);
       break;
     case VC_DRAFT_TOKDROP:
       VC_REQ(kv->kept_idx, 4, "kept_idx");

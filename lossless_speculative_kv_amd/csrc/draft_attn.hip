@@ -970,40 +970,52 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
     // slots first, so the body waves end together
     const uint32_t prog_lds = lds_addr(progress);
     auto pace = [&](int i) { pace_waves<NW>(prog_lds, wave, i); };
-    // the query loads go out first; they are converted once the ring's
-    // first loads are in flight
+    // the body length, then the query, go out first; the ring starts before
+    // either has arrived
+    // (a scalar load: its counter is not the one the ring's loads wait on)
+    const int blen = ((const __attribute__((address_space(4))) int*)(P.body_len))[b];
     KiviQueryRaw<D, W> qraw;
     kivi_query_load<D, W>(P, b, hk, lane, qraw);
     KiviQuery<D, W> Q;
-    const int nblk = min(max(P.body_len[b], 0), P.body_cap) / 32;
     // the workgroup's blocks [g0, g1) are dealt to its body waves in turn
     // (wave w takes g0 + w, g0 + w + NW, ...), so the waves of a workgroup
     // read neighbouring records; i counts this wave's blocks
+    const int nbc = P.body_cap / 32;
     const int g0 = split * NW * P.bpw;
-    const int g1 = min(g0 + NW * P.bpw, nblk);
-    const int cnt = max(0, (g1 - g0 - wave + NW - 1) / NW);
     auto gblk = [&](int i) { return g0 + wave + NW * i; };
-    const int b0 = 0, b1 = cnt;
-    if (b0 < b1) {
-      const size_t nbc = (size_t)(P.body_cap / 32);
-      KiviRes res;
-      res.blocks = make_rsrc(P.kivi_blocks + unit * nbc * BL::BYTES, nbc * BL::BYTES);
-      constexpr int NS = LL::NS;
-      char* const w0 = rs0 + wave * BL::BYTES;
-      char* const w1 = rs1 + wave * BL::BYTES;
-      char* const w2 = rs2 + wave * BL::BYTES;
-      char* const w3 = rs3 + (NS > 3 ? wave * BL::BYTES : 0);
-      char* const w4 = rs4 + (NS > 3 ? wave * BL::BYTES : 0);
-      char* const w5 = rs5 + (NS > 3 ? wave * BL::BYTES : 0);
+    auto count = [&](int nb) { return max(0, (min(g0 + NW * P.bpw, nb) - g0 - wave + NW - 1) / NW); };
+    // the first NS - 1 loads are issued for the range a full body would
+    // give (cnt <= cnt_cap). They agree with the real range up to the wave's
+    // last block; a stage past it is never computed on, and every load stays
+    // inside the unit's records.
+    const int cnt_cap = count(nbc);
+    KiviRes res;
+    res.blocks = make_rsrc(P.kivi_blocks + unit * (size_t)nbc * BL::BYTES, (size_t)nbc * BL::BYTES);
+    constexpr int NS = LL::NS;
+    char* const w0 = rs0 + wave * BL::BYTES;
+    char* const w1 = rs1 + wave * BL::BYTES;
+    char* const w2 = rs2 + wave * BL::BYTES;
+    char* const w3 = rs3 + (NS > 3 ? wave * BL::BYTES : 0);
+    char* const w4 = rs4 + (NS > 3 ? wave * BL::BYTES : 0);
+    char* const w5 = rs5 + (NS > 3 ? wave * BL::BYTES : 0);
+    if (cnt_cap > 0) {
+      const int last_cap = cnt_cap - 1;
+      issue_block<D, BITS>(w0, res, gblk(0), lane);
+      issue_block<D, BITS>(w1, res, gblk(min(1, last_cap)), lane);
+      if constexpr (NS == 6) {
+        issue_block<D, BITS>(w2, res, gblk(min(2, last_cap)), lane);
+        issue_block<D, BITS>(w3, res, gblk(min(3, last_cap)), lane);
+        issue_block<D, BITS>(w4, res, gblk(min(4, last_cap)), lane);
+      }
+      const int cnt = count(min(max(blen, 0), P.body_cap) / 32);
+      {
       // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of a
       // later block move from LDS to registers at the end of a step, so their
       // latency overlaps the step's last MFMAs. Past the wave's last block
       // the last one is loaded again (into a stage that is not read), which
       // keeps every wait count constant.
-      const int last = b1 - 1;
+      const int b0 = 0, last = max(cnt - 1, 0);
       KiviRaw<D, BITS, W> ra, rb;
-      issue_block<D, BITS>(w0, res, gblk(b0), lane);
-      issue_block<D, BITS>(w1, res, gblk(min(b0 + 1, last)), lane);
       if constexpr (NS == 6) {
         // three register sets: the operands of block i + 2 are read while
         // block i is computed, so the LDS reads have a whole step to land
@@ -1016,9 +1028,6 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
           wait_vm<3 * BL::NI>();  // block i + 2 has landed
           kivi_read<D, BITS, W>(nxt2, stage2, lane);
         };
-        issue_block<D, BITS>(w2, res, gblk(min(b0 + 2, last)), lane);
-        issue_block<D, BITS>(w3, res, gblk(min(b0 + 3, last)), lane);
-        issue_block<D, BITS>(w4, res, gblk(min(b0 + 4, last)), lane);
         kivi_query_finish<D, W>(P, lane, qraw, Q);
         wait_vm<3 * BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
@@ -1064,7 +1073,12 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
           if (blk + 6 > last) break;
         }
       }
+      }
+      // every ring load has landed before the ring's memory is reused
       wait_vm<0>();
+      // a wave whose real range is empty (a body shorter than its
+      // capacity) computed its first speculative block: drop it
+      if (cnt == 0) st.init();
     }
   } else {
     // the tail wave: fp16 rows with the values staged in LDS (so a block

@@ -122,6 +122,7 @@ KIVI_CASES = [
     (2, 40, 8, 128, 2, [1536, 4096], [100, 1], False),   # Qwen-32B layer shape, g = 5
     (1, 64, 8, 128, 2, [4096], [160], False),            # Llama-70B layer shape, g = 8
     (2, 8, 2, 128, 4, [0, 64], [5, 32], False),          # empty body; tail only
+    (2, 32, 8, 128, 2, [0, 512], [40, 3], False),        # empty body on the six-stage ring (g = 4, 2-bit)
     (1, 4, 2, 64, 2, [96], [1], False),                  # g = 2, single tail token
     (1, 32, 2, 64, 2, [640], [40], False),               # g = 16 (rows of two channel groups at D = 64)
     (1, 64, 4, 128, 2, [1024], [50], False),             # g = 16 (rows of four channel groups)

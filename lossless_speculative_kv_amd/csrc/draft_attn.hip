@@ -549,8 +549,9 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
 
 // ------------------------------------------------ unquantised row block ----
 // A 32-token block of 16-bit rows (fp16 KIVI tail, or bf16 rows for token
-// drop / dense), W = 1 rows. rows.k(t) / rows.v(t) give the row pointers of
-// token t < nvalid. Aqm[h][kk] is the unscaled query operand of K-step kk
+// drop / dense), W = 1 rows. rows.k(t, i) / rows.v(t, u) give the row
+// pointers of token t < nvalid, which is key row 16i + n or value row
+// lane / (D/8) + (512/D) u of the lane. Aqm[h][kk] is the unscaled query operand of K-step kk
 // (exact in fp16 and bf16, zero unless kk is the lane's group); scores are
 // scaled by log2(e)/sqrt(D) after the MFMA.
 // lds: this wave's staging area for the value rows, 32 rows of D halfs with
@@ -572,9 +573,11 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     constexpr int RPI = 64 / CPR;
 #pragma unroll
     for (int u = 0; u < 32 / RPI; ++u) {
+      // every lane loads (a row past the block's end reads its last row and
+      // is zeroed): a load under a per-lane condition waits on its own
       const int t = lane / CPR + RPI * u, c = lane % CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < nvalid) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows.v(t) + 8 * c));
+      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows.v(min(t, nvalid - 1), u) + 8 * c));
+      if (t >= nvalid) v = u32x4{0u, 0u, 0u, 0u};
       uint32_t* d = reinterpret_cast<uint32_t*>(lds + t * LSTR + 8 * c);
       *reinterpret_cast<u32x2*>(d) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(d + 2) = u32x2{v[2], v[3]};
@@ -586,19 +589,15 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = 16 * i + n;
-    if (t < nvalid) {
-      const uint16_t* kp = rows.k(t) + 8 * qg;
+    const uint16_t* kp = rows.k(min(t, nvalid - 1), i) + 8 * qg;
+    const bool ok = t < nvalid;
 #pragma unroll
-      for (int kk = 0; kk < NG; ++kk) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk));
-        Bk[i][kk][0] = v[0];
-        Bk[i][kk][1] = v[1];
-        Bk[i][kk][2] = v[2];
-        Bk[i][kk][3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NG; ++kk) Bk[i][kk][0] = Bk[i][kk][1] = Bk[i][kk][2] = Bk[i][kk][3] = 0u;
+    for (int kk = 0; kk < NG; ++kk) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk));
+      Bk[i][kk][0] = ok ? v[0] : 0u;
+      Bk[i][kk][1] = ok ? v[1] : 0u;
+      Bk[i][kk][2] = ok ? v[2] : 0u;
+      Bk[i][kk][3] = ok ? v[3] : 0u;
     }
   }
 
@@ -832,20 +831,34 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
 template <int D>
 struct PlainRows {
   const uint16_t *kb, *vb;
-  __device__ __forceinline__ const uint16_t* k(int t) const { return kb + (size_t)t * D; }
-  __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)t * D; }
+  __device__ __forceinline__ const uint16_t* k(int t, int) const { return kb + (size_t)t * D; }
+  __device__ __forceinline__ const uint16_t* v(int t, int) const { return vb + (size_t)t * D; }
 };
-template <int D, bool GATHER>
-struct SourceRows {
+
+// Gathered rows of one block: the kept positions of the rows a lane reads
+// (value rows lane / CPR + RPI u, key rows 16 i + n; a row past the block's
+// end takes the last row's position), loaded into registers one block
+// ahead, so a block's rows need only their own trip to memory.
+template <int D>
+struct KeptRows {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, NV = 32 / RPI;
   const uint16_t *kb, *vb;
-  const int32_t* idx;
-  int t0, cap;
-  __device__ __forceinline__ int pos(int t) const {
-    if constexpr (GATHER) return min((int)((unsigned)idx[t0 + t]), cap - 1);
-    else return t0 + t;
+  int pv[NV], pk[2];
+  // positions of block rows [t0, t0 + nvalid) of the unit's kept list;
+  // nvalid >= 1, and every position is clamped into the source rows
+  __device__ __forceinline__ void load(const int32_t* kept, int t0, int nvalid, int cap, int lane) {
+    int raw_v[NV], raw_k[2];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) raw_v[u] = kept[t0 + min(lane / CPR + RPI * u, nvalid - 1)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) raw_k[i] = kept[t0 + min(16 * i + (lane & 15), nvalid - 1)];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) pv[u] = min((int)((unsigned)raw_v[u]), cap - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pk[i] = min((int)((unsigned)raw_k[i]), cap - 1);
   }
-  __device__ __forceinline__ const uint16_t* k(int t) const { return kb + (size_t)pos(t) * D; }
-  __device__ __forceinline__ const uint16_t* v(int t) const { return vb + (size_t)pos(t) * D; }
+  __device__ __forceinline__ const uint16_t* k(int, int i) const { return kb + (size_t)pk[i] * D; }
+  __device__ __forceinline__ const uint16_t* v(int, int u) const { return vb + (size_t)pv[u] * D; }
 };
 
 // Waves of a row-kernel workgroup (token drop, dense): as many as the
@@ -1140,12 +1153,25 @@ __global__ __launch_bounds__((64 * RowShape<D, NHS>::NW), (RowShape<D, NHS>::PER
     const int g1 = min(g0 + NW * P.bpw, nblk);
     const uint16_t* sk = P.src_k + unit * (size_t)P.src_t_cap * D;
     const uint16_t* sv = P.src_v + unit * (size_t)P.src_t_cap * D;
-    const int32_t* kept = GATHER ? P.kept_idx + unit * (size_t)P.body_cap : nullptr;
     int i = 0;
-    for (int blk = g0 + wave; blk < g1; blk += NW, ++i) {
-      pace_waves<NW>(prog_lds, wave, i);
-      const SourceRows<D, GATHER> rows{sk, sv, kept, blk * 32, P.src_t_cap};
-      row_block<D, 1, NHS, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+    if constexpr (GATHER) {
+      const int32_t* kept = P.kept_idx + unit * (size_t)P.body_cap;
+      KeptRows<D> cur{sk, sv}, nxt{sk, sv};
+      if (g0 + wave < g1) cur.load(kept, (g0 + wave) * 32, min(32, nb - (g0 + wave) * 32), P.src_t_cap, lane);
+      for (int blk = g0 + wave; blk < g1; blk += NW, ++i) {
+        // the next block's positions (this block's again after the last)
+        const int nb2 = min(blk + NW, g1 - 1);
+        nxt.load(kept, nb2 * 32, min(32, nb - nb2 * 32), P.src_t_cap, lane);
+        pace_waves<NW>(prog_lds, wave, i);
+        row_block<D, 1, NHS, true>(cur, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+        cur = nxt;
+      }
+    } else {
+      for (int blk = g0 + wave; blk < g1; blk += NW, ++i) {
+        pace_waves<NW>(prog_lds, wave, i);
+        const PlainRows<D> rows{sk + (size_t)blk * 32 * D, sv + (size_t)blk * 32 * D};
+        row_block<D, 1, NHS, true>(rows, min(32, nb - blk * 32), lane, P.qscale, Aqm, st, my_lds, lds_p);
+      }
     }
   }
   tail_share<D, NHS, NW>(P, b, hk, split, wave, lane, st, my_lds, lds_p);

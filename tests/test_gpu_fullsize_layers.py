@@ -1,0 +1,107 @@
+"""Draft parity at full size for the other layer shapes, driven through the
+bench's engine, split plans and kernels (one draft step each), with sampled
+outputs computed one by one by the oracle:
+
+* Mistral-24B layer (B = 4, 32 q / 8 KV heads, context 131072, token drop
+  keeping 25%): the kept positions of sampled KV heads bit for bit against the
+  oracle dropper on the GPU's own scores, then draft attention of their query
+  heads over the gathered rows and the bf16 tail;
+* Qwen-32B layer (B = 16, 40 q / 8 KV heads, context 65536, KIVI-2, g = 5):
+  body records byte for byte against the oracle quantiser on the GPU's own
+  full-cache rows, then draft attention over the dequantised body and fp16
+  tail;
+* Llama-70B layer with a 1M-token context (B = 1, 64 q / 8 KV heads, KIVI-2,
+  g = 8, full cache in pinned host memory): the same for one KV head.
+
+Tolerances as in the kernel tests: attention max |d| <= 1e-2 and rel-L2 <=
+2e-3; kept positions and records bit-exact."""
+import gc
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from tests.gpu_util import assert_attention_close, log  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def build(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_speculative_kv_amd import configs, engine
+    cfg = configs.BY_NAME[name]
+    log(f"full size: building the {name} engine")
+    e = engine.Engine(cfg, rounds_cap=1)
+    e.begin_round()
+    e.draft_step(0)
+    torch.cuda.synchronize()
+    return e
+
+
+def release(e):
+    del e
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def check_kivi_unit(eng, b, hk):
+    c = eng.cfg
+    g = c.n_q_heads // c.n_kv_heads
+    nb = int(eng.body_len[b])
+    nt = int(eng.tail_len[b])
+    log(f"full size draft ({c.name}): sequence {b} KV head {hk}, body {nb}, tail {nt}")
+    rec = eng.kivi_blocks[b, hk, :nb // 32].cpu().numpy()
+    K = f64(eng.full_k[b, hk, :nb])
+    V = f64(eng.full_v[b, hk, :nb])
+    kc, ks, kz = oracle.quantize_keys(K, c.bits)
+    vc, vs, vz = oracle.quantize_values(V, c.bits)
+    assert np.array_equal(rec, oracle.pack_blocks(kc, ks, kz, vc, vs, vz, c.bits)), f"records of ({b}, {hk})"
+    del K, V, rec
+    Kv = np.concatenate([oracle.dequantize_keys(kc, ks, kz), f64(eng.tail_k[b, hk, :nt])])
+    Vv = np.concatenate([oracle.dequantize_values(vc, vs, vz), f64(eng.tail_v[b, hk, :nt])])
+    q = f64(eng.q_draft[b, hk * g:(hk + 1) * g])
+    ref = np.stack([oracle.attend(q[i], Kv, Vv) for i in range(g)])
+    got = eng.o_draft[b, hk * g:(hk + 1) * g].cpu().numpy()
+    mad, rl2 = assert_attention_close(got, ref, f"draft unit ({b}, {hk})")
+    log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
+
+
+def test_mistral_tokdrop_draft():
+    eng = build("mistral-24b-layer")
+    c = eng.cfg
+    g = c.n_q_heads // c.n_kv_heads
+    out = eng.o_draft.cpu().numpy()
+    for b, hk in [(0, 0), (c.batch - 1, c.n_kv_heads - 1), (2, 3)]:
+        kept = eng.kept[b, hk, :eng.n_keep].cpu().numpy()
+        want = oracle.select_kept(eng.scores[b, hk].cpu().numpy(), c.keep)
+        assert np.array_equal(kept, want), f"kept positions of ({b}, {hk})"
+        nt = int(eng.tail_len[b])
+        log(f"full size draft ({c.name}): sequence {b} KV head {hk}, kept {len(kept)}, tail {nt}")
+        K = np.concatenate([f64(eng.full_k[b, hk])[kept], f64(eng.tail_k[b, hk, :nt])])
+        V = np.concatenate([f64(eng.full_v[b, hk])[kept], f64(eng.tail_v[b, hk, :nt])])
+        q = f64(eng.q_draft[b, hk * g:(hk + 1) * g])
+        ref = np.stack([oracle.attend(q[i], K, V) for i in range(g)])
+        mad, rl2 = assert_attention_close(out[b, hk * g:(hk + 1) * g], ref, f"draft unit ({b}, {hk})")
+        log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
+    release(eng)
+
+
+def test_qwen_kivi_draft():
+    eng = build("qwen-32b-layer")
+    c = eng.cfg
+    for b, hk in [(0, 0), (c.batch - 1, c.n_kv_heads - 1), (9, 4)]:
+        check_kivi_unit(eng, b, hk)
+    release(eng)
+
+
+def test_llama70b_1m_kivi_draft():
+    eng = build("llama-70b-layer-1m")
+    check_kivi_unit(eng, 0, eng.cfg.n_kv_heads - 1)
+    release(eng)

@@ -430,11 +430,10 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   }
 }
 
-// Fold this call's splits (in order, eight at a time: the loads of a batch
+// Fold this call's splits (in order, kBatch at a time: the loads of a batch
 // are issued together) into the running state; on END write out.
-template <int D>
+template <int D, int kBatch>
 __global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
-  constexpr int kBatch = 8;
   const int c = threadIdx.x, row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * P.Hkv + hk;
   const size_t rr = unit * P.R + row;
@@ -591,8 +590,14 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   if (st != VC_OK) return st;
   const dim3 mgrid((unsigned)R, sh.n_kv_heads, sh.batch);
   hipEvent_t mstop = main_only ? nullptr : tm.stop;
-  if (sh.head_dim == 128) launch_ev(verify_merge_kernel<128>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
-  else launch_ev(verify_merge_kernel<64>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
+  // batches of four when the splits fit one (no duplicate loads), else eight
+  if (sh.head_dim == 128) {
+    if (P.S <= 4) launch_ev(verify_merge_kernel<128, 4>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
+    else launch_ev(verify_merge_kernel<128, 8>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
+  } else {
+    if (P.S <= 4) launch_ev(verify_merge_kernel<64, 4>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
+    else launch_ev(verify_merge_kernel<64, 8>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
+  }
   return check_launch("verify merge");
 }
 

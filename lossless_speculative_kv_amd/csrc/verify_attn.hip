@@ -431,48 +431,64 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
 }
 
 // Fold this call's splits (in order, kBatch at a time: the loads of a batch
-// are issued together) into the running state; on END write out.
+// are issued together, every one from a valid split, duplicates masked after
+// the load) into the running state; on END write out. A thread takes four
+// channels of one row (16-byte loads and stores), a workgroup
+// kMergeThreads / (D / 4) rows.
+constexpr int kMergeThreads = 256;
+
 template <int D, int kBatch>
-__global__ __launch_bounds__(D) void verify_merge_kernel(const VerifyParams P) {
-  const int c = threadIdx.x, row = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const VerifyParams P) {
+  constexpr int C4 = D / 4, RPW = kMergeThreads / C4;
+  const int c = 4 * (threadIdx.x % C4), row = blockIdx.x * RPW + threadIdx.x / C4, hk = blockIdx.y, b = blockIdx.z;
+  if (row >= P.R) return;
   const size_t unit = (size_t)b * P.Hkv + hk;
   const size_t rr = unit * P.R + row;
-  float M = kNegInf, L = 0.f, O = 0.f;
+  float M = kNegInf, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
   if (!(P.flags & VC_VERIFY_BEGIN)) {
     M = P.run_ml[rr * 2];
     L = P.run_ml[rr * 2 + 1];
-    O = P.run_o[rr * D + c];
+    O = *reinterpret_cast<const f32x4*>(P.run_o + rr * D + c);
   }
   for (int s0 = 0; s0 < P.S; s0 += kBatch) {
-    float ms[kBatch], ls[kBatch], os[kBatch];
+    float ms[kBatch], ls[kBatch];
+    f32x4 os[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const size_t pr = (unit * P.S + min(s0 + i, P.S - 1)) * P.R + row;
-      ms[i] = s0 + i < P.S ? P.part_ml[pr * 2] : kNegInf;
+      ms[i] = P.part_ml[pr * 2];
       ls[i] = P.part_ml[pr * 2 + 1];
-      os[i] = P.part_o[pr * D + c];
+      os[i] = *reinterpret_cast<const f32x4*>(P.part_o + pr * D + c);
     }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) ms[i] = s0 + i < P.S ? ms[i] : kNegInf;
     float mx = M;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
     if (mx == kNegInf) continue;  // nothing visible so far
     const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
-    O *= a;
     L *= a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[e] *= a;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const bool ok = ms[i] != kNegInf;
       const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
-      O = ok ? fmaf(os[i], w, O) : O;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[e] = ok ? fmaf(os[i][e], w, O[e]) : O[e];
       L = ok ? fmaf(ls[i], w, L) : L;
     }
     M = mx;
   }
   if (P.flags & VC_VERIFY_END) {
     const int j = row / P.g, hl = row % P.g;
-    P.out[(((size_t)j * P.B + b) * P.Hq + (size_t)hk * P.g + hl) * D + c] = (L > 0.f) ? O / L : 0.f;
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (L > 0.f) ? O[e] / L : 0.f;
+    *reinterpret_cast<f32x4*>(P.out + (((size_t)j * P.B + b) * P.Hq + (size_t)hk * P.g + hl) * D + c) = r;
   } else {
-    P.run_o[rr * D + c] = O;
+    *reinterpret_cast<f32x4*>(P.run_o + rr * D + c) = O;
     if (c == 0) {
       P.run_ml[rr * 2] = M;
       P.run_ml[rr * 2 + 1] = L;
@@ -588,15 +604,17 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   else launch_verify<64>(P, plan.rt, plan.pair, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
   vc_status st = check_launch("verify attention");
   if (st != VC_OK) return st;
-  const dim3 mgrid((unsigned)R, sh.n_kv_heads, sh.batch);
   hipEvent_t mstop = main_only ? nullptr : tm.stop;
+  const dim3 mblock(kMergeThreads);
   // batches of four when the splits fit one (no duplicate loads), else eight
   if (sh.head_dim == 128) {
-    if (P.S <= 4) launch_ev(verify_merge_kernel<128, 4>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
-    else launch_ev(verify_merge_kernel<128, 8>, mgrid, dim3(128), 0, stream, nullptr, mstop, P);
+    const dim3 mgrid((unsigned)((R + kMergeThreads / 32 - 1) / (kMergeThreads / 32)), sh.n_kv_heads, sh.batch);
+    if (P.S <= 4) launch_ev(verify_merge_kernel<128, 4>, mgrid, mblock, 0, stream, nullptr, mstop, P);
+    else launch_ev(verify_merge_kernel<128, 8>, mgrid, mblock, 0, stream, nullptr, mstop, P);
   } else {
-    if (P.S <= 4) launch_ev(verify_merge_kernel<64, 4>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
-    else launch_ev(verify_merge_kernel<64, 8>, mgrid, dim3(64), 0, stream, nullptr, mstop, P);
+    const dim3 mgrid((unsigned)((R + kMergeThreads / 16 - 1) / (kMergeThreads / 16)), sh.n_kv_heads, sh.batch);
+    if (P.S <= 4) launch_ev(verify_merge_kernel<64, 4>, mgrid, mblock, 0, stream, nullptr, mstop, P);
+    else launch_ev(verify_merge_kernel<64, 8>, mgrid, mblock, 0, stream, nullptr, mstop, P);
   }
   return check_launch("verify merge");
 }

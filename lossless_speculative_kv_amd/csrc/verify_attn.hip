@@ -516,9 +516,11 @@ struct VerifyPlan {
   bool pair;
 };
 
-// Row tiling: two row tiles per consumer wave up to 12 tiles, else three (at
-// most 6 consumer waves plus the 2 producers, so 2 waves per SIMD and the
-// whole register file for the row tiles' accumulators). Context split of a call:
+// Row tiling: wave pairs with two row tiles per wave up to 6 tiles and three
+// up to 9; beyond, one wave per group of three row tiles (at most 6 consumer
+// waves plus the 2 producers, so 2 waves per SIMD and the whole register file
+// for the row tiles' accumulators). Two tiles per wave there (more consumer
+// waves) measured slower: every consumer reads each whole K/V tile from LDS. Context split of a call:
 // about 256 workgroups (one per CU), whole 32-token tiles, at least 8 tiles
 // per split; the draft block rides on the last split. The split count never
 // decreases with chunk_tokens, so a workspace sized for the largest chunk

@@ -96,7 +96,7 @@ __device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_re
 // swizzle puts there. Every operand that is wave-uniform is made visibly so
 // (the buffer resource must sit in scalar registers).
 template <int D>
-__device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int tile, int lane, int half) {
+__device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int tile, int lane, int half, int c) {
   using T = Tile<D>;
   const uint64_t a = reinterpret_cast<uint64_t>(half ? sg.v : sg.k);
   const uint64_t au = ((uint64_t)uni((uint32_t)(a >> 32)) << 32) | uni((uint32_t)a);
@@ -105,12 +105,45 @@ __device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int t
   const int rb = (int)uni((uint32_t)sg.row_bytes), t0 = (int)uni((uint32_t)(tile * kTT));
   const int rl = lane / T::UPR, ul = lane % T::UPR;
   char* dst = stage + half * T::KB;
+  const int row = T::RPC * c + rl;
+  const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, kStreamPolicy);
+}
+
+// The same load for a wave that also reads the ring (consumer-issued
+// loads): written as an asm statement, so the compiler does not count it as
+// a pending write to LDS and does not wait for it (vmcnt(0)) before this
+// wave's reads of other stages. The asm has no register outputs; the caller
+// orders the data with explicit vmcnt waits and a barrier. M0 takes the
+// stage address (one wait state before the load reads it).
+template <int D>
+__device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, int tile, int lane, int half,
+                                                int c) {
+  using T = Tile<D>;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t a = reinterpret_cast<uint64_t>(half ? sg.v : sg.k);
+  // buffer descriptor: base, stride 0, extent in bytes, the same flags as
+  // the descriptors built for issue_chunk
+  const i32x4 rsrc = {(int)uni((uint32_t)a), (int)(uni((uint32_t)(a >> 32)) & 0xFFFFu), (int)uni(sg.bytes),
+                      0x00020000};
+  const int rb = (int)uni((uint32_t)sg.row_bytes), t0 = (int)uni((uint32_t)(tile * kTT));
+  const int rl = lane / T::UPR, ul = lane % T::UPR;
+  const int row = T::RPC * c + rl;
+  const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
+  const uint32_t m0 = uni(lds_addr(stage + half * T::KB + c * 1024));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
+      :
+      : "v"(voff), "s"(m0), "s"(rsrc)
+      : "memory", "m0");
+}
+
+template <int D>
+__device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int tile, int lane, int half) {
 #pragma unroll
-  for (int c = 0; c < T::CHUNKS; ++c) {
-    const int row = T::RPC * c + rl;
-    const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, kStreamPolicy);
-  }
+  for (int c = 0; c < Tile<D>::CHUNKS; ++c) issue_chunk<D>(stage, sg, tile, lane, half, c);
 }
 
 // Online-softmax state of RT row tiles. The row sums live in an MFMA
@@ -261,16 +294,25 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
 // the two waves of a pair sit on different SIMDs next to a wave of another
 // pair, so one wave's softmax (VALU) runs while another's products (MFMA)
 // do, and the pair's two partial states are merged through LDS at the end.
-template <int D, int RT, bool PAIR>
+//
+// With SELF (wave pairs, eight consumer waves, no producers) every consumer
+// wave issues a fixed share of each step's loads itself, AHEAD steps ahead,
+// and waits for its share of the current step before the step's barrier: the
+// two producer slots go to a fourth pair of row groups.
+template <int D, int RT, bool PAIR, bool SELF>
 __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
+  static_assert(!SELF || PAIR, "consumer-issued loads come with wave pairs");
   constexpr int NG = D / 32, MT = D / 16;
   constexpr int TPS = PAIR ? 2 : 1;          // tiles per barrier step
   constexpr int STAGES = PAIR ? 8 : 6;       // LDS ring depth in tiles
   constexpr int AHEAD = STAGES / TPS - 2;    // steps in flight ahead of the one computed
   using T = Tile<D>;
+  constexpr int SELF_WAVES = 8;
+  constexpr int PER = TPS * 2 * T::CHUNKS / SELF_WAVES;  // 1 KB loads per consumer per step (SELF)
+  static_assert(!SELF || PER * SELF_WAVES == TPS * 2 * T::CHUNKS, "even share of a step's loads");
   __shared__ __attribute__((aligned(16))) char ring[STAGES * 2 * T::KB];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ncons = blockDim.x / 64 - 2;
+  const int ncons = SELF ? SELF_WAVES : blockDim.x / 64 - 2;
   const int nw = ncons / TPS;  // row groups
   const int grp = wave % nw, parity = wave / nw;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -299,7 +341,23 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   const int ntiles = s0.ntiles + s1.ntiles;
   const int nsteps = (ntiles + TPS - 1) / TPS;
 
-  if (wave >= ncons) {
+  // SELF: this wave's share of the loads of one step (chunk q of the step's
+  // tiles goes to wave q / PER); past the last tile the last one is loaded
+  // again into a stage no step reads
+  auto issue_share = [&](int step) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = wave * PER + i;
+      const int ti = q / (2 * T::CHUNKS), half = (q / T::CHUNKS) % 2, c = q % T::CHUNKS;
+      int t = step * TPS + ti;
+      char* stage = ring + (t % STAGES) * 2 * T::KB;
+      t = min(t, ntiles - 1);
+      if (t < s0.ntiles) issue_chunk_asm<D>(stage, s0, t, lane, half, c);
+      else issue_chunk_asm<D>(stage, s1, t - s0.ntiles, lane, half, c);
+    }
+  };
+
+  if (!SELF && wave >= ncons) {
     // producer: K (first) or V (second) halves, AHEAD steps ahead
     const int half = wave - ncons;
     auto issue = [&](int t) {
@@ -350,6 +408,31 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
 
   VState<RT, MT> st;
   st.init();
+  if constexpr (SELF) {
+    // the query has landed before the ring starts, so the compiler (which
+    // does not see the ring's asm loads) has nothing left to wait for in the
+    // loop
+    wait_vm<0>();
+    if (ntiles > 0)
+      for (int sp = 0; sp < AHEAD; ++sp) issue_share(sp);
+  }
+  // One step's barrier. SELF: issue step sp + AHEAD, wait until this wave's
+  // share of step sp has landed, then a bare barrier (a workgroup fence would
+  // also wait for this wave's loads of the later steps; the asm statements
+  // keep the step's LDS reads below the barrier). Otherwise it pairs with the
+  // producers' bare barrier; the fence keeps this step's LDS reads below it
+  // (consumers have no loads in flight, so it costs nothing).
+  auto step_sync = [&](int sp) {
+    if constexpr (SELF) {
+      issue_share(sp + AHEAD);
+      wait_vm<AHEAD * PER>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
+  };
   // steps made of full context tiles need no mask; the partial last context
   // tile and the causal draft-block tiles follow in a second loop
   const int nfull_steps = (nval / kTT) / TPS;
@@ -357,14 +440,12 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) lim_all[rt] = kTT;
   for (int sp = 0; sp < nfull_steps; ++sp) {
-    // pairs with the producers' bare barrier; the fence keeps this step's LDS
-    // reads below it (consumers have no loads in flight, so it costs nothing)
-    __syncthreads();
+    step_sync(sp);
     const int t = sp * TPS + parity;
     tile_compute<D, RT, false>(ring + (t % STAGES) * 2 * T::KB, kTT, lane, Bq, lim_all, P.qscale, st);
   }
   for (int sp = nfull_steps; sp < nsteps; ++sp) {
-    __syncthreads();
+    step_sync(sp);
     const int t = sp * TPS + parity;
     if (t < ntiles) {
       const char* stage = ring + (t % STAGES) * 2 * T::KB;
@@ -381,6 +462,8 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   if constexpr (PAIR) {
     // hand the odd wave's state to the even wave through the (now idle) ring:
     // per row tile MT*4 accumulator words, the max and the sum, lane-major
+    // (SELF: every wave's ring loads have landed before the barrier)
+    if constexpr (SELF) wait_vm<0>();
     __syncthreads();
     constexpr int WORDS = MT * 4 + 2;
     float* xa = reinterpret_cast<float*>(ring) + (size_t)grp * RT * WORDS * 64 + lane;
@@ -497,15 +580,17 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
 }
 
 template <int D>
-void launch_verify(const VerifyParams& P, int rt, bool pair, int nwaves, dim3 grid, hipStream_t s,
+void launch_verify(const VerifyParams& P, int rt, bool pair, bool self, int nwaves, dim3 grid, hipStream_t s,
                    hipEvent_t start, hipEvent_t stop) {
-  const dim3 block(64 * (nwaves + 2));
-  if (pair) {
-    if (rt == 2) launch_ev(verify_kernel<D, 2, true>, grid, block, 0, s, start, stop, P);
-    else launch_ev(verify_kernel<D, 3, true>, grid, block, 0, s, start, stop, P);
+  const dim3 block(64 * (nwaves + (self ? 0 : 2)));
+  if (self) {
+    launch_ev(verify_kernel<D, 3, true, true>, grid, block, 0, s, start, stop, P);
+  } else if (pair) {
+    if (rt == 2) launch_ev(verify_kernel<D, 2, true, false>, grid, block, 0, s, start, stop, P);
+    else launch_ev(verify_kernel<D, 3, true, false>, grid, block, 0, s, start, stop, P);
   } else {
-    if (rt == 2) launch_ev(verify_kernel<D, 2, false>, grid, block, 0, s, start, stop, P);
-    else launch_ev(verify_kernel<D, 3, false>, grid, block, 0, s, start, stop, P);
+    if (rt == 2) launch_ev(verify_kernel<D, 2, false, false>, grid, block, 0, s, start, stop, P);
+    else launch_ev(verify_kernel<D, 3, false, false>, grid, block, 0, s, start, stop, P);
   }
 }
 
@@ -513,14 +598,16 @@ void launch_verify(const VerifyParams& P, int rt, bool pair, int nwaves, dim3 gr
 
 struct VerifyPlan {
   int rt, nwaves, tps, s_ctx;
-  bool pair;
+  bool pair, self;
 };
 
 // Row tiling: wave pairs with two row tiles per wave up to 6 tiles and three
-// up to 9; beyond, one wave per group of three row tiles (at most 6 consumer
-// waves plus the 2 producers, so 2 waves per SIMD and the whole register file
-// for the row tiles' accumulators). Two tiles per wave there (more consumer
-// waves) measured slower: every consumer reads each whole K/V tile from LDS. Context split of a call:
+// up to 9 (plus 2 producers); 10 to 12 tiles, four pairs of three that issue
+// their own loads; beyond, one wave per group of three row tiles (at most 6
+// consumer waves plus the 2 producers). Every case is 2 waves per SIMD at
+// most, with the whole register file for the row tiles' accumulators. Two
+// tiles per wave without pairs (more consumer waves) measured slower: every
+// consumer reads each whole K/V tile from LDS. Context split of a call:
 // about 256 workgroups (one per CU), whole 32-token tiles, at least 8 tiles
 // per split; the draft block rides on the last split. The split count never
 // decreases with chunk_tokens, so a workspace sized for the largest chunk
@@ -528,11 +615,14 @@ struct VerifyPlan {
 VerifyPlan verify_plan(const vc_attn_shape& sh, int n_rows, int chunk_tokens) {
   const int R = n_rows * (sh.n_q_heads / sh.n_kv_heads);
   const int tiles = (R + 15) / 16;
-  // up to 9 row tiles: wave pairs (at most 3 groups, 6 consumer waves);
-  // beyond: one wave per group of three row tiles (at most 6 waves)
-  const bool pair = tiles <= 9;
+  // up to 9 row tiles: wave pairs (at most 3 groups, 6 consumer waves, 2
+  // producers); 10 to 12: wave pairs of 4 groups that issue their own loads
+  // (8 consumer waves); beyond: one wave per group of three row tiles (at
+  // most 6 waves)
+  const bool self = tiles >= 10 && tiles <= 12;
+  const bool pair = tiles <= 9 || self;
   const int rt = (pair && tiles <= 6) ? 2 : 3;
-  const int nwaves = ((tiles + rt - 1) / rt) * (pair ? 2 : 1);
+  const int nwaves = self ? 8 : ((tiles + rt - 1) / rt) * (pair ? 2 : 1);
   const long long units = (long long)sh.batch * sh.n_kv_heads;
   const long long ctx_tiles = ((long long)chunk_tokens + kTT - 1) / kTT;
   long long s_ctx = (256 + units - 1) / units;
@@ -540,7 +630,7 @@ VerifyPlan verify_plan(const vc_attn_shape& sh, int n_rows, int chunk_tokens) {
   if (s_ctx > max_s) s_ctx = max_s;
   if (s_ctx < 1) s_ctx = 1;
   const long long tps = ((ctx_tiles + s_ctx - 1) / s_ctx) * kTT;
-  return VerifyPlan{rt, nwaves, (int)(tps > 0 ? tps : kTT), (int)s_ctx, pair};
+  return VerifyPlan{rt, nwaves, (int)(tps > 0 ? tps : kTT), (int)s_ctx, pair, self};
 }
 
 int verify_max_rows() { return 6 * 3 * 16; }
@@ -602,8 +692,10 @@ vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, cons
   const dim3 grid(P.S, sh.n_kv_heads, sh.batch);
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
-  if (sh.head_dim == 128) launch_verify<128>(P, plan.rt, plan.pair, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
-  else launch_verify<64>(P, plan.rt, plan.pair, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
+  if (sh.head_dim == 128)
+    launch_verify<128>(P, plan.rt, plan.pair, plan.self, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
+  else
+    launch_verify<64>(P, plan.rt, plan.pair, plan.self, plan.nwaves, grid, stream, tm.start, main_only ? tm.stop : nullptr);
   vc_status st = check_launch("verify attention");
   if (st != VC_OK) return st;
   hipEvent_t mstop = main_only ? nullptr : tm.stop;

@@ -257,8 +257,9 @@ VERIFY_CASES = [
     (2, 8, 2, 128, 1, [33, 1], None),
     (2, 16, 2, 128, 36, [1024, 300], None),   # R = 288, the largest row count; ragged context
     (1, 36, 4, 128, 15, [1024], None),        # R = 135: nine row tiles, the last one partly filled
-    (2, 32, 8, 128, 41, [1500, 777], None),   # R = 164: eleven row tiles, two per wave; ragged context
-    (1, 32, 8, 128, 48, [900], None),         # R = 192: twelve row tiles, the most at two per wave
+    (2, 32, 8, 128, 41, [1500, 777], None),   # R = 164: eleven row tiles; ragged context
+    (1, 32, 8, 128, 48, [900], None),         # R = 192: twelve row tiles (four wave pairs issuing their own loads)
+    (1, 16, 4, 64, 44, [1000], 384),          # R = 176 at D = 64: eleven row tiles, chunked
 ]
 
 

@@ -366,7 +366,7 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
   lds_words<NWL>(blk + BL::KC + ((16 + n) * WPT + qg * NWL) * 4, r.kw[1]);
   lds_words<VWL>(blk + BL::VC + lane * VWL * 4, r.vw);
   lds_words<4 * W>(blk + BL::KS + (qg * NG + W * jr) * 16, r.ks);
-  lds_words<CPL / 2>(blk + BL::KZ + CPL * n * 2, r.kz);
+  if constexpr (W == 1) lds_words<CPL / 2>(blk + BL::KZ + CPL * n * 2, r.kz);
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     uint32_t t[4];
@@ -385,9 +385,13 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
 //       CPL*t + e times log2(e)/sqrt(D), in fp32.
 template <int D, int W>
 struct KiviQuery {
-  static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL;
+  static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL, NG = Geo<D, W>::NG;
   uint32_t qp[W][4];
   float qz[HPL][CPL];
+  // rows of two or more channel groups (W >= 2): A operand of the key
+  // zero-point product, lane (q, (hl, jr)), K-step kk: fp16 pairs of
+  // q[hl][32 kk + 8 q + 0..7] on the head's first row (jr = 0), zero elsewhere
+  uint32_t qn[NG][4];
   float qscale;  // log2(e)/sqrt(D), applied to the fp32 scores
 };
 
@@ -399,9 +403,10 @@ struct KiviQuery {
 // one.
 template <int D, int W>
 struct KiviQueryRaw {
-  static constexpr int CPL = Geo<D, W>::CPL, HPL = Geo<D, W>::HPL;
+  static constexpr int CPL = Geo<D, W>::CPL, HPL = Geo<D, W>::HPL, NG = Geo<D, W>::NG;
   uint32_t qp[W][4];          // channels 8(q*NG + W*jr + w) + 0..7 of head hl
-  uint32_t qz[HPL][CPL / 2];  // channels CPL*t + 0..CPL-1 of head HPL*q + u
+  uint32_t qz[HPL][CPL / 2];  // channels CPL*t + 0..CPL-1 of head HPL*q + u (W = 1)
+  uint32_t qn[NG][4];         // channels 32 kk + 8q + 0..7 of head hl (W >= 2)
 };
 
 template <int N>
@@ -431,10 +436,15 @@ __device__ __forceinline__ void kivi_query_load(const DraftParams& P, int b, int
   const int hlc = hl < P.g ? hl : 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) global_words<4>(qb + (size_t)hlc * D + 8 * (qg * NG + W * jr + w), R.qp[w]);
+  if constexpr (W >= 2) {
 #pragma unroll
-  for (int u = 0; u < HPL; ++u) {
-    const int hb = HPL * qg + u;
-    global_words<CPL / 2>(qb + (size_t)(hb < P.g ? hb : 0) * D + CPL * n, R.qz[u]);
+    for (int kk = 0; kk < NG; ++kk) global_words<4>(qb + (size_t)hlc * D + 32 * kk + 8 * qg, R.qn[kk]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      const int hb = HPL * qg + u;
+      global_words<CPL / 2>(qb + (size_t)(hb < P.g ? hb : 0) * D + CPL * n, R.qz[u]);
+    }
   }
 }
 
@@ -457,18 +467,46 @@ __device__ __forceinline__ void kivi_query_finish(const DraftParams& P, int lane
       Q.qp[w][r] = pack_f16(x[0], x[1]);
     }
   Q.qscale = P.qscale;
+  if constexpr (W >= 2) {
+    const bool ok0 = ok && (n % NR) == 0;
 #pragma unroll
-  for (int u = 0; u < HPL; ++u) {
-    const bool okb = HPL * qg + u < P.g;
+    for (int kk = 0; kk < G::NG; ++kk)
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(half_of(R.qz[u], e)) * P.qscale : 0.f;
+      for (int r = 0; r < 4; ++r)
+        Q.qn[kk][r] = pack_f16(ok0 ? bf16_bits_to_f32(R.qn[kk][r] & 0xFFFFu) : 0.f,
+                               ok0 ? bf16_bits_to_f32(R.qn[kk][r] >> 16) : 0.f);
+  } else {
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      const bool okb = HPL * qg + u < P.g;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(half_of(R.qz[u], e)) * P.qscale : 0.f;
+    }
   }
 }
 
 // One 32-token block of the quantised body.
+// Rows of two or more channel groups: the key zero-point term sum_c q_c
+// zero_c of each head on the MFMA, the natural-order query of the head's
+// first row times the zero points read from the block's ring stage. The
+// product is exact in fp32 and seeds both score tiles of kivi_compute.
 template <int D, int BITS, int W>
-__device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int lane, const KiviQuery<D, W>& Q,
-                                             DState<D, W, 1>& st, uint32_t* lds_p) {
+__device__ __forceinline__ f32x4 kivi_zero_term(const char* stage, int lane, const KiviQuery<D, W>& Q) {
+  using BL = BlockLayout<D, BITS>;
+  const int qg = lane >> 4;
+  f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const u32x4 z = *reinterpret_cast<const u32x4*>(stage + BL::KZ + (32 * kk + 8 * qg) * 2);
+    cb = mfma_f16(u32x4{Q.qn[kk][0], Q.qn[kk][1], Q.qn[kk][2], Q.qn[kk][3]}, z, cb);
+  }
+  return cb;
+}
+
+// cb: the zero-point term from kivi_zero_term (W >= 2; zero for W = 1).
+template <int D, int BITS, int W>
+__device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, const f32x4& cb, int lane,
+                                             const KiviQuery<D, W>& Q, DState<D, W, 1>& st, uint32_t* lds_p) {
   using G = Geo<D, W>;
   constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, MT = G::MT, CPL = G::CPL;
   constexpr int NWL = KiviRaw<D, BITS, W>::NWL, VWL = KiviRaw<D, BITS, W>::VWL;
@@ -495,24 +533,30 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, int
       const uint32_t sp = __builtin_amdgcn_perm(w1, w0, (r & 1) ? 0x07060302u : 0x05040100u);
       Aq[w][r] = as_u32(as_f16x2(Q.qp[w][r]) * as_f16x2(sp));
     }
-  // zero-point bias of the lane's heads: sum over channels CPL*t .. (fp32
-  // query times fp16 zero point, mixed-precision FMAs in two chains) and
-  // over the row
+  // key zero-point term sum_c q_c zero_c of each head. One-group rows (W = 1):
+  // fp32 query (scaled) times fp16 zero point over channels CPL*t .., in two
+  // mixed-precision FMA chains, then over the row, added in the softmax.
+  // Wider rows: cb, already inside the scores.
   float bias[HPL];
+  if constexpr (W >= 2) {
 #pragma unroll
-  for (int u = 0; u < HPL; ++u) {
-    float x0 = 0.f, x1 = 0.f;
+    for (int u = 0; u < HPL; ++u) bias[u] = 0.f;
+  } else {
 #pragma unroll
-    for (int p = 0; p < CPL / 2; ++p) {
-      x0 = fmaf(Q.qz[u][2 * p], f16_lo(raw.kz[p]), x0);
-      x1 = fmaf(Q.qz[u][2 * p + 1], f16_hi(raw.kz[p]), x1);
+    for (int u = 0; u < HPL; ++u) {
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int p = 0; p < CPL / 2; ++p) {
+        x0 = fmaf(Q.qz[u][2 * p], f16_lo(raw.kz[p]), x0);
+        x1 = fmaf(Q.qz[u][2 * p + 1], f16_hi(raw.kz[p]), x1);
+      }
+      bias[u] = row_sum16(x0 + x1);
     }
-    bias[u] = row_sum16(x0 + x1);
   }
   f32x4 c[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    c[i] = cb;
 #pragma unroll
     for (int kk = 0; kk < NG; ++kk) {
       const bool on = (jr == kk / W);
@@ -1037,7 +1081,7 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
                          const char* stage2) {
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
           pace(refill_blk - 5);
-          kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
+          kivi_compute<D, BITS, W>(cur, f32x4{0.f, 0.f, 0.f, 0.f}, lane, Q, st, lds_p);
           wait_vm<3 * BL::NI>();  // block i + 2 has landed
           kivi_read<D, BITS, W>(nxt2, stage2, lane);
         };
@@ -1060,11 +1104,15 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
           if (blk + 6 > last) break;
         }
       } else {
-        auto step = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt, char* refill, int refill_blk,
-                        const char* next_stage) {
+        auto step = [&](const KiviRaw<D, BITS, W>& cur, const char* cur_stage, KiviRaw<D, BITS, W>& nxt,
+                        char* refill, int refill_blk, const char* next_stage) {
+          // the zero-point term reads the block's stage before the refill
+          // is issued (only the next block's load is then in flight)
+          f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (W >= 2) cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
           pace(refill_blk - 2);
-          kivi_compute<D, BITS, W>(cur, lane, Q, st, lds_p);
+          kivi_compute<D, BITS, W>(cur, cb, lane, Q, st, lds_p);
           wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
           kivi_read<D, BITS, W>(nxt, next_stage, lane);
         };
@@ -1072,17 +1120,18 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         wait_vm<BL::NI>();
         kivi_read<D, BITS, W>(ra, w0, lane);
         for (int blk = b0;; blk += 6) {
-          step(ra, rb, w2, blk + 2, w1);
+          // block i sits in stage i mod 3
+          step(ra, w0, rb, w2, blk + 2, w1);
           if (blk + 1 > last) break;
-          step(rb, ra, w0, blk + 3, w2);
+          step(rb, w1, ra, w0, blk + 3, w2);
           if (blk + 2 > last) break;
-          step(ra, rb, w1, blk + 4, w0);
+          step(ra, w2, rb, w1, blk + 4, w0);
           if (blk + 3 > last) break;
-          step(rb, ra, w2, blk + 5, w1);
+          step(rb, w0, ra, w2, blk + 5, w1);
           if (blk + 4 > last) break;
-          step(ra, rb, w0, blk + 6, w2);
+          step(ra, w1, rb, w0, blk + 6, w2);
           if (blk + 5 > last) break;
-          step(rb, ra, w1, blk + 7, w0);
+          step(rb, w2, ra, w1, blk + 7, w0);
           if (blk + 6 > last) break;
         }
       }

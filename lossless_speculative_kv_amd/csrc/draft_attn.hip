@@ -347,12 +347,11 @@ __device__ __forceinline__ void lds_words(const char* p, uint32_t* w) {
 
 template <int D, int BITS, int W>
 struct KiviRaw {
-  static constexpr int NWL = D * BITS / 128, VWL = D * BITS / 64, CPL = Geo<D, W>::CPL;
-  uint32_t kw[2][NWL];   // key codes of tokens t and t + 16
-  uint32_t vw[VWL];      // value codes of the lane's slots
-  uint32_t ks[4 * W];    // key scales of the lane's W 8-channel runs
-  uint32_t kz[CPL / 2];  // key zero points of channels CPL*t ..
-  u32x4 vs[W], vz[W];    // value scales / zeros of the lane's 8 slots, per group
+  static constexpr int NWL = D * BITS / 128, VWL = D * BITS / 64;
+  uint32_t kw[2][NWL];  // key codes of tokens t and t + 16
+  uint32_t vw[VWL];     // value codes of the lane's slots
+  uint32_t ks[4 * W];   // key scales of the lane's W 8-channel runs
+  u32x4 vs[W], vz[W];   // value scales / zeros of the lane's 8 slots, per group
 };
 
 // The lane's operands of one staged block.
@@ -360,13 +359,11 @@ template <int D, int BITS, int W>
 __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* blk, int lane) {
   using BL = BlockLayout<D, BITS>;
   constexpr int NG = D / 32, NR = NG / W, WPT = BL::WPT, NWL = KiviRaw<D, BITS, W>::NWL, VWL = BL::VWL;
-  constexpr int CPL = D / 16;
   const int n = lane & 15, qg = lane >> 4, jr = n % NR;
   lds_words<NWL>(blk + BL::KC + (n * WPT + qg * NWL) * 4, r.kw[0]);
   lds_words<NWL>(blk + BL::KC + ((16 + n) * WPT + qg * NWL) * 4, r.kw[1]);
   lds_words<VWL>(blk + BL::VC + lane * VWL * 4, r.vw);
   lds_words<4 * W>(blk + BL::KS + (qg * NG + W * jr) * 16, r.ks);
-  if constexpr (W == 1) lds_words<CPL / 2>(blk + BL::KZ + CPL * n * 2, r.kz);
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     uint32_t t[4];
@@ -381,16 +378,13 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
 //   qp: A layout, lane (q, (hl, jr)), run w = K-step W*jr + w: fp16 pairs
 //       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)], zero for
 //       padding heads (the scores are scaled after the MFMA);
-//   qz: score layout, lane (q, t): the query of head HPL*q + u at channels
-//       CPL*t + e times log2(e)/sqrt(D), in fp32.
+//   qn: A operand of the key zero-point product, lane (q, (hl, jr)), K-step
+//       kk: fp16 pairs of q[hl][32 kk + 8q + 0..7] on the head's first row
+//       (jr = 0), zero elsewhere.
 template <int D, int W>
 struct KiviQuery {
-  static constexpr int HPL = Geo<D, W>::HPL, CPL = Geo<D, W>::CPL, NG = Geo<D, W>::NG;
+  static constexpr int NG = Geo<D, W>::NG;
   uint32_t qp[W][4];
-  float qz[HPL][CPL];
-  // rows of two or more channel groups (W >= 2): A operand of the key
-  // zero-point product, lane (q, (hl, jr)), K-step kk: fp16 pairs of
-  // q[hl][32 kk + 8 q + 0..7] on the head's first row (jr = 0), zero elsewhere
   uint32_t qn[NG][4];
   float qscale;  // log2(e)/sqrt(D), applied to the fp32 scores
 };
@@ -403,10 +397,9 @@ struct KiviQuery {
 // one.
 template <int D, int W>
 struct KiviQueryRaw {
-  static constexpr int CPL = Geo<D, W>::CPL, HPL = Geo<D, W>::HPL, NG = Geo<D, W>::NG;
-  uint32_t qp[W][4];          // channels 8(q*NG + W*jr + w) + 0..7 of head hl
-  uint32_t qz[HPL][CPL / 2];  // channels CPL*t + 0..CPL-1 of head HPL*q + u (W = 1)
-  uint32_t qn[NG][4];         // channels 32 kk + 8q + 0..7 of head hl (W >= 2)
+  static constexpr int NG = Geo<D, W>::NG;
+  uint32_t qp[W][4];   // channels 8(q*NG + W*jr + w) + 0..7 of head hl
+  uint32_t qn[NG][4];  // channels 32 kk + 8q + 0..7 of head hl
 };
 
 template <int N>
@@ -430,30 +423,22 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t* w, int i) { return (
 template <int D, int W>
 __device__ __forceinline__ void kivi_query_load(const DraftParams& P, int b, int hk, int lane, KiviQueryRaw<D, W>& R) {
   using G = Geo<D, W>;
-  constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, CPL = G::CPL;
+  constexpr int NG = G::NG, NR = G::NR;
   const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
   const uint16_t* qb = P.q + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
   const int hlc = hl < P.g ? hl : 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) global_words<4>(qb + (size_t)hlc * D + 8 * (qg * NG + W * jr + w), R.qp[w]);
-  if constexpr (W >= 2) {
 #pragma unroll
-    for (int kk = 0; kk < NG; ++kk) global_words<4>(qb + (size_t)hlc * D + 32 * kk + 8 * qg, R.qn[kk]);
-  } else {
-#pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      const int hb = HPL * qg + u;
-      global_words<CPL / 2>(qb + (size_t)(hb < P.g ? hb : 0) * D + CPL * n, R.qz[u]);
-    }
-  }
+  for (int kk = 0; kk < NG; ++kk) global_words<4>(qb + (size_t)hlc * D + 32 * kk + 8 * qg, R.qn[kk]);
 }
 
 template <int D, int W>
 __device__ __forceinline__ void kivi_query_finish(const DraftParams& P, int lane, const KiviQueryRaw<D, W>& R,
                                                   KiviQuery<D, W>& Q) {
   using G = Geo<D, W>;
-  constexpr int NR = G::NR, HPL = G::HPL, CPL = G::CPL;
-  const int n = lane & 15, qg = lane >> 4, hl = n / NR;
+  constexpr int NR = G::NR;
+  const int n = lane & 15, hl = n / NR;
   const bool ok = hl < P.g;
 #pragma unroll
   for (int w = 0; w < W; ++w)
@@ -467,29 +452,20 @@ __device__ __forceinline__ void kivi_query_finish(const DraftParams& P, int lane
       Q.qp[w][r] = pack_f16(x[0], x[1]);
     }
   Q.qscale = P.qscale;
-  if constexpr (W >= 2) {
-    const bool ok0 = ok && (n % NR) == 0;
+  const bool ok0 = ok && (n % NR) == 0;
 #pragma unroll
-    for (int kk = 0; kk < G::NG; ++kk)
+  for (int kk = 0; kk < G::NG; ++kk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Q.qn[kk][r] = pack_f16(ok0 ? bf16_bits_to_f32(R.qn[kk][r] & 0xFFFFu) : 0.f,
-                               ok0 ? bf16_bits_to_f32(R.qn[kk][r] >> 16) : 0.f);
-  } else {
-#pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      const bool okb = HPL * qg + u < P.g;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) Q.qz[u][e] = okb ? bf16_bits_to_f32(half_of(R.qz[u], e)) * P.qscale : 0.f;
-    }
-  }
+    for (int r = 0; r < 4; ++r)
+      Q.qn[kk][r] = pack_f16(ok0 ? bf16_bits_to_f32(R.qn[kk][r] & 0xFFFFu) : 0.f,
+                             ok0 ? bf16_bits_to_f32(R.qn[kk][r] >> 16) : 0.f);
 }
 
 // One 32-token block of the quantised body.
-// Rows of two or more channel groups: the key zero-point term sum_c q_c
-// zero_c of each head on the MFMA, the natural-order query of the head's
-// first row times the zero points read from the block's ring stage. The
-// product is exact in fp32 and seeds both score tiles of kivi_compute.
+// The key zero-point term sum_c q_c zero_c of each head on the MFMA: the
+// natural-order query of the head's first row times the zero points read
+// from the block's ring stage. The product is exact in fp32 and seeds both
+// score tiles of kivi_compute.
 template <int D, int BITS, int W>
 __device__ __forceinline__ f32x4 kivi_zero_term(const char* stage, int lane, const KiviQuery<D, W>& Q) {
   using BL = BlockLayout<D, BITS>;
@@ -503,7 +479,7 @@ __device__ __forceinline__ f32x4 kivi_zero_term(const char* stage, int lane, con
   return cb;
 }
 
-// cb: the zero-point term from kivi_zero_term (W >= 2; zero for W = 1).
+// cb: the key zero-point term from kivi_zero_term.
 template <int D, int BITS, int W>
 __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, const f32x4& cb, int lane,
                                              const KiviQuery<D, W>& Q, DState<D, W, 1>& st, uint32_t* lds_p) {
@@ -533,26 +509,10 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
       const uint32_t sp = __builtin_amdgcn_perm(w1, w0, (r & 1) ? 0x07060302u : 0x05040100u);
       Aq[w][r] = as_u32(as_f16x2(Q.qp[w][r]) * as_f16x2(sp));
     }
-  // key zero-point term sum_c q_c zero_c of each head. One-group rows (W = 1):
-  // fp32 query (scaled) times fp16 zero point over channels CPL*t .., in two
-  // mixed-precision FMA chains, then over the row, added in the softmax.
-  // Wider rows: cb, already inside the scores.
+  // the key zero-point term (cb) is already inside the scores
   float bias[HPL];
-  if constexpr (W >= 2) {
 #pragma unroll
-    for (int u = 0; u < HPL; ++u) bias[u] = 0.f;
-  } else {
-#pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-      for (int p = 0; p < CPL / 2; ++p) {
-        x0 = fmaf(Q.qz[u][2 * p], f16_lo(raw.kz[p]), x0);
-        x1 = fmaf(Q.qz[u][2 * p + 1], f16_hi(raw.kz[p]), x1);
-      }
-      bias[u] = row_sum16(x0 + x1);
-    }
-  }
+  for (int u = 0; u < HPL; ++u) bias[u] = 0.f;
   f32x4 c[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1077,11 +1037,12 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         // three register sets: the operands of block i + 2 are read while
         // block i is computed, so the LDS reads have a whole step to land
         KiviRaw<D, BITS, W> rc;
-        auto step3 = [&](const KiviRaw<D, BITS, W>& cur, KiviRaw<D, BITS, W>& nxt2, char* refill, int refill_blk,
-                         const char* stage2) {
+        auto step3 = [&](const KiviRaw<D, BITS, W>& cur, const char* cur_stage, KiviRaw<D, BITS, W>& nxt2,
+                         char* refill, int refill_blk, const char* stage2) {
+          const f32x4 cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
           pace(refill_blk - 5);
-          kivi_compute<D, BITS, W>(cur, f32x4{0.f, 0.f, 0.f, 0.f}, lane, Q, st, lds_p);
+          kivi_compute<D, BITS, W>(cur, cb, lane, Q, st, lds_p);
           wait_vm<3 * BL::NI>();  // block i + 2 has landed
           kivi_read<D, BITS, W>(nxt2, stage2, lane);
         };
@@ -1090,17 +1051,18 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         kivi_read<D, BITS, W>(ra, w0, lane);
         kivi_read<D, BITS, W>(rb, w1, lane);
         for (int blk = b0;; blk += 6) {
-          step3(ra, rc, w5, blk + 5, w2);
+          // block i sits in stage i mod 6
+          step3(ra, w0, rc, w5, blk + 5, w2);
           if (blk + 1 > last) break;
-          step3(rb, ra, w0, blk + 6, w3);
+          step3(rb, w1, ra, w0, blk + 6, w3);
           if (blk + 2 > last) break;
-          step3(rc, rb, w1, blk + 7, w4);
+          step3(rc, w2, rb, w1, blk + 7, w4);
           if (blk + 3 > last) break;
-          step3(ra, rc, w2, blk + 8, w5);
+          step3(ra, w3, rc, w2, blk + 8, w5);
           if (blk + 4 > last) break;
-          step3(rb, ra, w3, blk + 9, w0);
+          step3(rb, w4, ra, w3, blk + 9, w0);
           if (blk + 5 > last) break;
-          step3(rc, rb, w4, blk + 10, w1);
+          step3(rc, w5, rb, w4, blk + 10, w1);
           if (blk + 6 > last) break;
         }
       } else {
@@ -1108,8 +1070,7 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
                         char* refill, int refill_blk, const char* next_stage) {
           // the zero-point term reads the block's stage before the refill
           // is issued (only the next block's load is then in flight)
-          f32x4 cb = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (W >= 2) cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
+          const f32x4 cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
           pace(refill_blk - 2);
           kivi_compute<D, BITS, W>(cur, cb, lane, Q, st, lds_p);

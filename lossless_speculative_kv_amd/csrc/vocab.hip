@@ -149,40 +149,52 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
   for (int t = 0; t < MS; ++t) hrow[t] = P.hb + (size_t)(16 * t + n) * P.K + 8 * qg;
 
   // W k-steps of 128 are double-buffered in registers: the loads of step
-  // i + 1 are in flight while step i is multiplied
+  // i + 1 are in flight while step i is multiplied. Every W load is
+  // unconditional: a row past the vocabulary reads row 0 and only feeds
+  // logits the epilogue skips (a load under a per-lane condition, or masked
+  // right after it, is waited for at once). A step's hidden operands are
+  // loaded just before the next step's W: vector-memory loads complete in
+  // issue order, so waiting for the hidden values leaves the W loads in
+  // flight.
   auto load = [&](u32x4 (&A)[NA][4], int k0) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < 4; ++kk) A[a][kk] = *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk);
   };
-  auto compute = [&](const u32x4 (&A)[NA][4], int k0) {
+  auto load_h = [&](u32x4 (&B)[MS][4], int k0) {
 #pragma unroll
-    for (int t = 0; t < MS; ++t) {
-      u32x4 B[4];
+    for (int t = 0; t < MS; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) B[kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 32 * kk);
+      for (int kk = 0; kk < 4; ++kk) B[t][kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 32 * kk);
+  };
+  auto compute = [&](const u32x4 (&A)[NA][4], const u32x4 (&B)[MS][4]) {
+#pragma unroll
+    for (int t = 0; t < MS; ++t)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B[kk], acc[a][t]);
-    }
+        for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B[t][kk], acc[a][t]);
   };
-  u32x4 Aa[NA][4], Ab[NA][4];
+  u32x4 Aa[NA][4], Ab[NA][4], B[MS][4];
   // a wave past the last vocab row has nothing to stream (and must not lead
   // the pacing)
   if (vbase < P.V) {
     load(Aa, 0);
     int k0 = 0;
     for (; k0 + 256 <= P.K; k0 += 256) {
+      load_h(B, k0);
       load(Ab, k0 + 128);
       pace_waves<kStreamWaves>(prog_lds, wave, k0 >> 8);
-      compute(Aa, k0);
+      compute(Aa, B);
+      load_h(B, k0 + 128);
       if (k0 + 256 < P.K) load(Aa, k0 + 256);
-      compute(Ab, k0 + 128);
+      compute(Ab, B);
     }
-    if (k0 < P.K) compute(Aa, k0);  // K / 128 odd: the last step is already loaded
+    if (k0 < P.K) {  // K / 128 odd: the last step's W is already loaded
+      load_h(B, k0);
+      compute(Aa, B);
+    }
   }
   int mrow[MS];
 #pragma unroll
@@ -242,12 +254,14 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
   // W for one chunk: lane group qg of K-step kk reads k0 + 32*kk + 8*qg (with the other lane
   // groups, 64 contiguous bytes of each row per instruction)
   constexpr int KS = kKC / 32;  // K-steps per chunk
+  // (unconditional loads: a row past the vocabulary reads row 0 and only
+  // feeds logits the epilogue skips; a load under a per-lane condition, or
+  // masked right after it, is waited for at once)
   auto load_w = [&](u32x4 (&A)[NA][KS], int k0) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        A[a][kk] = wok[a] ? *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk + 8 * qg) : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < KS; ++kk) A[a][kk] = *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk + 8 * qg);
   };
   auto compute = [&](const u32x4 (&A)[NA][KS], const uint16_t* cur) {
 #pragma unroll
@@ -272,13 +286,13 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
     constexpr int HPT = (16 * NMT * (kKC / 8) + 64 * kStagedWaves - 1) / (64 * kStagedWaves);
     u32x4 hreg[HPT];
     const int chunks = P.Mp * (kKC / 8);
+    // (a slot past the chunk loads the chunk's last unit and is not stored)
     auto hload = [&](int k0) {
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
-        const int c = threadIdx.x + i * 64 * kStagedWaves;
+        const int c = min((int)threadIdx.x + i * 64 * kStagedWaves, chunks - 1);
         const int m = c / (kKC / 8), x = c % (kKC / 8);
-        hreg[i] = c < chunks ? *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x)
-                             : u32x4{0u, 0u, 0u, 0u};
+        hreg[i] = *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x);
       }
     };
     auto hstore = [&](int buf) {
@@ -290,28 +304,37 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
         if (c < chunks) *reinterpret_cast<u32x4*>(dst + m * HSTR + 8 * x) = hreg[i];
       }
     };
-    u32x4 Aa[NA][KS], Ab[NA][KS];
+    // W chunks in three register sets, loaded two chunks ahead (one chunk
+    // ahead left the kernel bound by the loads' latency)
+    // The loads of a chunk go out hidden first, then W: waiting for a hidden
+    // chunk one iteration later (vector-memory loads complete in issue
+    // order) then leaves that chunk's W loads in flight.
+    u32x4 Aa[NA][KS], Ab[NA][KS], Ac[NA][KS];
     hload(0);
     hstore(0);
     if (nk > 1) hload(kKC);
     load_w(Aa, 0);
+    if (nk > 1) load_w(Ab, kKC);
     __syncthreads();
-    // iteration kc: W of kc + 1 in flight, hidden kc + 1 -> LDS, hidden kc + 2 in flight
-    auto iter = [&](const u32x4 (&Acur)[NA][KS], u32x4 (&Anext)[NA][KS], int kc) {
-      if (kc + 1 < nk) {
-        load_w(Anext, (kc + 1) * kKC);
-        hstore((kc + 1) & 1);
-        if (kc + 2 < nk) hload((kc + 2) * kKC);
+    // iteration kc: hidden kc + 1 -> LDS; hidden and W of kc + 2 issued; W of
+    // kc + 1 still in flight
+    auto iter = [&](const u32x4 (&Acur)[NA][KS], u32x4 (&Aload)[NA][KS], int kc) {
+      if (kc + 1 < nk) hstore((kc + 1) & 1);
+      if (kc + 2 < nk) {
+        hload((kc + 2) * kKC);
+        load_w(Aload, (kc + 2) * kKC);
       }
       compute(Acur, hs + (kc & 1) * stage_halfs);
       __syncthreads();
     };
     int kc = 0;
-    for (; kc + 2 <= nk; kc += 2) {
-      iter(Aa, Ab, kc);
+    for (; kc + 3 <= nk; kc += 3) {
+      iter(Aa, Ac, kc);
       iter(Ab, Aa, kc + 1);
+      iter(Ac, Ab, kc + 2);
     }
-    if (kc < nk) iter(Aa, Ab, kc);
+    if (kc < nk) iter(Aa, Ac, kc);
+    if (kc + 1 < nk) iter(Ab, Aa, kc + 1);
   } else {
     stage(0, 0);
     __syncthreads();

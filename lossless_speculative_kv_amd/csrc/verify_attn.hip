@@ -115,7 +115,7 @@ __device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int 
 // a pending write to LDS and does not wait for it (vmcnt(0)) before this
 // wave's reads of other stages. The asm has no register outputs; the caller
 // orders the data with explicit vmcnt waits and a barrier. M0 takes the
-// stage address (one wait state before the load reads it).
+// stage address (one wait state before the load reads it) and is restored.
 template <int D>
 __device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, int tile, int lane, int half,
                                                 int c) {
@@ -131,13 +131,18 @@ __device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, 
   const int row = T::RPC * c + rl;
   const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
   const uint32_t m0 = uni(lds_addr(stage + half * T::KB + c * 1024));
+  // M0 is reserved to the compiler (a clobber of it is not honoured), so the
+  // statement puts its value back after the load has read it
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
-      :
+      "buffer_load_dwordx4 %1, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(voff), "s"(m0), "s"(rsrc)
-      : "memory", "m0");
+      : "memory");
 }
 
 template <int D>

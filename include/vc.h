@@ -119,7 +119,10 @@ enum { VC_DRAFT_DENSE = 0, VC_DRAFT_KIVI = 1, VC_DRAFT_TOKDROP = 2 };
 typedef struct {
   int32_t kind;
   int32_t bits;       /* KIVI: 2 or 4; ignored otherwise */
-  int32_t body_cap;   /* body capacity in tokens (KIVI: multiple of 32) */
+  int32_t body_cap;   /* body capacity in tokens (KIVI: multiple of 32, and one
+                         (sequence, KV head)'s records, body_cap / 32 records of
+                         8 * head_dim * (bits + 1) bytes, below 2^31 bytes;
+                         VC_ERR_UNSUPPORTED otherwise) */
   int32_t tail_cap;   /* tail capacity in tokens (multiple of 32) */
   const int32_t *body_len; /* [B] */
   const int32_t *tail_len; /* [B], >= 1 when attending */

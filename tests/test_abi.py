@@ -68,6 +68,21 @@ def test_draft_argument_checks():
     assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv(kivi_blocks=0x100010)), C.byref(out)) == L.VC_ERR_INVALID_ARG
     assert "aligned" in L.last_error()
     assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(kivi_kv()), C.byref(out)) == L.VC_OK
+
+
+def test_kivi_records_within_32_bit_offsets():
+    # one (sequence, KV head)'s records are addressed with 32-bit byte offsets:
+    # at D = 128, 2-bit, a record is 3072 bytes, so 699050 records fit below
+    # 2^31 bytes and 699051 do not
+    sh = shape()
+    out = C.c_size_t()
+    rec = 8 * 128 * 3
+    assert (2**31 - 1) // rec == 699050
+    ok = kivi_kv(body_cap=699050 * 32)
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(ok), C.byref(out)) == L.VC_OK
+    big = kivi_kv(body_cap=699051 * 32)
+    assert L.lib.vc_draft_workspace_bytes(C.byref(sh), C.byref(big), C.byref(out)) == L.VC_ERR_UNSUPPORTED
+    assert "2^31" in L.last_error()
     assert out.value > 0
     # workspace too small
     rc = L.lib.vc_draft_decode_attn(C.byref(sh), 0x10000, C.byref(kivi_kv()), 0x10000, 0x10000, 16, None)

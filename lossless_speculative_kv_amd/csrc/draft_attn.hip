@@ -987,9 +987,9 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
     // slots first, so the body waves end together
     const uint32_t prog_lds = lds_addr(progress);
     auto pace = [&](int i) { pace_waves<NW>(prog_lds, wave, i); };
-    // the body length, then the query, go out first; the ring starts before
-    // either has arrived
-    // (a scalar load: its counter is not the one the ring's loads wait on)
+    // The body length (a scalar load, on a counter the ring's loads do not
+    // wait on) and the query go out first; the ring starts before either has
+    // arrived.
     const int blen = ((const __attribute__((address_space(4))) int*)(P.body_len))[b];
     KiviQueryRaw<D, W> qraw;
     kivi_query_load<D, W>(P, b, hk, lane, qraw);
@@ -1025,12 +1025,12 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         issue_block<D, BITS>(w4, res, gblk(min(4, last_cap)), lane);
       }
       const int cnt = count(min(max(blen, 0), P.body_cap) / 32);
-      {
       // NS-stage ring, loads issued NS - 1 blocks ahead; the operands of a
       // later block move from LDS to registers at the end of a step, so their
       // latency overlaps the step's last MFMAs. Past the wave's last block
       // the last one is loaded again (into a stage that is not read), which
-      // keeps every wait count constant.
+      // keeps every wait count constant. A wave whose real range is empty
+      // runs one step on its first speculative block and drops it below.
       const int b0 = 0, last = max(cnt - 1, 0);
       KiviRaw<D, BITS, W> ra, rb;
       if constexpr (NS == 6) {
@@ -1095,7 +1095,6 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
           step(rb, w2, ra, w1, blk + 7, w0);
           if (blk + 6 > last) break;
         }
-      }
       }
       // every ring load has landed before the ring's memory is reused
       wait_vm<0>();

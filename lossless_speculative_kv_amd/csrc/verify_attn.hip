@@ -90,11 +90,11 @@ struct Segment {
 
 __device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Issue the direct-to-LDS loads of the K (half 0) or V (half 1) part of one
-// tile; one producer wave per half. Lane l of chunk c fills LDS unit 64c + l,
-// i.e. row RPC*c + l / UPR, unit l % UPR, with the global unit that the
-// swizzle puts there. Every operand that is wave-uniform is made visibly so
-// (the buffer resource must sit in scalar registers).
+// Issue the direct-to-LDS load of 1 KB chunk c of the K (half 0) or V
+// (half 1) part of one tile. Lane l of chunk c fills LDS unit 64c + l, i.e.
+// row RPC*c + l / UPR, unit l % UPR, with the global unit that the swizzle
+// puts there. Every operand that is wave-uniform is made visibly so (the
+// buffer resource must sit in scalar registers).
 template <int D>
 __device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int tile, int lane, int half, int c) {
   using T = Tile<D>;
@@ -145,6 +145,7 @@ __device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, 
       : "memory");
 }
 
+// A whole half of a tile: one producer wave per half.
 template <int D>
 __device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int tile, int lane, int half) {
 #pragma unroll

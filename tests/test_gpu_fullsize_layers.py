@@ -13,6 +13,12 @@ outputs computed one by one by the oracle:
 * Llama-70B layer with a 1M-token context (B = 1, 64 q / 8 KV heads, KIVI-2,
   g = 8, full cache in pinned host memory): the same for one KV head.
 
+Each test then runs the layer's verification pass and checks sampled
+(sequence, head, draft row) outputs over the whole context plus the causal
+draft block: on the Mistral-24B layer (eleven row tiles) the wave pairs that
+issue their own loads, on the Qwen-32B layer the wave pairs with producer
+waves, on the 1M-token layer the chunked pass staged from host memory.
+
 Tolerances as in the kernel tests: attention max |d| <= 1e-2 and rel-L2 <=
 2e-3; kept positions and records bit-exact."""
 import gc
@@ -49,6 +55,31 @@ def release(e):
     del e
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def check_verify(eng, samples):
+    """Verification pass of the round's block, then the oracle on sampled
+    (sequence, KV head, draft rows): row j sees the context and block rows
+    0..j (query head hk * g + j mod g)."""
+    c = eng.cfg
+    g = c.n_q_heads // c.n_kv_heads
+    eng.embed_block()
+    eng.verify_attention()
+    torch.cuda.synchronize()
+    ctx = eng.ctx_len.cpu().numpy()
+    o = eng.o_ver.cpu().numpy()
+    for b, hk, rows in samples:
+        n = int(ctx[b])
+        K = f64(eng.full_k[b, hk, :n])
+        V = f64(eng.full_v[b, hk, :n])
+        kn = f64(eng.kn[:, b, hk])
+        vn = f64(eng.vn[:, b, hk])
+        for j in rows:
+            h = hk * g + (j % g)
+            log(f"full size verify ({c.name}): sequence {b} head {h} row {j}, context {n}")
+            ref = oracle.attend(f64(eng.qv[j, b, h]), np.concatenate([K, kn[:j + 1]]), np.concatenate([V, vn[:j + 1]]))
+            mad, rl2 = assert_attention_close(o[j, b, h], ref, f"verify ({b}, {h}, row {j})")
+            log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
 
 
 def check_kivi_unit(eng, b, hk):
@@ -90,6 +121,7 @@ def test_mistral_tokdrop_draft():
         ref = np.stack([oracle.attend(q[i], K, V) for i in range(g)])
         mad, rl2 = assert_attention_close(out[b, hk * g:(hk + 1) * g], ref, f"draft unit ({b}, {hk})")
         log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
+    check_verify(eng, [(0, 0, (0, 21, c.k)), (c.batch - 1, c.n_kv_heads - 1, (3, c.k))])
     release(eng)
 
 
@@ -98,10 +130,13 @@ def test_qwen_kivi_draft():
     c = eng.cfg
     for b, hk in [(0, 0), (c.batch - 1, c.n_kv_heads - 1), (9, 4)]:
         check_kivi_unit(eng, b, hk)
+    check_verify(eng, [(0, 0, (0, 12, c.k)), (c.batch - 1, c.n_kv_heads - 1, (7, c.k))])
     release(eng)
 
 
 def test_llama70b_1m_kivi_draft():
     eng = build("llama-70b-layer-1m")
-    check_kivi_unit(eng, 0, eng.cfg.n_kv_heads - 1)
+    c = eng.cfg
+    check_kivi_unit(eng, 0, c.n_kv_heads - 1)
+    check_verify(eng, [(0, 3, (0, c.k))])
     release(eng)

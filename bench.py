@@ -190,7 +190,9 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path is measured on a single "
-              "MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "MI355X. Across GPUs it would shard by sequence (draft and verify attention need no exchange) and, "
+              "for one long sequence, by context, merging (max, sum, output) partials; the vocabulary shards by "
+              "columns with one 64-bit argmax key per row.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -260,6 +260,8 @@ VERIFY_CASES = [
     (2, 32, 8, 128, 41, [1500, 777], None),   # R = 164: eleven row tiles; ragged context
     (1, 32, 8, 128, 48, [900], None),         # R = 192: twelve row tiles (four wave pairs issuing their own loads)
     (1, 16, 4, 64, 44, [1000], 384),          # R = 176 at D = 64: eleven row tiles, chunked
+    (1, 32, 8, 128, 38, [800], None),         # R = 152: ten row tiles, the last one half filled
+    (1, 8, 2, 128, 9, [1500], None),          # six context splits: a merge batch of 8 with two masked
 ]
 
 

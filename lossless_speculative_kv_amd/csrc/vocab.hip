@@ -11,7 +11,8 @@
 //
 // Two kernels share the epilogue:
 //  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
-//    rows; W goes straight from HBM to registers, h (bf16, tiny) from L2.
+//    rows; W goes straight from HBM to registers, h (tiny) from L2: fp32
+//    rounded to bf16 in registers for one m-tile, else the bf16 copy.
 //    A workgroup of 8 waves fills a CU and its waves are paced.
 //  * vocab_staged: any M. Each wave owns 32 vocab rows and all M rows; the
 //    hidden rows are staged in LDS in 32-wide k chunks (double-buffered) and
@@ -144,9 +145,19 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
     wok[a] = v < P.V;
     wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K + 8 * qg;
   }
-  const uint16_t* hrow[MS];
+  // With one m-tile the hidden rows are read as fp32 (L2 hits: every wave
+  // reads them) and rounded to bf16 (nearest even) in registers; a row past
+  // M reads row M - 1 and only feeds keys and logits that are never written.
+  // Two m-tiles read the bf16 copy (the fp32 registers would spill).
+  constexpr bool kRound = MS == 1;
+  using HRaw = std::conditional_t<kRound, f32x4[MS][4][2], u32x4[MS][4]>;
+  const float* hrow[MS];
+  const uint16_t* hrow16[MS];
 #pragma unroll
-  for (int t = 0; t < MS; ++t) hrow[t] = P.hb + (size_t)(16 * t + n) * P.K + 8 * qg;
+  for (int t = 0; t < MS; ++t) {
+    hrow[t] = P.h + (size_t)min(16 * t + n, P.M - 1) * P.K + 8 * qg;
+    hrow16[t] = P.hb + (size_t)(16 * t + n) * P.K + 8 * qg;
+  }
 
   // W k-steps of 128 are double-buffered in registers: the loads of step
   // i + 1 are in flight while step i is multiplied. Every W load is
@@ -162,11 +173,35 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) A[a][kk] = *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk);
   };
-  auto load_h = [&](u32x4 (&B)[MS][4], int k0) {
+  auto load_h = [&](HRaw& H, int k0) {
 #pragma unroll
     for (int t = 0; t < MS; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) B[t][kk] = *reinterpret_cast<const u32x4*>(hrow[t] + k0 + 32 * kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        if constexpr (kRound) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            H[t][kk][j] = *reinterpret_cast<const f32x4*>(hrow[t] + k0 + 32 * kk + 4 * j);
+        } else {
+          H[t][kk] = *reinterpret_cast<const u32x4*>(hrow16[t] + k0 + 32 * kk);
+        }
+      }
+  };
+  auto to_bf16 = [&](const HRaw& H, u32x4 (&B)[MS][4]) {
+#pragma unroll
+    for (int t = 0; t < MS; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if constexpr (kRound) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            B[t][kk][2 * j] = f32_to_bf16_bits(H[t][kk][j][0]) | (f32_to_bf16_bits(H[t][kk][j][1]) << 16);
+            B[t][kk][2 * j + 1] = f32_to_bf16_bits(H[t][kk][j][2]) | (f32_to_bf16_bits(H[t][kk][j][3]) << 16);
+          }
+        } else {
+          B[t][kk] = H[t][kk];
+        }
+      }
   };
   auto compute = [&](const u32x4 (&A)[NA][4], const u32x4 (&B)[MS][4]) {
 #pragma unroll
@@ -177,22 +212,31 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
         for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B[t][kk], acc[a][t]);
   };
   u32x4 Aa[NA][4], Ab[NA][4], B[MS][4];
+  HRaw H;
   // a wave past the last vocab row has nothing to stream (and must not lead
   // the pacing)
   if (vbase < P.V) {
     load(Aa, 0);
     int k0 = 0;
+    // (the scheduling barriers keep the W loads issued before the hidden
+    // values are converted: the scheduler would otherwise sink them past
+    // the wait for the hidden loads)
     for (; k0 + 256 <= P.K; k0 += 256) {
-      load_h(B, k0);
+      load_h(H, k0);
       load(Ab, k0 + 128);
+      __builtin_amdgcn_sched_barrier(0);
       pace_waves<kStreamWaves>(prog_lds, wave, k0 >> 8);
+      to_bf16(H, B);
       compute(Aa, B);
-      load_h(B, k0 + 128);
+      load_h(H, k0 + 128);
       if (k0 + 256 < P.K) load(Aa, k0 + 256);
+      __builtin_amdgcn_sched_barrier(0);
+      to_bf16(H, B);
       compute(Ab, B);
     }
     if (k0 < P.K) {  // K / 128 odd: the last step's W is already loaded
-      load_h(B, k0);
+      load_h(H, k0);
+      to_bf16(H, B);
       compute(Aa, B);
     }
   }
@@ -594,15 +638,19 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
   hipEvent_t mstart = main_only ? tm.start : nullptr, mstop = main_only ? tm.stop : nullptr;
-  {
+  // the stream kernel with one m-tile rounds the hidden rows itself; the
+  // others read the bf16 copy
+  const bool convert = !plan.stream || plan.ms != 1;
+  if (convert) {
     const size_t n = (size_t)plan.Mp * K;
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     launch_ev(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, main_only ? nullptr : tm.start, nullptr, P);
   }
   if (plan.stream) {
     const dim3 block(64 * kStreamWaves);
-    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, mstart, mstop, P);
-    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, mstart, mstop, P);
+    hipEvent_t start = (main_only || convert) ? mstart : tm.start;
+    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
+    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
   } else if (plan.tiled) {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);

@@ -326,7 +326,7 @@ def test_verify_parity(L, case):
 TILED_FAULT = ("a tiled vocab kernel made the GPU report an illegal memory access on this shape (M = 33, "
                "three row tiles), also after a fix; its path is switched off and the case stays off the GPU "
                "until the cause is found")
-VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096),
+VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097), (20, 512, 3000),
                pytest.param((33, 1024, 5000), marks=pytest.mark.skip(reason=TILED_FAULT)), (264, 4096, 8192),
                (416, 1024, 3001), (164, 512, 2048)]
 

@@ -199,10 +199,7 @@ vc_status vc_verify_attn(const vc_attn_shape *shape, int32_t n_rows, const void 
  * argmax [m_rows]: first index of the largest fp32 logit (-0 == +0).
  * max_logit [m_rows] (optional, may be NULL): that logit.
  * logits [m_rows][vocab] (optional, may be NULL): all logits.
- * hidden must be a multiple of 128; m_rows <= 448; vocab < 2^31.
- * The workspace holds a completion counter that must be zero before the first
- * call and that every call leaves at zero: a workspace is zeroed once and then
- * reused. Calls that share a workspace must not run concurrently. */
+ * hidden must be a multiple of 128; m_rows <= 448; vocab < 2^31. */
 vc_status vc_vocab_workspace_bytes(int32_t m_rows, int32_t hidden, int32_t vocab, size_t *bytes);
 vc_status vc_vocab_logits(int32_t m_rows, int32_t hidden, int32_t vocab, const float *h, const void *w,
                           int32_t *argmax, float *max_logit, float *logits, void *ws, size_t ws_bytes,

@@ -22,9 +22,8 @@
 //    multiplied.
 // Argmax: each workgroup reduces (logit, index) to one 64-bit key per row,
 // key = ordered(logit) << 32 | ~index, whose maximum is the largest logit with
-// the lowest index (-0 is folded to +0). The max over workgroups is taken by
-// the last workgroup of the stream kernel to finish, and by a second kernel
-// after the staged kernel. The result does not depend on scheduling.
+// the lowest index (-0 is folded to +0); a second kernel takes the max over
+// workgroups. The result does not depend on scheduling.
 #include "vc_internal.h"
 
 namespace vc {
@@ -36,7 +35,6 @@ struct VocabParams {
   uint16_t* hb;       // bf16 [Mp][K] (workspace)
   const uint16_t* w;  // bf16 [V][K]
   uint64_t* keys;     // [nwg][M] (workspace)
-  uint32_t* done;     // workgroups of the stream kernel finished (workspace, zero between calls)
   int32_t* argmax;    // [M]
   float* max_logit;   // [M] or null
   float* logits;      // [M][V] or null
@@ -119,71 +117,10 @@ __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc
   }
 }
 
-constexpr int kStreamWaves = 8;  // waves per stream-kernel workgroup
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)x, off), hi = __shfl_xor((uint32_t)(x >> 32), off);
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    x = y > x ? y : x;
-  }
-  return x;
-}
-
-// End of the stream kernel, after its keys are stored: the workgroup waits
-// for its key stores, counts itself in, and the last one to do so reduces
-// the keys of all workgroups (device-coherent loads; wave w takes rows w,
-// w + 8, ..., its lanes the workgroups), writes argmax / max logit and sets
-// the count back to zero for the next call. Every load reads a clamped,
-// valid slot (duplicates do not change a maximum).
-template <int MS>
-__device__ __forceinline__ void stream_finish(const VocabParams& P, int lane, int wave) {
-  constexpr int RMAX = 16 * MS;
-  constexpr int RW = (RMAX + kStreamWaves - 1) / kStreamWaves;  // rows per wave
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's key stores have completed
-  __shared__ int last;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(P.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-  __syncthreads();
-  if (!last) return;
-  uint64_t best[RW];
-#pragma unroll
-  for (int i = 0; i < RW; ++i) best[i] = 0;
-  constexpr int GL = 4;  // workgroups per lane whose keys are loaded together
-  for (int g0 = 0; g0 < P.nwg; g0 += 64 * GL) {
-    uint64_t x[RW][GL];
-#pragma unroll
-    for (int i = 0; i < RW; ++i)
-#pragma unroll
-      for (int j = 0; j < GL; ++j) {
-        const int g = min(g0 + 64 * j + lane, P.nwg - 1), m = min(wave + kStreamWaves * i, P.M - 1);
-        x[i][j] = __hip_atomic_load(&P.keys[(size_t)g * P.M + m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      uint64_t k = x[i][0];
-#pragma unroll
-      for (int j = 1; j < GL; ++j) k = x[i][j] > k ? x[i][j] : k;
-      k = wave_max_u64(k);
-      best[i] = k > best[i] ? k : best[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int m = wave + kStreamWaves * i;
-    if (lane == 0 && m < P.M) {
-      P.argmax[m] = key_index(best[i]);
-      if (P.max_logit) P.max_logit[m] = key_value(best[i]);
-    }
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(P.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Stream kernel: 8 waves x 64 vocab rows. Its registers hold two waves per
 // SIMD, so a workgroup fills a CU (a CU with two workgroups would serve the
 // older first and finish the younger late) and the waves are paced.
+constexpr int kStreamWaves = 8;
 
 template <int MS>
 __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(const VocabParams P) {
@@ -317,9 +254,8 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
     uint64_t k = red[0][m];
 #pragma unroll
     for (int w = 1; w < kStreamWaves; ++w) k = red[w][m] > k ? red[w][m] : k;
-    __hip_atomic_store(&P.keys[(size_t)blockIdx.x * P.M + m], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
   }
-  stream_finish<MS>(P, lane, wave);
 }
 
 // Staged kernel: 8 waves x 32 vocab rows; all m-tiles (NMT >= ceil(M/16)).
@@ -680,7 +616,7 @@ int vocab_max_rows() { return 28 * 16; }
 
 size_t vocab_ws_bytes(int M, int K, int V) {
   const VocabPlan p = vocab_plan(M, K, V);
-  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256) + 256;
+  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256);
 }
 
 vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32_t* argmax, float* max_logit,
@@ -690,7 +626,6 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.h = h;
   P.hb = static_cast<uint16_t*>(ws);
   P.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256));
-  P.done = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(P.keys) + align_up((size_t)plan.nwg * M * 8, 256));
   P.w = static_cast<const uint16_t*>(w);
   P.argmax = argmax;
   P.max_logit = max_logit;
@@ -713,11 +648,9 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   }
   if (plan.stream) {
     const dim3 block(64 * kStreamWaves);
-    // the argmax reduce is the kernel's own last workgroup
-    hipEvent_t start = (main_only || convert) ? mstart : tm.start, stop = main_only ? mstop : tm.stop;
-    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, start, stop, P);
-    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, start, stop, P);
-    return check_launch("vocab projection");
+    hipEvent_t start = (main_only || convert) ? mstart : tm.start;
+    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
+    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
   } else if (plan.tiled) {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);

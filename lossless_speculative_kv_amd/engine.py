@@ -128,9 +128,8 @@ class Engine:
         self.ws_draft = self._ws(L.vc_draft_workspace_bytes(sh, self.kv)).zero_()
         max_chunk = c.chunk if c.staged else self.full_cap
         self.ws_verify = self._ws(L.vc_verify_workspace_bytes(sh, k + 1, max_chunk))
-        # the vocab workspaces hold a completion counter, zero between calls
-        self.ws_vocab_d = self._ws(L.vc_vocab_workspace_bytes(B, c.hidden, c.vocab)).zero_()
-        self.ws_vocab_v = self._ws(L.vc_vocab_workspace_bytes((k + 1) * B, c.hidden, c.vocab)).zero_()
+        self.ws_vocab_d = self._ws(L.vc_vocab_workspace_bytes(B, c.hidden, c.vocab))
+        self.ws_vocab_v = self._ws(L.vc_vocab_workspace_bytes((k + 1) * B, c.hidden, c.vocab))
         self.ws_commit = self._ws(L.vc_commit_workspace_bytes(sh))
 
     # ---------------------------------------------------------------- setup

@@ -346,15 +346,13 @@ def test_vocab_parity(L, case):
     am = torch.full((M,), -1, dtype=torch.int32, device="cuda")
     ml = torch.zeros((M,), dtype=torch.float32, device="cuda")
     lg = torch.zeros((M, V), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(L.vc_vocab_workspace_bytes(M, K, V), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(L.vc_vocab_workspace_bytes(M, K, V), dtype=torch.uint8, device="cuda")
     L.vc_vocab_logits(M, K, V, dh.data_ptr(), dW.data_ptr(), am.data_ptr(), ml.data_ptr(), lg.data_ptr(),
                       ws.data_ptr(), ws.numel(), stream())
     am2 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
     L.vc_vocab_logits(M, K, V, dh.data_ptr(), dW.data_ptr(), am2.data_ptr(), None, None, ws.data_ptr(), ws.numel(),
                       stream())
     torch.cuda.synchronize()
-    # the completion counter (the workspace's last 256 bytes) is back at zero
-    assert int(ws[-256:].sum().item()) == 0
     am, ml, lg, am2 = am.cpu().numpy(), ml.cpu().numpy(), lg.cpu().numpy(), am2.cpu().numpy()
     # argmax of the GPU's own fp32 logits (first index on ties): bit-exact
     assert np.array_equal(am, np.argmax(lg, axis=1))

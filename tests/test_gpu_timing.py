@@ -60,7 +60,7 @@ def test_vocab_call_records_events(L, M, K, V):
     dh = to_dev((rng.standard_normal((M, K)) * 0.05).astype(np.float32))
     dW = bf16_tensor(synth.w_vocab_rows(M, 0, V, K))
     am = torch.empty((M,), dtype=torch.int32, device="cuda")
-    ws = torch.zeros(L.vc_vocab_workspace_bytes(M, K, V), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(L.vc_vocab_workspace_bytes(M, K, V), dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     check_timed(L, lambda: L.vc_vocab_logits(M, K, V, dh.data_ptr(), dW.data_ptr(), am.data_ptr(), None, None,
                                              ws.data_ptr(), ws.numel(), s), "vocab")

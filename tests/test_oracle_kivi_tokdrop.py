@@ -56,6 +56,36 @@ def test_group_extremes_and_error_bound(bits):
     assert (np.abs(V - xh) <= bound).all()
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_key_roundtrip_error_bound(bits):
+    """Keys (per channel over 32 tokens, three-bit scales rounded up):
+    every dequantised key is within half a step of the original, plus the
+    fp16 rounding of the zero point, on groups with distinct ranges per
+    channel (a scale or zero taken from the wrong channel or group, or a
+    dequantisation that tiles instead of repeating the group parameters,
+    breaks the bound); the scale is the exact step rounded up by less than a
+    quarter, and the group minimum maps to code 0."""
+    rng = np.random.default_rng(30 + bits)
+    T, D = 128, 64
+    spread = np.exp(rng.uniform(-3, 3, size=(T // 32, 1, D)))
+    centre = rng.standard_normal((T // 32, 1, D)) * 4
+    K = (rng.standard_normal((T // 32, 32, D)) * spread + centre).reshape(T, D)
+    codes, scale, zero = quantize_keys(K, bits)
+    qmax = (1 << bits) - 1
+    assert codes.min() >= 0 and codes.max() <= qmax
+    g = K.reshape(T // 32, 32, D)
+    mn, mx = g.min(axis=1), g.max(axis=1)
+    s_exact = (mx - mn) / qmax
+    assert (scale >= s_exact).all() and (scale < 1.25 * s_exact).all()
+    c = codes.reshape(T // 32, 32, D)
+    assert (np.take_along_axis(c, g.argmin(axis=1)[:, None, :], axis=1) == 0).all()
+    xh = dequantize_keys(codes, scale, zero)
+    bound = np.repeat(scale / 2 + np.abs(zero - mn), 32, axis=0) + 1e-12
+    assert (np.abs(K - xh) <= bound).all()
+    # the bound is tight enough to matter: the steps span six octaves
+    assert np.abs(K - xh).max() > 0.25 * np.repeat(scale, 32, axis=0).min()
+
+
 def test_key_grouping_is_per_channel_over_32_tokens():
     K = np.zeros((64, 4))
     K[:32, 1] = np.linspace(0, 3, 32)      # channel 1, first group: range 3

@@ -82,3 +82,27 @@ def test_wrong_gqa_mapping_is_caught(monkeypatch):
         return o, hid[0], lg[0], int(np.argmax(lg[0]))
     monkeypatch.setattr(oracle.model.SequenceState, "draft_step", bad_draft)
     assert _fails(tr.test_identity_compressor_accepts_everything, "dense", {})
+
+
+def test_flushing_the_newest_rows_is_caught(monkeypatch):
+    def bad_flush(self):
+        R, G = self.cfg.residual, oracle.kivi.GROUP
+        while self.tail_k.shape[1] >= R + G:
+            for h in range(self.cfg.n_kv_heads):
+                blk = self._quantize_block(h, self.tail_k[h, -G:], self.tail_v[h, -G:])
+                bd = self.body[h]
+                for key in ("kc", "ks", "kz", "vc", "vs", "vz"):
+                    bd[key] = np.concatenate([bd[key], blk[key]])
+            self.tail_k = self.tail_k[:, :-G]
+            self.tail_v = self.tail_v[:, :-G]
+    monkeypatch.setattr(oracle.model.SequenceState, "flush", bad_flush)
+    assert _fails(tr.test_kivi_flush_quantises_the_oldest_tail_rows)
+
+
+def test_key_dequantisation_with_tiled_parameters_is_caught(monkeypatch):
+    def bad(codes, scale, zero):
+        n = np.asarray(codes).shape[0] // oracle.kivi.GROUP
+        return (np.asarray(codes, np.float64) * np.tile(np.asarray(scale), (oracle.kivi.GROUP, 1))[:n * 32]
+                + np.tile(np.asarray(zero), (oracle.kivi.GROUP, 1))[:n * 32])
+    monkeypatch.setattr(tk, "dequantize_keys", bad)
+    assert _fails(tk.test_key_roundtrip_error_bound, 2)

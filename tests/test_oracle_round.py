@@ -12,6 +12,7 @@
 import numpy as np
 import pytest
 
+from oracle import quantize_keys, quantize_values
 from oracle.model import ModelConfig, full_kv_greedy, make_states
 
 
@@ -59,6 +60,72 @@ def test_lossless_stream_equals_full_cache_greedy(kind, bits, keep, seed):
     for b in range(cfg.batch):
         stream = [int(t) for r in res[b] for t in r["committed"] if t >= 0]
         assert stream == full_kv_greedy(cfg, b, len(stream), model)
+
+
+def kivi_cache_is_quantised_prefix(cfg, st):
+    """The KIVI draft cache of a sequence, at a round boundary, is the
+    quantisation of the oldest body_len committed rows (32-token key groups,
+    per-token value groups) followed by the remaining committed rows,
+    unquantised, as the tail. Compared with the full cache, which the oracle
+    grows on its own (the embedding of each committed token)."""
+    n_body = st.body_len()
+    n_ctx = st.k_full.shape[1]
+    assert st.tail_k.shape[1] == n_ctx - n_body
+    for h in range(cfg.n_kv_heads):
+        kc, ks, kz = quantize_keys(st.k_full[h, :n_body], cfg.bits)
+        vc, vs, vz = quantize_values(st.v_full[h, :n_body], cfg.bits)
+        bd = st.body[h]
+        for got, want in zip((bd["kc"], bd["ks"], bd["kz"], bd["vc"], bd["vs"], bd["vz"]), (kc, ks, kz, vc, vs, vz)):
+            assert np.array_equal(got, want)
+        assert np.array_equal(st.tail_k[h], st.k_full[h, n_body:])
+        assert np.array_equal(st.tail_v[h], st.v_full[h, n_body:])
+
+
+def test_kivi_flush_quantises_the_oldest_tail_rows():
+    """Drafts from full-cache greedy decoding are all accepted, so each round
+    commits k + 1 tokens and the tail (R + k + 1 rows) crosses the flush
+    threshold R + 32: the flushed block must be the oldest 32 tail rows (the
+    residual of the previous round boundary), the tail keeps the rest in
+    order. Checked against the quantised-prefix invariant and, directly,
+    against the rows that were oldest before the round."""
+    cfg = small_cfg(kind="kivi", bits=2, k=40, residual=32, batch=1, context=96)
+    model, states = make_states(cfg)
+    st = states[0]
+    ref = full_kv_greedy(cfg, 0, 3 * (cfg.k + 1), model)
+    kivi_cache_is_quantised_prefix(cfg, st)
+    pos = 0
+    for _ in range(3):
+        body0, tail0 = st.body_len(), st.tail_k.shape[1]
+        oldest_k = st.tail_k[:, :32].copy()
+        oldest_v = st.tail_v[:, :32].copy()
+        r = st.run_round(forced_drafts=ref[pos:pos + cfg.k])
+        pos += cfg.k + 1
+        assert r["m"] == cfg.k
+        n_tail = tail0 + cfg.k + 1
+        nf = (n_tail - cfg.residual) // 32
+        assert nf >= 1
+        assert st.body_len() == body0 + 32 * nf
+        assert st.tail_k.shape[1] == n_tail - 32 * nf
+        assert cfg.residual <= st.tail_k.shape[1] < cfg.residual + 32
+        for h in range(cfg.n_kv_heads):
+            kc, ks, kz = quantize_keys(oldest_k[h], cfg.bits)
+            vc, vs, vz = quantize_values(oldest_v[h], cfg.bits)
+            bd = st.body[h]
+            sl = slice(body0, body0 + 32)
+            assert np.array_equal(bd["kc"][sl], kc) and np.array_equal(bd["vc"][sl], vc)
+            assert np.array_equal(bd["ks"][body0 // 32], ks[0]) and np.array_equal(bd["kz"][body0 // 32], kz[0])
+            assert np.array_equal(bd["vs"][sl], vs) and np.array_equal(bd["vz"][sl], vz)
+        kivi_cache_is_quantised_prefix(cfg, st)
+
+
+@pytest.mark.parametrize("bits,seed", [(2, 21), (4, 22)])
+def test_kivi_cache_stays_a_quantised_prefix(bits, seed):
+    """Unforced rounds (any accept lengths): the invariant holds at every
+    round boundary, flush or not."""
+    cfg = small_cfg(kind="kivi", bits=bits, k=20, residual=32, seed=seed)
+    model, states, res = run(cfg, 4)
+    for st in states:
+        kivi_cache_is_quantised_prefix(cfg, st)
 
 
 def test_kivi_flush_moves_tail_into_body():

@@ -89,10 +89,22 @@ typedef struct {
  *   groups of 32 tokens, values per token over groups of 32 channels, each
  *   group with an fp16 scale and zero point (x = code * scale + zero). The
  *   tail holds the most recent tokens unquantised, as fp16. body_len[b] must
- *   be a multiple of 32. Stored layout: the body is block-major, one record
- *   of BLK = 8 * D * (bits + 1) bytes (vc_kivi_block_bytes) per 32-token
- *   block, kivi_blocks [u][body_cap/32][BLK] with u = b * n_kv_heads + h, so
- *   that a block is one contiguous read. A record holds, at byte offsets:
+ *   be a multiple of 32.
+ *   Key scales: the kernel multiplies each query value (taken as fp16, exact
+ *   for bf16 values of magnitude 2^-17 .. 65504) by the key scale of its
+ *   channel in fp16. A key scale with at most three significant bits (what
+ *   vc_kivi_quantize writes) makes that product exact, and the result is then
+ *   within the attention tolerance of exact attention over the dequantised
+ *   cache. Any other finite fp16 key scale is accepted, but each product is
+ *   rounded to fp16: a score s_t = q . k_t / sqrt(D) gains an error of at most
+ *   eps_t = sum_d (2^-11 |q_d scale_d| + 2^-25) code_td / sqrt(D), and each
+ *   output channel d moves by at most (exp(2 eps) - 1) sum_t p_t |v_td - o_d|
+ *   more (eps the largest eps_t of the row, p the exact softmax weights, o the
+ *   exact output).
+ *   Stored layout: the body is block-major, one record of
+ *   BLK = 8 * D * (bits + 1) bytes (vc_kivi_block_bytes) per 32-token block,
+ *   kivi_blocks [u][body_cap/32][BLK] with u = b * n_kv_heads + h, so that a
+ *   block is one contiguous read. A record holds, at byte offsets:
  *     0          key codes uint32 [32][D*bits/32]: token-major; channel d of
  *                a token in word floor(d*bits/32) at bit (d*bits) % 32, LSB
  *                first.

@@ -17,7 +17,7 @@ stream equals full-cache greedy decoding). Parity unpinned: nothing here
 has absolute throughput or acceptance values to check against, because
 the pages print none.
 """
-from .attention import attend, attend_masked
+from .attention import attend, attend_masked, attend_prefix
 from .kivi import (quantize_keys, quantize_values, dequantize_keys, dequantize_values,
                    pack_key_codes, pack_value_codes, pack_value_side, unpack_key_codes,
                    unpack_value_codes, unpack_value_side, fp16_round, value_slot_token, pack_blocks,
@@ -27,7 +27,7 @@ from .vocab import to_bf16, logits, argmax_first, tie_bound
 from .accept import greedy_accept
 
 __all__ = [
-    "attend", "attend_masked", "quantize_keys", "quantize_values", "dequantize_keys",
+    "attend", "attend_masked", "attend_prefix", "quantize_keys", "quantize_values", "dequantize_keys",
     "dequantize_values", "pack_key_codes", "pack_value_codes", "pack_value_side",
     "unpack_key_codes", "unpack_value_codes", "unpack_value_side", "fp16_round", "pack_blocks", "unpack_blocks",
     "record_bytes", "record_offsets",

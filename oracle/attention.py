@@ -40,3 +40,26 @@ def attend_masked(Q, K, V, visible) -> np.ndarray:
         sel = np.asarray(visible[r], dtype=bool)
         out[r] = attend(Q[r], np.asarray(K)[sel], np.asarray(V)[sel])
     return out
+
+
+def attend_prefix(Q, K, V, n_visible) -> np.ndarray:
+    """Row-wise attention where row r sees the first n_visible[r] tokens of
+    K, V (1 <= n_visible[r] <= T): the verification rows of a draft block see
+    the whole context plus the block rows up to their own (VeriCache summary,
+    "Core algorithm": one pass checks all drafted tokens). The same
+    definition as ``attend`` per row, written with matrices: scores
+    Q K^T / sqrt(D), the invisible ones excluded, softmax per row, times V.
+
+    Q: [R][D]; K, V: [T][D]; n_visible: [R] ints.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    n_visible = np.asarray(n_visible)
+    if (n_visible < 1).any() or (n_visible > K.shape[0]).any():
+        raise ValueError("every row must see between 1 and T tokens")
+    S = (Q @ K.T) / np.sqrt(Q.shape[1])
+    visible = np.arange(K.shape[0])[None, :] < n_visible[:, None]
+    S = np.where(visible, S, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    return (P @ V) / P.sum(axis=1, keepdims=True)

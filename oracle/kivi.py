@@ -62,8 +62,12 @@ def _quantize_groups(x, bits: int, axis: int, key_scale: bool = False):
     return codes.astype(np.int64), scale, zero
 
 
-def quantize_keys(K, bits: int):
+def quantize_keys(K, bits: int, three_bit_scale: bool = True):
     """K: [T][D] with T a multiple of 32. Per-channel groups of 32 tokens.
+
+    three_bit_scale=False takes the value rule for the scale instead (fp16
+    nearest of (max - min) / (2^b - 1)): the plain min/max quantiser, used to
+    build caches whose key scales the draft kernel cannot fold exactly.
 
     Returns codes int [T][D], scale [T/32][D], zero [T/32][D] (fp16 values).
     """
@@ -72,7 +76,7 @@ def quantize_keys(K, bits: int):
     if T % GROUP:
         raise ValueError("key token count must be a multiple of 32")
     g = K.reshape(T // GROUP, GROUP, D)
-    codes, scale, zero = _quantize_groups(g, bits, axis=1, key_scale=True)
+    codes, scale, zero = _quantize_groups(g, bits, axis=1, key_scale=three_bit_scale)
     return codes.reshape(T, D), scale[:, 0, :], zero[:, 0, :]
 
 

@@ -7,8 +7,9 @@ kernels. The oracle computes sampled outputs one by one:
   oracle quantiser applied to the GPU's own full-cache rows;
 * draft attention of every query head of those KV heads against fp64
   attention over the dequantised body and the fp16 tail;
-* verification attention of sampled (sequence, head, draft row) triples over
-  the full context plus the causal draft block;
+* verification attention of every row of two whole (sequence, KV head)
+  units, and sampled rows of a third, over the full context plus the causal
+  draft block;
 * the draft-step argmax of every sequence against fp64 logits (exact except
   within the near-tie bound).
 Tolerances as in the kernel tests: attention max |d| <= 1e-2 and rel-L2 <=
@@ -19,7 +20,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from tests.gpu_util import assert_attention_close, log  # noqa: E402
+from tests.gpu_util import assert_attention_close, check_argmax_chunked, check_verify_unit, log  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -71,25 +72,31 @@ def test_records_and_draft_attention(eng):
 
 
 def test_verify_attention(eng):
+    """Every verification row of two whole KV-head units, then sampled rows of
+    a third."""
     c = eng.cfg
-    g = c.n_q_heads // c.n_kv_heads
     eng.embed_block()
     eng.verify_attention()
     torch.cuda.synchronize()
+    for b, hk in UNITS[:2]:
+        log(f"full size verify: whole unit (sequence {b}, KV head {hk}), {(c.k + 1) * (c.n_q_heads // c.n_kv_heads)} rows")
+        mad, rl2, worst = check_verify_unit(eng, b, hk)
+        log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e} (worst row {worst:.2e})")
+    g = c.n_q_heads // c.n_kv_heads
     ctx = eng.ctx_len.cpu().numpy()
     o = eng.o_ver.cpu().numpy()
-    for b, hk in UNITS:
-        n = int(ctx[b])
-        K = bf16_to_f64(eng.full_k[b, hk, :n])
-        V = bf16_to_f64(eng.full_v[b, hk, :n])
-        kn = bf16_to_f64(eng.kn[:, b, hk])
-        vn = bf16_to_f64(eng.vn[:, b, hk])
-        for j in (0, 17, c.k):
-            h = hk * g + (j % g)
-            log(f"full size verify: sequence {b} head {h} row {j}, context {n}")
-            Ka, Va = np.concatenate([K, kn[:j + 1]]), np.concatenate([V, vn[:j + 1]])
-            ref = oracle.attend(bf16_to_f64(eng.qv[j, b, h]), Ka, Va)
-            assert_attention_close(o[j, b, h], ref, f"verify ({b}, {h}, row {j})")
+    b, hk = UNITS[2]
+    n = int(ctx[b])
+    K = bf16_to_f64(eng.full_k[b, hk, :n])
+    V = bf16_to_f64(eng.full_v[b, hk, :n])
+    kn = bf16_to_f64(eng.kn[:, b, hk])
+    vn = bf16_to_f64(eng.vn[:, b, hk])
+    for j in (0, 17, c.k):
+        h = hk * g + (j % g)
+        log(f"full size verify: sequence {b} head {h} row {j}, context {n}")
+        Ka, Va = np.concatenate([K, kn[:j + 1]]), np.concatenate([V, vn[:j + 1]])
+        ref = oracle.attend(bf16_to_f64(eng.qv[j, b, h]), Ka, Va)
+        assert_attention_close(o[j, b, h], ref, f"verify ({b}, {h}, row {j})")
 
 
 def test_draft_vocab_argmax(eng):
@@ -97,24 +104,5 @@ def test_draft_vocab_argmax(eng):
     h = oracle.to_bf16(eng.o_draft.reshape(c.batch, -1).cpu().numpy())
     got = eng.xs[1].cpu().numpy()
     log(f"full size vocab: {c.batch} rows x {c.vocab} x {c.hidden}")
-    best = np.full(c.batch, -np.inf)
-    arg = np.zeros(c.batch, np.int64)
-    lg_got = np.zeros(c.batch)
-    step = 16384
-    for v0 in range(0, c.vocab, step):
-        Wc = eng.W[v0:v0 + step].float().cpu().numpy().astype(np.float64)
-        lg = oracle.logits(h, Wc)
-        am = oracle.argmax_first(lg)
-        m = lg[np.arange(c.batch), am]
-        upd = m > best
-        best[upd], arg[upd] = m[upd], am[upd] + v0
-        inside = (got >= v0) & (got < v0 + Wc.shape[0])
-        lg_got[inside] = lg[np.arange(c.batch)[inside], got[inside] - v0]
-    excused = 0
-    for b in range(c.batch):
-        if got[b] != arg[b]:
-            W2 = eng.W[int(arg[b])].float().cpu().numpy().astype(np.float64)[None, :]
-            bound = oracle.tie_bound(h[b:b + 1], W2, [0])[0]
-            assert best[b] - lg_got[b] <= bound, f"row {b}: gap {best[b] - lg_got[b]} > {bound}"
-            excused += 1
+    excused = check_argmax_chunked(eng.W, h, got)
     log(f"  near-tie excused rows: {excused}/{c.batch}")

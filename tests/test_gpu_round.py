@@ -71,7 +71,24 @@ def ref_tie(model, o_gpu_row, o_ref_row, tok_gpu, what):
     return 1
 
 
-def run_case(configs, engine, cfg, rounds):
+def check_kivi_records(eng, states, cfg, what):
+    """The GPU's body records, byte for byte, against the oracle's body
+    (quantised by the oracle from its own fp64 rows) in the stored layout."""
+    blocks = eng.kivi_blocks.cpu().numpy()
+    for b, st in enumerate(states):
+        nb = st.body_len()
+        for h in range(cfg.n_kv_heads):
+            bd = st.body[h]
+            want = oracle.pack_blocks(bd["kc"], bd["ks"], bd["kz"], bd["vc"], bd["vs"], bd["vz"], cfg.bits)
+            assert np.array_equal(blocks[b, h, :nb // 32], want), f"{what}: records of ({b}, {h})"
+
+
+def run_case(configs, engine, cfg, rounds, forced=False):
+    """forced: after each draft step is checked, the drafted token is replaced
+    by the full-cache greedy token (teacher forcing as in the oracle's
+    run_round(forced_drafts=...)), so every round accepts all k drafts unless
+    verification meets a near-tie; the KIVI tail then crosses R + 32 and the
+    residual flush runs."""
     eng = engine.Engine(cfg, rounds_cap=rounds)
     ocfg = oracle_cfg(cfg)
     model = SynthModel(ocfg)
@@ -79,10 +96,13 @@ def run_case(configs, engine, cfg, rounds):
     k, B = cfg.k, cfg.batch
     excused = 0
     streams = [[] for _ in range(B)]
+    greedy = [full_kv_greedy(ocfg, b, rounds * (k + 1), model) for b in range(B)] if forced else None
     hist = []  # per round: draft hiddens [k][B], verify hiddens [k+1][B], references, tokens
+    flush_total = 0
     for r in range(rounds):
         log(f"{cfg.name} round {r}")
         tail_start = [st.tail_k.shape[1] for st in states]
+        body_before = [int(x) for x in eng.body_len.cpu().numpy()]
         rec = {"draft": [], "draft_ref": []}
         eng.begin_round()
         for j in range(k):
@@ -96,6 +116,12 @@ def run_case(configs, engine, cfg, rounds):
                 assert_attention_close(o[b], o_ref, f"{cfg.name} r{r} draft step {j} seq {b}")
                 excused += check_token(model, o[b], int(xs[j + 1, b]), f"draft r{r} j{j} b{b}")
                 refs.append(o_ref)
+            if forced:
+                # force only while the committed stream follows full-cache greedy
+                # decoding (a near-tie in verification may part them)
+                row = [greedy[b][len(streams[b]) + j] if streams[b] == greedy[b][:len(streams[b])]
+                       else int(xs[j + 1, b]) for b in range(B)]
+                eng.xs[j + 1] = torch.tensor(row, dtype=torch.int32, device=eng.xs.device)
             rec["draft"].append(o.copy())
             rec["draft_ref"].append(refs)
         eng.embed_block()
@@ -130,6 +156,11 @@ def run_case(configs, engine, cfg, rounds):
         ctx = eng.ctx_len.cpu().numpy()
         tl = eng.tail_len.cpu().numpy()
         bl = eng.body_len.cpu().numpy()
+        if cfg.kind == "kivi":
+            check_kivi_records(eng, states, cfg, f"{cfg.name} r{r}")
+            flushes = [int(bl[b]) - body_before[b] for b in range(B)]
+            log(f"  body growth {flushes}")
+            flush_total += sum(flushes)
         for b, st in enumerate(states):
             assert ctx[b] == st.k_full.shape[1]
             if cfg.kind != "dense":
@@ -139,6 +170,7 @@ def run_case(configs, engine, cfg, rounds):
             if cfg.kind == "dense":
                 assert bl[b] == ctx[b] and tl[b] == 0
         log(f"  accept lengths {na.tolist()}")
+    eng.flushed_tokens = flush_total
     return eng, states, streams, excused, model, hist
 
 
@@ -179,6 +211,8 @@ ROUND_CASES = {
                   bits=4, residual=32, seed=11),
     "kivi2-flush": dict(batch=2, n_q_heads=16, n_kv_heads=4, head_dim=128, context=512, vocab=2048, k=40,
                         kind="kivi", bits=2, residual=32, outliers=True, seed=12),
+    "kivi4-flush-d64": dict(batch=3, n_q_heads=8, n_kv_heads=4, head_dim=64, context=320, vocab=1024, k=20,
+                            kind="kivi", bits=4, residual=64, seed=16),
     "tokdrop": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, context=1024, vocab=1024, k=5,
                     kind="tokdrop", keep=0.25, seed=13),
     "dense": dict(batch=2, n_q_heads=8, n_kv_heads=4, head_dim=64, context=300, vocab=512, k=7, kind="dense",
@@ -188,12 +222,21 @@ ROUND_CASES = {
 }
 
 
+# cases whose drafts are forced to the full-cache greedy tokens: every round
+# accepts all k, so the KIVI tail crosses R + 32 and flushes each round
+FORCED = {"kivi2-flush", "kivi4-flush-d64"}
+
+
 @pytest.mark.parametrize("name", list(ROUND_CASES))
 def test_round_teacher_forced(eng_mod, name):
     configs, engine = eng_mod
     cfg = configs.RoundConfig(name=f"round-{name}", **ROUND_CASES[name])
     rounds = 3
-    eng, states, streams, excused, model, hist = run_case(configs, engine, cfg, rounds)
+    forced = name in FORCED
+    eng, states, streams, excused, model, hist = run_case(configs, engine, cfg, rounds, forced=forced)
+    if forced:
+        # at least one 32-token block per sequence joined the body over the rounds
+        assert eng.flushed_tokens >= 32 * cfg.batch, f"flushed {eng.flushed_tokens} tokens"
     log(f"  near-tie excused tokens: {excused}")
     if name == "dense":
         flips = check_dense_acceptance(eng, cfg, model, hist)

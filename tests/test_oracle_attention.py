@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, attend_masked
+from oracle import attend, attend_masked, attend_prefix
 
 
 def test_single_token_returns_its_value():
@@ -83,3 +83,22 @@ def test_masked_rows_match_torch_sdpa_with_causal_block():
         torch.tensor(Q)[None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None],
         attn_mask=torch.tensor(vis)[None, None])
     np.testing.assert_allclose(attend_masked(Q, K, V, vis), ref[0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_attention_matches_per_row_and_sdpa():
+    """attend_prefix against attend row by row (pinned above) and against the
+    library routine with the equivalent boolean mask; rows see ragged
+    prefixes, including a single token and every token."""
+    rng = np.random.default_rng(41)
+    R, T, D = 9, 37, 16
+    Q, K, V = rng.standard_normal((R, D)), rng.standard_normal((T, D)) * 2, rng.standard_normal((T, D))
+    nv = np.array([1, 5, 36, 37, 20, 2, 30, 37, 11])
+    got = attend_prefix(Q, K, V, nv)
+    for r in range(R):
+        np.testing.assert_allclose(got[r], attend(Q[r], K[:nv[r]], V[:nv[r]]), rtol=0, atol=1e-13)
+    mask = torch.from_numpy(np.arange(T)[None, :] < nv[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], attn_mask=mask[None])[0]
+    np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        attend_prefix(Q, K, V, np.zeros(R, int))

@@ -237,3 +237,21 @@ def test_key_scale_times_bf16_query_is_exact_in_fp16():
         normal = np.abs(prod) >= 2.0 ** -14
         assert normal.mean() > 0.9
         assert np.array_equal(fp16_round(prod[normal]), prod[normal])
+
+
+def test_plain_fp16_key_scale_rule():
+    """three_bit_scale=False: the key scale is the fp16 nearest of the exact
+    step, as for values (hand-worked: range 3 over 2 bits gives step 1.0; range
+    1.1 gives 0.36666..., whose fp16 nearest is 0.3667 = 751 * 2^-11), and the
+    codes are still the nearest levels, clamped."""
+    K = np.zeros((32, 2))
+    K[:, 0] = np.linspace(0, 3, 32)
+    K[:, 1] = np.linspace(-0.5, 0.6, 32)
+    codes, scale, zero = quantize_keys(K, 2, three_bit_scale=False)
+    assert scale[0, 0] == 1.0 and zero[0, 0] == 0.0
+    assert scale[0, 1] == 751 * 2.0 ** -11 and zero[0, 1] == -0.5
+    _, s3, _ = quantize_keys(K, 2)
+    assert s3[0, 1] == 0.375   # three significant bits, rounded up
+    for d in range(2):
+        u = (K[:, d] - zero[0, d]) / scale[0, d]
+        assert np.array_equal(codes[:, d], np.clip(np.rint(u), 0, 3))

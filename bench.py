@@ -5,27 +5,39 @@ k draft steps (embedding, draft decode attention over the compressed cache,
 vocab projection + argmax), the verification pass over the full cache (verify
 attention, vocab projection + argmax), greedy acceptance and commit (full
 cache append, tail rewrite, residual flush). Inputs are resident in HBM when
-the timed region starts.
+the timed region starts. The default workload is the Qwen-32B-shaped layer
+(B = 16, 40 q / 8 KV heads, context 65536, KIVI-2, k = 25), the largest whose
+full cache and compressed cache both live in HBM; the 1M-token Llama-70B
+layer (full cache in pinned host memory, staged over the host link) is
+measured after it as an extra block.
 
 metric (per decoder layer): accepted tokens per second per layer,
     value = sum over timed rounds and sequences of (m + 1)
             / (timed rounds * (k * t_draft_attn + t_verify_attn)),
-with t_draft_attn / t_verify_attn the average duration of a whole draft /
+with t_draft_attn / t_verify_attn the median duration of a whole draft /
 verification attention call (attention kernel + split merge), measured inside
 the timed region by HIP events that the calls' own kernel dispatches record
-(vc_time_next_call: no queue markers, so timing does not idle the GPU). A
-real model projects to the vocabulary once per token, not once per layer,
-so the vocab projection is outside the per-layer metric; the whole-round
-wall clock is reported as ms_per_step and round_tok_s.
+(vc_time_next_call: no queue markers, so timing does not idle the GPU); p10
+and p90 of the same formula are reported beside it. A real model projects to
+the vocabulary once per token, not once per layer, so the vocab projection is
+outside the per-layer metric; the whole-round wall clock is ms_per_step and
+round_tok_s.
+
+Comparator: full-KV decoding per layer, B / t(dense draft kernel over the
+whole committed context plus the new token), measured in the same run; the
+ratio value / comparator is reported, and the same time model at the pages'
+25 and 40 accepted tokens per round (derived figures).
 
 roofline: the draft decode attention kernel (the dominant term of the
 metric): algorithmic bytes per launch (compressed body + fp16 tail + q + out)
-over the kernel's own average duration (events around the attention kernel
+over the kernel's own median duration (events around the attention kernel
 alone, on alternate draft steps), against 8 TB/s; `traffic` is the HBM bytes
 per launch from the committed FETCH_SIZE / WRITE_SIZE measurement when the
 kernel source has not changed since. The same figures for the verification
 kernel are under verify_attn.
-cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload.
+cpu_baseline: the fp64 CPU oracle timed by the same formula (its draft-step
+and verification attention, on one sequence and one KV-head group, scaled
+by batch x KV heads).
 """
 from __future__ import annotations
 
@@ -47,7 +59,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3-8b-layer")
+    ap.add_argument("--workload", default="qwen-32b-layer")
+    ap.add_argument("--extra", default="llama-70b-layer-1m",
+                    help="comma-separated workloads measured after the main one (3 rounds each) and reported "
+                         "under extra_workloads; empty for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -138,11 +153,32 @@ def traffic_for(kernel, workload):
     return entry["fetch_bytes"] + entry["write_bytes"]
 
 
-def cpu_baseline(cfg, accepted_per_round, quiet):
-    """The CPU oracle (fp64 numpy) on a bounded sample: one sequence and one
-    KV-head group (its g query heads) of the same layer, one whole round
-    (k draft steps + verify + accept + commit), projected to the batch by
-    B * Hkv (attention work is linear in it)."""
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q)) if len(v) else 0.0
+
+
+def dist_us(v):
+    """Median, p10, p90 of a list of seconds, in microseconds."""
+    return {"median": pct(v, 50) * 1e6, "p10": pct(v, 10) * 1e6, "p90": pct(v, 90) * 1e6, "n": len(v)}
+
+
+def cpu_baseline(cfg, accepted_per_round, quiet, budget_s=18.0):
+    """The CPU oracle (fp64 numpy) timed by the metric's own formula.
+
+    On one sequence and one KV-head group of the layer (the g query heads of
+    KV head 0), the oracle's draft step (SequenceState.draft_step: tail
+    append, attention of the g heads over the dequantised body or kept rows
+    plus the tail) and its verification (SequenceState.verify: the round's
+    rows over the full context plus the causal block) are timed separately,
+    each scaled by B * Hkv (attention work is linear in it), and
+        value = accepted tokens per round / (k * t_draft + t_verify),
+    with the accepted tokens per round of the GPU run (identical by parity).
+    The sample's vocabulary has 256 entries, so the projection inside
+    draft_step / verify is negligible beside attention. A verification sample
+    that would exceed the budget covers the block's first r rows and is
+    scaled by (k + 1) / r (row j costs the context plus j + 1 block rows).
+    Median, p10 and p90 over repetitions."""
     import numpy as np
 
     from oracle.model import ModelConfig, make_states
@@ -151,36 +187,207 @@ def cpu_baseline(cfg, accepted_per_round, quiet):
         threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
-    g = cfg.group
+    g, k = cfg.group, cfg.k
     ocfg = ModelConfig(batch=1, n_q_heads=g, n_kv_heads=1, head_dim=cfg.head_dim, context=cfg.context,
-                       vocab=8192, k=cfg.k, kind=cfg.kind, bits=cfg.bits, residual=cfg.residual, keep=cfg.keep,
+                       vocab=256, k=k, kind=cfg.kind, bits=cfg.bits, residual=cfg.residual, keep=cfg.keep,
                        outliers=cfg.outliers, seed=cfg.seed)
     log("cpu baseline: building the oracle sample", quiet)
     _, states = make_states(ocfg)
-    # consecutive rounds of the sample until about 12 s of CPU work (at least
-    # one round, at most eight), averaged per round
+    st = states[0]
+    xs = [st.x0]
+    d_times = []
+    t_begin = time.perf_counter()
+    while len(d_times) < k and (len(d_times) < 2 or time.perf_counter() - t_begin < budget_s / 3):
+        t0 = time.perf_counter()
+        _, _, _, nxt = st.draft_step(xs[-1])
+        d_times.append(time.perf_counter() - t0)
+        xs.append(int(nxt))
+    while len(xs) < k + 1:
+        xs.append((xs[-1] * 7 + 1) % 256)   # tokens for the verification rows the sample did not draft
     t0 = time.perf_counter()
-    rounds = 0
-    while True:
-        states[0].run_round()
-        rounds += 1
-        spent = time.perf_counter() - t0
-        if spent >= 12.0 or rounds >= 8:
-            break
-    dt = spent / rounds
+    st.verify(xs[:1])
+    t_row = time.perf_counter() - t0
+    rows = int(max(1, min(k + 1, (budget_s * 2 / 3) / (3 * t_row * 1.05))))
+    v_times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        st.verify(xs[:rows])
+        v_times.append((time.perf_counter() - t0) * (k + 1) / rows)
+    spent = time.perf_counter() - t_begin
     scale = cfg.batch * cfg.n_kv_heads
-    projected = dt * scale
-    value = accepted_per_round / projected
-    log(f"cpu baseline: {rounds} sample rounds in {spent:.2f} s, projected round {projected:.1f} s", quiet)
+    td = np.array(d_times) * scale
+    tv = np.array(v_times) * scale
+
+    def val(a, b):
+        return accepted_per_round / (k * a + b)
+    value = val(pct(td, 50), pct(tv, 50))
+    log(f"cpu baseline: {len(d_times)} draft steps, {rows}-row verification x3 in {spent:.1f} s", quiet)
     return {
         "value": value, "unit": "accepted tok/s/layer", "cores": threads, "kind": "oracle",
-        "sample": (f"1 sequence x 1 KV-head group ({g} q heads) of the {cfg.name} shape, {rounds} consecutive whole "
-                   f"oracle rounds (each k={cfg.k} draft steps + verify + accept + commit, vocab 8192 x "
-                   f"{g * cfg.head_dim}) in {spent:.2f} s, {dt:.2f} s per round, scaled x{scale} (batch x KV heads) "
-                   f"to {projected:.1f} s per round; accepted tokens per round taken from the GPU run (identical by "
-                   f"parity)"),
-        "sample_seconds": spent, "sample_rounds": rounds, "host_cpus": os.cpu_count(),
+        "p10": val(pct(td, 90), pct(tv, 90)), "p90": val(pct(td, 10), pct(tv, 10)),
+        "sample": (f"the oracle's draft step (x{len(d_times)}) and verification ({rows} of {k + 1} rows, x3) on 1 "
+                   f"sequence x 1 KV-head group ({g} q heads) of the {cfg.name} shape (context {cfg.context}), "
+                   f"{spent:.1f} s of CPU work; each time scaled x{scale} (batch x KV heads) and, for "
+                   f"verification, x{(k + 1) / rows:.2f} (rows); value = accepted tokens per round of the GPU "
+                   f"run / (k * t_draft + t_verify), medians (p10/p90 from the slow/fast ends)"),
+        "t_draft_step_s": {"median": pct(td, 50), "p10": pct(td, 10), "p90": pct(td, 90)},
+        "t_verify_s": {"median": pct(tv, 50), "p10": pct(tv, 10), "p90": pct(tv, 90)},
+        "sample_seconds": spent, "host_cpus": os.cpu_count(),
     }
+
+
+def full_kv_decode(eng, n_calls=12):
+    """Full-KV decoding per layer, the comparator of the metric: the dense
+    (identity) draft kernel over each sequence's whole committed context plus
+    one new token, timed by the call's own dispatches. Returns (durations in
+    seconds, algorithmic bytes per launch)."""
+    import torch
+
+    from lossless_speculative_kv_amd import _lib as L
+    c = eng.cfg
+    B, Hq, Hkv, D = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim
+    kv = L.vc_draft_kv()
+    kv.kind, kv.body_cap, kv.tail_cap = L.VC_DRAFT_DENSE, eng.full_cap, 32
+    body = eng.ctx_len.clone()
+    tail = torch.ones((B,), dtype=torch.int32, device=eng.dev)
+    tk = torch.zeros((B, Hkv, 32, D), dtype=torch.bfloat16, device=eng.dev)
+    tv = torch.zeros_like(tk)
+    tk[:, :, 0] = eng.kn[0]
+    tv[:, :, 0] = eng.vn[0]
+    kv.body_len, kv.tail_len = body.data_ptr(), tail.data_ptr()
+    kv.src_k, kv.src_v, kv.src_t_cap = eng.full_k.data_ptr(), eng.full_v.data_ptr(), eng.full_cap
+    kv.tail_k, kv.tail_v = tk.data_ptr(), tv.data_ptr()
+    ws = torch.zeros(L.vc_draft_workspace_bytes(eng.shape, kv), dtype=torch.uint8, device=eng.dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=eng.dev)
+    s = eng.stream
+    ev = []
+    for _ in range(n_calls):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        b.record(s)
+        ev.append((a, b))
+    torch.cuda.synchronize(eng.dev)
+    for i in range(n_calls + 2):
+        if i >= 2:
+            a, b = ev[i - 2]
+            L.vc_time_next_call(a.cuda_event, b.cuda_event, L.VC_TIME_CALL)
+        L.vc_draft_decode_attn(eng.shape, eng.q_draft.data_ptr(), kv, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                               s.cuda_stream)
+    torch.cuda.synchronize(eng.dev)
+    times = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    ctx = eng.ctx_len.cpu().numpy()
+    nbytes = sum(Hkv * (int(ctx[b]) + 1) * 4 * D for b in range(B)) + B * Hq * D * 6
+    return times, nbytes
+
+
+def measure(cfg, steps, warmup, q, comparator=True):
+    """Warm-up rounds, then `steps` timed rounds of one workload; returns the
+    figures of the JSON line (without the CPU baseline)."""
+    import numpy as np
+    import torch
+
+    from lossless_speculative_kv_amd import engine
+
+    log(f"workload {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} D={cfg.head_dim} "
+        f"T={cfg.context} k={cfg.k} V={cfg.vocab} kind={cfg.kind}", q)
+    t_setup = time.perf_counter()
+    eng = engine.Engine(cfg, rounds_cap=warmup + steps)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s", q)
+    for _ in range(warmup):
+        eng.round()
+    torch.cuda.synchronize()
+    body0, tail0, ctx0 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
+    eng.prepare_timing(steps * (2 * cfg.k + 2) + 4)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.round()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"{steps} timed rounds in {wall * 1e3:.1f} ms", q)
+    body1, tail1, ctx1 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
+    ev = eng.events
+    eng.events = None
+
+    times = {}
+    for name, a, b in ev:
+        times.setdefault(name, []).append(a.elapsed_time(b) * 1e-3)
+    n_acc = eng.n_accept[warmup:warmup + steps].cpu().numpy()
+    accepted = float((n_acc + 1).sum())
+    acc_round = accepted / steps
+    # whole calls (attention kernel + split merge) were timed on even draft
+    # steps / even rounds, the attention kernel alone on odd ones; the events
+    # are recorded by the kernels' own dispatches (vc_time_next_call)
+    med = {name: pct(v, 50) for name, v in times.items()}
+    get = lambda name: med.get(name, 0.0)  # noqa: E731
+    t_draft, t_draft_main = get("draft_attn"), get("draft_attn_main")
+    t_verify, t_verify_main = get("verify_attn"), get("verify_attn_main")
+    k, B = cfg.k, cfg.batch
+    per_round = k * t_draft + t_verify
+    value = acc_round / per_round if per_round > 0 else 0.0
+    d10, d90 = pct(times.get("draft_attn", []), 10), pct(times.get("draft_attn", []), 90)
+    v10, v90 = pct(times.get("verify_attn", []), 10), pct(times.get("verify_attn", []), 90)
+
+    mid_body = [(int(a) + int(b)) / 2 for a, b in zip(body0, body1)]
+    mid_tail = [(int(a) + int(b)) / 2 + k / 2 for a, b in zip(tail0, tail1)]  # tail grows by 1 per draft step
+    mid_ctx = [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)]
+    draft_bytes = draft_bytes_per_launch(cfg, mid_body, mid_tail)
+    verify_bytes = verify_bytes_per_launch(cfg, mid_ctx)
+    draft_gbs = draft_bytes / t_draft_main / 1e9 if t_draft_main > 0 else 0.0
+    t_vmain = t_verify_main if t_verify_main > 0 else t_verify   # staged: whole chunked pass only
+    verify_gbs = verify_bytes / t_vmain / 1e9 if t_vmain > 0 else 0.0
+
+    # MFMA utilisation: algorithmic flops over the main kernel's own duration
+    mfma = {
+        "verify_attn": mfma_entry("verify_kernel", verify_flops_per_launch(cfg, mid_ctx), t_vmain),
+        "draft_vocab": mfma_entry("vocab product, M = batch", 2.0 * B * cfg.hidden * cfg.vocab, get("draft_vocab_main")),
+        "verify_vocab": mfma_entry("vocab product, M = (k+1) * batch", 2.0 * (k + 1) * B * cfg.hidden * cfg.vocab,
+                                   get("verify_vocab_main")),
+    }
+    w_bytes = 2.0 * cfg.hidden * cfg.vocab
+    for key in ("draft_vocab", "verify_vocab"):
+        t = mfma[key]["avg_launch_us"] * 1e-6
+        mfma[key]["weight_GBs"] = w_bytes / t / 1e9 if t > 0 else 0.0
+        mfma[key]["median_launch_us"] = mfma[key].pop("avg_launch_us")
+
+    # comparator: full-KV decoding per layer
+    if comparator and not cfg.staged:
+        d_times, d_bytes = full_kv_decode(eng)
+        t_full = pct(d_times, 50)
+        full = {"tok_s_layer": B / t_full, "t_call": dist_us(d_times), "kernel": "draft_rows_kernel (dense)",
+                "bytes_per_launch": d_bytes, "achieved_GBs": d_bytes / t_full / 1e9,
+                "frac": d_bytes / t_full / 1e9 / HBM_PEAK_GBS,
+                "definition": "B / t(dense draft attention over the committed context plus the new token)"}
+    elif comparator:
+        full = {"tok_s_layer": B / t_verify if t_verify > 0 else 0.0,
+                "definition": ("full cache in host memory: every decoded token needs a pass over it across the host "
+                               "link, as one verification pass does; B / t(verification pass, staged)")}
+    else:
+        full = None
+    what_if = {str(a): B * a / ((a - 1) * t_draft + t_verify) for a in (25, 40)}
+    ceiling = B * (k + 1) / per_round if per_round > 0 else 0.0
+    out = {
+        "cfg": cfg, "value": value, "ms_per_step": wall / steps * 1e3, "round_tok_s": accepted / wall,
+        "value_p10": acc_round / (k * d90 + v90) if d90 + v90 > 0 else 0.0,
+        "value_p90": acc_round / (k * d10 + v10) if d10 + v10 > 0 else 0.0,
+        "t_draft_call": dist_us(times.get("draft_attn", [])), "t_draft_kernel": dist_us(times.get("draft_attn_main", [])),
+        "t_verify_call": dist_us(times.get("verify_attn", [])),
+        "t_verify_kernel": dist_us(times.get("verify_attn_main", [])),
+        "draft_bytes": draft_bytes, "draft_gbs": draft_gbs, "t_draft_main": t_draft_main, "t_draft": t_draft,
+        "verify_bytes": verify_bytes, "verify_gbs": verify_gbs, "t_vmain": t_vmain, "t_verify": t_verify,
+        "mfma": mfma, "full": full,
+        "what_if": {"all_accepted_m_eq_k": ceiling, "accepted_25_per_round": what_if["25"],
+                    "accepted_40_per_round": what_if["40"],
+                    "note": ("derived from the measured call times: B * a / ((a - 1) * t_draft + t_verify) for a "
+                             "accepted tokens per round (a - 1 drafts all accepted plus the bonus); a = k + 1 is "
+                             "this configuration's ceiling, 25 and 40 are the pages' range")},
+        "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": acc_round,
+                   "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
+        "kernels": {name: {"median_us": pct(v, 50) * 1e6, "calls": len(v)} for name, v in times.items()},
+    }
+    del eng
+    return out
 
 
 def main():
@@ -194,83 +401,24 @@ def main():
               "for one long sequence, by context, merging (max, sum, output) partials; the vocabulary shards by "
               "columns with one 64-bit argmax key per row.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
+    import gc
+
     import torch
 
-    from lossless_speculative_kv_amd import configs, engine
+    from lossless_speculative_kv_amd import configs
 
     cfg = configs.BY_NAME[args.workload]
     q = args.quiet
-    log(f"workload {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} D={cfg.head_dim} "
-        f"T={cfg.context} k={cfg.k} V={cfg.vocab} kind={cfg.kind}", q)
-    t_setup = time.perf_counter()
-    eng = engine.Engine(cfg, rounds_cap=args.warmup + args.steps)
-    torch.cuda.synchronize()
-    log(f"setup {time.perf_counter() - t_setup:.1f} s", q)
-
-    for _ in range(args.warmup):
-        eng.round()
-    torch.cuda.synchronize()
-    body0, tail0, ctx0 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
-    eng.prepare_timing(args.steps * (2 * cfg.k + 2) + 4)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        eng.round()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    body1, tail1, ctx1 = (eng.body_len.cpu().numpy(), eng.tail_len.cpu().numpy(), eng.ctx_len.cpu().numpy())
-    ev = eng.events
-    eng.events = None
-
-    times = {}
-    for name, a, b in ev:
-        times.setdefault(name, []).append(a.elapsed_time(b) * 1e-3)
-    n_acc = eng.n_accept[args.warmup:args.warmup + args.steps].cpu().numpy()
-    accepted = float((n_acc + 1).sum())
-    # whole calls (attention kernel + split merge) were timed on even draft
-    # steps / even rounds, the attention kernel alone on odd ones; the events
-    # are recorded by the kernels' own dispatches (vc_time_next_call)
-    def avg(name):
-        v = times.get(name, [])
-        return float(np.mean(v)) if v else 0.0
-    t_draft_avg, t_draft_main = avg("draft_attn"), avg("draft_attn_main")
-    t_verify_avg, t_verify_main = avg("verify_attn"), avg("verify_attn_main")
-    attn_time = args.steps * (cfg.k * t_draft_avg + t_verify_avg)
-    value = accepted / attn_time if attn_time > 0 else 0.0
-
-    mid_body = [(int(a) + int(b)) / 2 for a, b in zip(body0, body1)]
-    mid_tail = [(int(a) + int(b)) / 2 + cfg.k / 2 for a, b in zip(tail0, tail1)]  # tail grows by 1 per draft step
-    draft_bytes = draft_bytes_per_launch(cfg, mid_body, mid_tail)
-    verify_bytes = verify_bytes_per_launch(cfg, [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)])
-    draft_gbs = draft_bytes / t_draft_main / 1e9 if t_draft_main > 0 else 0.0
-    t_vmain = t_verify_main if t_verify_main > 0 else t_verify_avg   # staged: whole chunked pass only
-    verify_gbs = verify_bytes / t_vmain / 1e9 if t_vmain > 0 else 0.0
-
-    B, k = cfg.batch, cfg.k
-    # MFMA utilisation: algorithmic flops over the main kernel's own duration
-    mid_ctx = [(int(a) + int(b)) / 2 for a, b in zip(ctx0, ctx1)]
-    mfma = {
-        "verify_attn": mfma_entry("verify_kernel", verify_flops_per_launch(cfg, mid_ctx), t_vmain),
-        "draft_vocab": mfma_entry("vocab product, M = batch", 2.0 * B * cfg.hidden * cfg.vocab,
-                                  avg("draft_vocab_main")),
-        "verify_vocab": mfma_entry("vocab product, M = (k+1) * batch", 2.0 * (k + 1) * B * cfg.hidden * cfg.vocab,
-                                   avg("verify_vocab_main")),
-    }
-    w_bytes = 2.0 * cfg.hidden * cfg.vocab
-    for key in ("draft_vocab", "verify_vocab"):
-        t = mfma[key]["avg_launch_us"] * 1e-6
-        mfma[key]["weight_GBs"] = w_bytes / t / 1e9 if t > 0 else 0.0
-    ceiling = B * (k + 1) / (k * t_draft_avg + t_verify_avg) if (k * t_draft_avg + t_verify_avg) > 0 else 0.0
-    breakdown = {name: {"avg_us": float(np.mean(v)) * 1e6, "calls": len(v)} for name, v in times.items()}
+    r = measure(cfg, args.steps, args.warmup, q)
+    full = r["full"]
     result = {
         "metric": "accepted tok/s/layer; draft & verify attn HBM GB/s as % of 8 TB/s peak",
-        "value": value,
+        "value": r["value"],
         "unit": "accepted tok/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -280,30 +428,50 @@ def main():
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "context": cfg.context,
                    "draft_k": cfg.k, "compressor": cfg.kind if cfg.kind != "kivi" else f"kivi-{cfg.bits}",
                    "residual": cfg.residual, "vocab": cfg.vocab, "hidden": cfg.hidden},
+        "value_p10": r["value_p10"], "value_p90": r["value_p90"],
         "roofline": {"bound": "hbm", "kernel": draft_kernel_name(cfg),
-                     "achieved": draft_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": draft_gbs / HBM_PEAK_GBS, "traffic": traffic_for(draft_kernel_name(cfg), cfg.name),
-                     "bytes_per_launch": draft_bytes, "avg_launch_us": t_draft_main * 1e6,
-                     "call_us": t_draft_avg * 1e6},
-        "verify_attn": {"kernel": "verify_kernel", "achieved_GBs": verify_gbs, "frac": verify_gbs / HBM_PEAK_GBS,
-                        "traffic": traffic_for("verify_kernel", cfg.name),
-                        "bytes_per_launch": verify_bytes, "avg_launch_us": t_vmain * 1e6,
-                        "call_us": t_verify_avg * 1e6},
-        "mfma": mfma,
-        **({"staging": {"host_resident_full_cache": True, "chunk_tokens": cfg.chunk,
-                        "device_chunk_buffers": cfg.stage_buffers,
-                        "verify_host_link_GBs": verify_gbs,
-                        "note": "verify time covers the whole chunked pass with its host-to-device copies "
-                                "(PCIe-inclusive); the first chunks are copied while the round drafts"}}
-           if cfg.staged else {}),
-        "accept": {"mean_m": float(n_acc.mean()), "accepted_per_round": accepted / args.steps,
-                   "histogram_m": np.bincount(n_acc.ravel(), minlength=k + 1).tolist()},
-        "round_tok_s": accepted / wall,
-        "what_if_all_accepted_tok_s_layer": ceiling,
-        "kernels": breakdown,
+                     "achieved": r["draft_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["draft_gbs"] / HBM_PEAK_GBS, "traffic": traffic_for(draft_kernel_name(cfg), cfg.name),
+                     "bytes_per_launch": r["draft_bytes"], "median_launch_us": r["t_draft_main"] * 1e6,
+                     "call_us": r["t_draft"] * 1e6, "launch_us": r["t_draft_kernel"], "call": r["t_draft_call"]},
+        "verify_attn": {"kernel": "verify_kernel", "achieved_GBs": r["verify_gbs"],
+                        "frac": r["verify_gbs"] / HBM_PEAK_GBS, "traffic": traffic_for("verify_kernel", cfg.name),
+                        "bytes_per_launch": r["verify_bytes"], "median_launch_us": r["t_vmain"] * 1e6,
+                        "call_us": r["t_verify"] * 1e6, "launch_us": r["t_verify_kernel"],
+                        "call": r["t_verify_call"]},
+        "full_kv_decode": full,
+        "vs_full_kv_decode": (r["value"] / full["tok_s_layer"]) if full and full["tok_s_layer"] > 0 else None,
+        "what_if": r["what_if"],
+        "mfma": r["mfma"],
+        "accept": r["accept"],
+        "round_tok_s": r["round_tok_s"],
+        "kernels": r["kernels"],
     }
+    r = None
+    gc.collect()
+    torch.cuda.empty_cache()
+    extras = {}
+    for name in [x for x in args.extra.split(",") if x and x != cfg.name]:
+        e = measure(configs.BY_NAME[name], 3, 1, q)
+        ec = e["cfg"]
+        extras[name] = {
+            "value": e["value"], "unit": "accepted tok/s/layer", "ms_per_step": e["ms_per_step"], "steps": 3,
+            "draft_attn": {"kernel": draft_kernel_name(ec), "achieved_GBs": e["draft_gbs"],
+                           "frac": e["draft_gbs"] / HBM_PEAK_GBS, "bytes_per_launch": e["draft_bytes"],
+                           "median_launch_us": e["t_draft_main"] * 1e6, "call": e["t_draft_call"]},
+            "verify_pass": {"t_call": e["t_verify_call"], "bytes": e["verify_bytes"],
+                            "GBs": e["verify_gbs"],
+                            **({"note": "PCIe-inclusive: the pass streams the host-resident full cache in chunks"}
+                               if ec.staged else {})},
+            "full_kv_decode": e["full"], "what_if": e["what_if"], "accept": e["accept"],
+            "vs_full_kv_decode": (e["value"] / e["full"]["tok_s_layer"]) if e["full"] else None,
+        }
+        e = None
+        gc.collect()
+        torch.cuda.empty_cache()
+    result["extra_workloads"] = extras
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, accepted / args.steps, q)
+        result["cpu_baseline"] = cpu_baseline(cfg, result["accept"]["accepted_per_round"], q)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--workload", default="qwen-32b-layer")
     ap.add_argument("--extra", default="llama-70b-layer-1m",
                     help="comma-separated workloads measured after the main one (3 rounds each) and reported "
-                         "under extra_workloads; empty for none")
+                         "under extra_workloads; 'none' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -451,7 +451,7 @@ def main():
     gc.collect()
     torch.cuda.empty_cache()
     extras = {}
-    for name in [x for x in args.extra.split(",") if x and x != cfg.name]:
+    for name in [x for x in args.extra.split(",") if x and x not in (cfg.name, "none")]:
         e = measure(configs.BY_NAME[name], 3, 1, q)
         ec = e["cfg"]
         extras[name] = {

@@ -164,6 +164,25 @@ vc_status vc_draft_workspace_bytes(const vc_attn_shape *shape, const vc_draft_kv
 vc_status vc_draft_decode_attn(const vc_attn_shape *shape, const void *q, const vc_draft_kv *kv,
                                float *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free variant of vc_draft_decode_attn, for callers that cannot
+ * allocate (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation and kernels, with the workspace
+ * taken from an 8 MiB device array inside the library instead of a caller
+ * buffer (one copy per GPU the library runs on, held until the process
+ * ends): a 260,352-byte region of split counters, then room for
+ * 8,128,256 bytes of split partials, i.e. a call whose
+ * vc_draft_workspace_bytes, less its counter words
+ * (B * n_kv_heads * 4 rounded up to 256), exceeds that returns
+ * VC_ERR_WORKSPACE and enqueues nothing (about B * n_q_heads * splits <=
+ * 15,000 rows at head_dim 128). The caller still owns q, the cache and out.
+ * The first call on a device also enqueues one small kernel on `stream` that
+ * clears the counters; every completed call leaves them zero. All calls on
+ * one GPU share the array: calls that may overlap on one GPU (different
+ * streams, or graphs replayed concurrently) race and must be serialised by
+ * the caller. Allocates and frees nothing. */
+vc_status vc_draft_decode_attn_noalloc(const vc_attn_shape *shape, const void *q, const vc_draft_kv *kv, float *out,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Verification attention over the full cache                                 */
 /* ------------------------------------------------------------------------- */

@@ -20,6 +20,7 @@ VC_TIME_CALL, VC_TIME_MAIN_KERNEL = 0, 1
 
 EXPORTS = [
     "vc_version", "vc_last_error", "vc_time_next_call", "vc_kivi_block_bytes", "vc_draft_workspace_bytes", "vc_draft_decode_attn",
+    "vc_draft_decode_attn_noalloc",
     "vc_verify_workspace_bytes", "vc_verify_attn", "vc_vocab_workspace_bytes", "vc_vocab_logits",
     "vc_greedy_accept", "vc_commit_workspace_bytes", "vc_commit_round", "vc_kivi_quantize",
     "vc_tokdrop_workspace_bytes", "vc_tokdrop_select", "vc_stage_full_kv",
@@ -81,6 +82,7 @@ _sigs = {
     "vc_kivi_block_bytes": ([C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "vc_draft_workspace_bytes": ([_S, C.POINTER(vc_draft_kv), C.POINTER(C.c_size_t)], C.c_int32),
     "vc_draft_decode_attn": ([_S, _P, C.POINTER(vc_draft_kv), _P, _P, C.c_size_t, _P], C.c_int32),
+    "vc_draft_decode_attn_noalloc": ([_S, _P, C.POINTER(vc_draft_kv), _P, _P], C.c_int32),
     "vc_verify_workspace_bytes": ([_S, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)], C.c_int32),
     "vc_verify_attn": ([_S, C.c_int32, _P, _P, _P, C.POINTER(vc_kv_chunk), _P, C.c_int32, _P, _P, C.c_size_t, _P],
                        C.c_int32),
@@ -138,6 +140,11 @@ def vc_draft_workspace_bytes(shape: vc_attn_shape, kv: vc_draft_kv) -> int:
 
 def vc_draft_decode_attn(shape, q, kv, out, ws, ws_bytes, stream):
     check(lib.vc_draft_decode_attn(C.byref(shape), q, C.byref(kv), out, ws, ws_bytes, stream), "vc_draft_decode_attn")
+
+
+def vc_draft_decode_attn_noalloc(shape, q, kv, out, stream):
+    check(lib.vc_draft_decode_attn_noalloc(C.byref(shape), q, C.byref(kv), out, stream),
+          "vc_draft_decode_attn_noalloc")
 
 
 def vc_verify_workspace_bytes(shape, n_rows, max_chunk_tokens) -> int:

@@ -17,6 +17,10 @@ namespace vc {
 size_t draft_ws_bytes(const vc_attn_shape& sh, const vc_draft_kv& kv);
 vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out, void* ws,
                        hipStream_t stream);
+size_t draft_partial_bytes(const vc_attn_shape& sh, const vc_draft_kv& kv);
+size_t draft_noalloc_max_partial_bytes();
+vc_status draft_launch_noalloc(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out,
+                               hipStream_t stream);
 size_t verify_ws_bytes(const vc_attn_shape& sh, int n_rows, int max_chunk_tokens);
 vc_status verify_launch(const vc_attn_shape& sh, int n_rows, const void* q, const void* k_new, const void* v_new,
                         const vc_kv_chunk& ctx, const int32_t* ctx_len, int flags, float* out, void* ws,
@@ -195,6 +199,21 @@ vc_status vc_draft_decode_attn(const vc_attn_shape* shape, const void* q, const 
   VC_REQ(out, 16, "out");
   if ((st = check_ws(ws, ws_bytes, vc::draft_ws_bytes(*shape, *kv))) != VC_OK) return st;
   return vc::draft_launch(*shape, q, *kv, out, ws, stream);
+}
+
+vc_status vc_draft_decode_attn_noalloc(const vc_attn_shape* shape, const void* q, const vc_draft_kv* kv, float* out,
+                                       hipStream_t stream) {
+  TimingClear timing_clear;
+  vc_status st;
+  if ((st = check_shape(shape)) != VC_OK) return st;
+  if ((st = check_draft_kv(shape, kv)) != VC_OK) return st;
+  VC_REQ(q, 16, "q");
+  VC_REQ(out, 16, "out");
+  const size_t need = vc::draft_partial_bytes(*shape, *kv), have = vc::draft_noalloc_max_partial_bytes();
+  if (need > have)
+    return fail(VC_ERR_WORKSPACE, "this call needs %zu bytes of split partials; the allocation-free entry point "
+                "holds %zu (use vc_draft_decode_attn with a workspace)", need, have);
+  return vc::draft_launch_noalloc(*shape, q, *kv, out, stream);
 }
 
 vc_status vc_verify_workspace_bytes(const vc_attn_shape* shape, int32_t n_rows, int32_t max_chunk_tokens,

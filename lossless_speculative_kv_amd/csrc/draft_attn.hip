@@ -1321,15 +1321,21 @@ size_t draft_ws_bytes(const vc_attn_shape& sh, const vc_draft_kv& kv) {
          align_up(rows * 2 * sizeof(float), 256);
 }
 
-vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out, void* ws,
-                       hipStream_t stream) {
+// Bytes of the split partials alone (the workspace after its counters).
+size_t draft_partial_bytes(const vc_attn_shape& sh, const vc_draft_kv& kv) {
+  return draft_ws_bytes(sh, kv) - draft_counter_bytes(sh);
+}
+
+// counters: one zeroed word per (sequence, KV head); partials: the split
+// partials (draft_partial_bytes, 256-byte aligned).
+static vc_status draft_launch_parts(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out,
+                                    uint32_t* counters, char* partials, hipStream_t stream) {
   const DraftPlan plan = draft_plan(sh, kv);
   DraftParams P{};
   P.q = static_cast<const uint16_t*>(q);
   const size_t rows = (size_t)sh.batch * sh.n_q_heads * plan.splits;
-  char* w = static_cast<char*>(ws);
-  P.counters = reinterpret_cast<uint32_t*>(w);
-  w += draft_counter_bytes(sh);
+  char* w = partials;
+  P.counters = counters;
   P.part_o = reinterpret_cast<float*>(w);
   w += align_up(rows * sh.head_dim * sizeof(float), 256);
   P.part_ml = reinterpret_cast<float*>(w);
@@ -1360,6 +1366,72 @@ vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv
   const DraftKernelPick k = pick_kernel(sh, kv);
   launch_ev(k.fn, grid, dim3(k.threads), 0, stream, tm.start, tm.stop, P);
   return check_launch("draft attention");
+}
+
+vc_status draft_launch(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out, void* ws,
+                       hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  return draft_launch_parts(sh, q, kv, out, reinterpret_cast<uint32_t*>(w), w + draft_counter_bytes(sh), stream);
+}
+
+// ------------------------------------------------ allocation-free variant ----
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid allocation): the draft workspace lives in this
+// file-scope device array instead of a caller buffer. Each GPU the library
+// runs on holds its own copy until the process ends. In host code the
+// array's name is only a stand-in; its device address comes from
+// hipGetSymbolAddress, taken once per device and used wherever host code
+// needs the array (kernel arguments, the clearing kernel).
+//
+// Layout: a fixed counter region (one word for every possible (sequence, KV
+// head), 255 x 255) cleared once when the device is first used and left zero
+// by every completed call, then the split partials of the call. The partials
+// never overlap a counter, so calls of any shape can follow each other.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr size_t kNoAllocCounterBytes = (size_t(255) * 255 * sizeof(uint32_t) + 255) / 256 * 256;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+// Largest partials a call may need.
+size_t draft_noalloc_max_partial_bytes() { return kNoAllocScratchBytes - kNoAllocCounterBytes; }
+
+// The draft call on this device's scratch array. On the first call for a
+// device its address is looked up and the counter region is cleared by a
+// kernel on `stream`, ahead of any draft kernel there.
+vc_status draft_launch_noalloc(const vc_attn_shape& sh, const void* q, const vc_draft_kv& kv, float* out,
+                               hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(VC_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  char* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || ptr == nullptr)
+        return fail(VC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                         kNoAllocCounterBytes / sizeof(uint32_t));
+      const vc_status st = check_launch("draft scratch clear");
+      if (st != VC_OK) return st;
+      g_scratch_ptr[dev] = ptr;
+    }
+    base = static_cast<char*>(g_scratch_ptr[dev]);
+  }
+  return draft_launch_parts(sh, q, kv, out, reinterpret_cast<uint32_t*>(base), base + kNoAllocCounterBytes, stream);
 }
 
 }  // namespace vc

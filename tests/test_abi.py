@@ -139,3 +139,18 @@ def test_kivi_block_bytes():
     assert L.lib.vc_kivi_block_bytes(96, 2, C.byref(out)) == L.VC_ERR_UNSUPPORTED
     assert L.lib.vc_kivi_block_bytes(128, 3, C.byref(out)) == L.VC_ERR_UNSUPPORTED
     assert L.lib.vc_kivi_block_bytes(128, 2, None) == L.VC_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_oversized_calls():
+    """The allocation-free draft call rejects, on the host, a call whose split
+    partials exceed its fixed scratch (255 sequences x 4080 query heads at
+    head_dim 128 need far more than 8 MiB), and checks its arguments like the
+    workspace call."""
+    sh = L.vc_attn_shape(255, 4080, 255, 128)
+    rc = L.lib.vc_draft_decode_attn_noalloc(C.byref(sh), 0x10000, C.byref(kivi_kv()), 0x10000, None)
+    assert rc == L.VC_ERR_WORKSPACE
+    assert "partials" in L.last_error()
+    rc = L.lib.vc_draft_decode_attn_noalloc(C.byref(shape()), None, C.byref(kivi_kv()), 0x10000, None)
+    assert rc == L.VC_ERR_INVALID_ARG
+    rc = L.lib.vc_draft_decode_attn_noalloc(C.byref(shape()), 0x10000, C.byref(kivi_kv(bits=3)), 0x10000, None)
+    assert rc == L.VC_ERR_UNSUPPORTED

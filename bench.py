@@ -280,9 +280,11 @@ def full_kv_decode(eng, n_calls=12):
     return times, nbytes
 
 
-def measure(cfg, steps, warmup, q, comparator=True):
+def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
     """Warm-up rounds, then `steps` timed rounds of one workload; returns the
-    figures of the JSON line (without the CPU baseline)."""
+    figures of the JSON line (without the CPU baseline). With graph_reps, a
+    round is then captured in a HIP graph and replayed that many times
+    (wall clock per replay, next to the eager round's)."""
     import numpy as np
     import torch
 
@@ -291,7 +293,7 @@ def measure(cfg, steps, warmup, q, comparator=True):
     log(f"workload {cfg.name}: B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} D={cfg.head_dim} "
         f"T={cfg.context} k={cfg.k} V={cfg.vocab} kind={cfg.kind}", q)
     t_setup = time.perf_counter()
-    eng = engine.Engine(cfg, rounds_cap=warmup + steps)
+    eng = engine.Engine(cfg, rounds_cap=warmup + steps + (graph_reps + 2 if graph_reps else 0))
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s", q)
     for _ in range(warmup):
@@ -365,6 +367,21 @@ def measure(cfg, steps, warmup, q, comparator=True):
                                "link, as one verification pass does; B / t(verification pass, staged)")}
     else:
         full = None
+    graph = None
+    if graph_reps and not cfg.staged:
+        g = eng.capture_round()
+        g.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(graph_reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = {"round_ms": (time.perf_counter() - tg) / graph_reps * 1e3, "replays": graph_reps,
+                 "eager_round_ms": wall / steps * 1e3,
+                 "note": "one HIP graph launch per round (Engine.capture_round) against the eager round of the "
+                         "timed region (one host call per kernel, timing events on)"}
+        log(f"graph replay {graph['round_ms']:.3f} ms per round (eager {graph['eager_round_ms']:.3f} ms)", q)
+        del g
     what_if = {str(a): B * a / ((a - 1) * t_draft + t_verify) for a in (25, 40)}
     ceiling = B * (k + 1) / per_round if per_round > 0 else 0.0
     out = {
@@ -376,7 +393,7 @@ def measure(cfg, steps, warmup, q, comparator=True):
         "t_verify_kernel": dist_us(times.get("verify_attn_main", [])),
         "draft_bytes": draft_bytes, "draft_gbs": draft_gbs, "t_draft_main": t_draft_main, "t_draft": t_draft,
         "verify_bytes": verify_bytes, "verify_gbs": verify_gbs, "t_vmain": t_vmain, "t_verify": t_verify,
-        "mfma": mfma, "full": full,
+        "mfma": mfma, "full": full, "graph": graph,
         "what_if": {"all_accepted_m_eq_k": ceiling, "accepted_25_per_round": what_if["25"],
                     "accepted_40_per_round": what_if["40"],
                     "note": ("derived from the measured call times: B * a / ((a - 1) * t_draft + t_verify) for a "
@@ -409,7 +426,7 @@ def main():
 
     cfg = configs.BY_NAME[args.workload]
     q = args.quiet
-    r = measure(cfg, args.steps, args.warmup, q)
+    r = measure(cfg, args.steps, args.warmup, q, graph_reps=args.steps)
     full = r["full"]
     result = {
         "metric": "accepted tok/s/layer; draft & verify attn HBM GB/s as % of 8 TB/s peak",
@@ -445,6 +462,7 @@ def main():
         "mfma": r["mfma"],
         "accept": r["accept"],
         "round_tok_s": r["round_tok_s"],
+        "graph_round": r["graph"],
         "kernels": r["kernels"],
     }
     r = None

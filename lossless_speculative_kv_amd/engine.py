@@ -385,3 +385,35 @@ class Engine:
         self.verify_attention()
         self.verify_vocab()
         self.accept_commit()
+
+    def capture_round(self) -> "torch.cuda.CUDAGraph":
+        """Capture one whole round (k draft steps with their embeddings and
+        vocab projections, the verification pass and its projection, accept
+        and commit) into a HIP graph. Every replay runs the next round from
+        the device-resident state (tokens, cache lengths, caches) with a
+        single launch from the host; nothing in the round reads the host, so
+        the replays chain like eager rounds. The accept lengths and committed
+        tokens of every replay land in round slot `graph_slot` (the round
+        index at capture time). Needs the full cache on the device (staging
+        waits on events across streams) and timing switched off."""
+        if self.cfg.staged:
+            raise ValueError("graph capture needs the full cache on the device")
+        if self.events is not None:
+            raise ValueError("switch timing off before capturing a round")
+        if self.round_idx >= self.rounds_cap:
+            raise RuntimeError("round capacity exhausted; raise rounds_cap")
+        g = torch.cuda.CUDAGraph()
+        saved = self.stream
+        slot = self.round_idx
+        torch.cuda.synchronize(self.dev)
+        try:
+            with torch.cuda.graph(g):
+                # the capture runs on torch's side stream: every call of the
+                # round goes there
+                self.stream = torch.cuda.current_stream(self.dev)
+                self.round()
+        finally:
+            self.stream = saved
+            self.round_idx = slot + 1
+        self.graph_slot = slot
+        return g

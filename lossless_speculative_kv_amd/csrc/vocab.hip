@@ -9,12 +9,15 @@
 // 16-byte pieces): lane group qg takes k = k0 + 32*kk + 8*qg + s in K-step kk
 // (the B operand uses the same permutation).
 //
-// Two kernels share the epilogue:
+// Three kernels share the epilogue:
 //  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
 //    rows; W goes straight from HBM to registers, h (tiny) from L2: fp32
 //    rounded to bf16 in registers for one m-tile, else the bf16 copy.
 //    A workgroup of 8 waves fills a CU and its waves are paced.
-//  * vocab_staged: any M. Each wave owns 32 vocab rows and all M rows; the
+//  * vocab_ring: 33 <= M <= 416 (verification). 8 waves = 4 vocab groups x
+//    2 row groups; W and hidden rows pass through an LDS ring of
+//    direct-to-LDS loads that every wave issues its share of.
+//  * vocab_staged: M above 416. Each wave owns 32 vocab rows and all M rows; the
 //    hidden rows are staged in LDS in 32-wide k chunks (double-buffered) and
 //    shared by the 8 waves of the workgroup, so W is read from HBM exactly
 //    once. Up to 18 row tiles the loads run ahead: the next W chunk and the
@@ -39,6 +42,7 @@ struct VocabParams {
   float* max_logit;   // [M] or null
   float* logits;      // [M][V] or null
   int M, Mp, K, V, nwg;
+  int hb_sliced;  // hb layout: 0 row-major [Mp][K]; 1 k-slice-major [K/32][Mp][32]
 };
 
 __device__ __forceinline__ uint64_t make_key(float v, int idx) {
@@ -69,12 +73,16 @@ __device__ __forceinline__ uint64_t max_q_u64(uint64_t x) {
   return k0 > k1 ? k0 : k1;
 }
 
-// h fp32 -> bf16 (nearest even), rows M..Mp-1 zero.
+// h fp32 -> bf16 (nearest even), rows M..Mp-1 zero; row-major, or
+// k-slice-major (each 32-wide k slice of all rows contiguous) for the ring
+// kernel, whose every stage then reads one contiguous block of hidden rows.
 __global__ __launch_bounds__(256) void hidden_to_bf16_kernel(const VocabParams P) {
   const size_t n = (size_t)P.Mp * P.K;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const size_t m = i / P.K;
-    P.hb[i] = (m < (size_t)P.M) ? (uint16_t)f32_to_bf16_bits(P.h[i]) : (uint16_t)0;
+    const size_t m = i / P.K, k = i % P.K;
+    const uint16_t v = (m < (size_t)P.M) ? (uint16_t)f32_to_bf16_bits(P.h[i]) : (uint16_t)0;
+    const size_t dst = P.hb_sliced ? ((k / 32) * P.Mp + m) * 32 + k % 32 : i;
+    P.hb[dst] = v;
   }
 }
 
@@ -550,6 +558,166 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
   }
 }
 
+// Ring kernel (up to 26 row tiles): the verification product, MFMA-bound at
+// large M. 8 waves = 4 vocab groups of 64 rows x 2 row groups of NT row
+// tiles; a workgroup covers 256 vocab rows and all Mp hidden rows, so each W
+// row is read from HBM once, and W and the hidden rows move in 32-wide k
+// slices through a ring of STAGES = AHEAD + 2 LDS stages. Every wave issues
+// a fixed share of each stage's direct-to-LDS loads (1 KB each: 16 rows x
+// 64 bytes), AHEAD stages ahead, waits for its share of the current stage
+// and meets the others at a bare barrier. The loads are asm statements
+// (the compiler does not count them as pending LDS writes, so it inserts no
+// vmcnt(0) before the ring reads) and the ring is read with plain LDS loads
+// (16 bytes per lane, one row per lane, XOR-swizzled pieces so that each
+// eight lanes hit distinct banks). Per stage a wave multiplies its 4 vocab
+// tiles by its NT row tiles: 4 + NT operand reads for 4 * NT MFMAs.
+// A stage reads 64 bytes of each 128-byte line of a W row; the loads keep the
+// default cache policy, so the line's other half is an L2 hit one stage
+// later (with non-temporal W loads each line was fetched from HBM twice:
+// M = 264 went 452 -> 366 us, M = 33 at K = 8192 535 -> 417 us). The hidden
+// rows sit in a k-slice-major copy, so a stage's hidden part is one
+// contiguous block.
+constexpr int kRingWaves = 8;
+constexpr int kRingRows = 256;  // vocab rows per workgroup
+constexpr int kRingWch = 16;    // W chunks per stage
+
+template <int NT>
+struct RingGeo {
+  static constexpr int HCH = 2 * NT;                          // hidden chunks per stage
+  static constexpr int NCH = kRingWch + HCH;                  // chunks per stage
+  static constexpr int PER = (NCH + kRingWaves - 1) / kRingWaves;  // loads per wave per stage
+  static constexpr int SB = NCH * 1024;                       // bytes per stage
+  static constexpr int AHEAD = NT <= 2 ? 4 : NT <= 5 ? 3 : NT <= 9 ? 2 : 1;
+  static constexpr int STAGES = AHEAD + 2;
+  static_assert(STAGES * SB <= 150 * 1024, "ring fits the LDS");
+  static_assert(AHEAD * PER < 64, "vmcnt range");
+};
+
+// piece position of 16-byte piece p of a 64-byte row r in the ring
+__device__ __forceinline__ int ring_piece(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+// One 1 KB direct-to-LDS load: lane l copies global bytes voff .. voff + 15
+// of the buffer to LDS address m0 + 16 l (default cache policy). Written as
+// an asm statement (see above); M0 is reserved to the compiler, so its value
+// is put back.
+__device__ __forceinline__ void ring_dma(const int (&rsrc)[4], uint32_t m0, int voff) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 r = {rsrc[0], rsrc[1], rsrc[2], rsrc[3]};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(m0), "s"(r)
+      : "memory");
+}
+
+template <int NT>
+__global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const VocabParams P) {
+  using G = RingGeo<NT>;
+  constexpr int NA = 4;
+  __shared__ __attribute__((aligned(1024))) char ring[G::STAGES * G::SB];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, qg = lane >> 4;
+  const int vg = wave % 4, mg = wave / 4;
+  const int vwg = blockIdx.x * kRingRows;
+  const int mtiles = P.Mp / 16;
+  const int nk = P.K / 32;
+  const int mt0 = mg * NT;  // first row tile of this wave's row group
+  // buffer descriptors (base, stride 0, extent in bytes, flags): this
+  // workgroup's W rows (rows past the vocabulary read as zero) and the
+  // padded bf16 hidden rows
+  const uint64_t wb = reinterpret_cast<uint64_t>(P.w) + (uint64_t)vwg * (uint64_t)P.K * 2u;
+  const uint32_t wrows = (uint32_t)min(kRingRows, P.V - vwg);
+  const int rw[4] = {(int)__builtin_amdgcn_readfirstlane((uint32_t)wb),
+                     (int)(__builtin_amdgcn_readfirstlane((uint32_t)(wb >> 32)) & 0xFFFFu),
+                     (int)__builtin_amdgcn_readfirstlane(wrows * (uint32_t)P.K * 2u), 0x00020000};
+  const uint64_t hb = reinterpret_cast<uint64_t>(P.hb);
+  const int rh[4] = {(int)__builtin_amdgcn_readfirstlane((uint32_t)hb),
+                     (int)(__builtin_amdgcn_readfirstlane((uint32_t)(hb >> 32)) & 0xFFFFu),
+                     (int)__builtin_amdgcn_readfirstlane((uint32_t)P.Mp * (uint32_t)P.K * 2u), 0x00020000};
+  // lane l of a chunk fills row 16c + l / 4 at piece position l % 4, i.e. the
+  // global piece that the swizzle places there
+  const int lrow = lane >> 2, lpos = lane & 3;
+  const uint32_t ring0 = lds_addr(ring);
+  // Hidden chunks past the row tiles (2 NT tiles allocated, Mp / 16 real)
+  // would read the next slice's rows in the k-slice-major copy; they load the
+  // last real chunk again instead (into their own, never-read stage rows).
+  // this wave's share of stage s: chunks wave * PER + i (past the last chunk:
+  // the last one again, same data to the same place); past the last stage
+  // the last k slice is loaded again into a stage no step reads
+  auto issue = [&](int s) {
+    const uint32_t slot = ring0 + (uint32_t)((s % G::STAGES) * G::SB);
+    const int k0 = min(s, nk - 1) * 32;
+#pragma unroll
+    for (int i = 0; i < G::PER; ++i) {
+      const int q = min(wave * G::PER + i, G::NCH - 1);  // wave-uniform
+      const int hsrc = min(q - kRingWch, mtiles - 1);     // hidden chunk whose rows are read
+      const int row = 16 * (q < kRingWch ? q : hsrc) + lrow;
+      // W rows are row-major; the hidden copy is k-slice-major ([K/32][Mp][32])
+      const int voff =
+          (q < kRingWch ? (row * P.K + k0) * 2 : ((k0 / 32) * P.Mp + row) * 64) + 16 * ring_piece(row, lpos);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + (uint32_t)q * 1024u);
+      if (q < kRingWch) ring_dma(rw, m0, voff);
+      else ring_dma(rh, m0, voff);
+    }
+  };
+  f32x4 acc[NA][NT];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < G::AHEAD; ++s) issue(s);
+  for (int s = 0; s < nk; ++s) {
+    issue(s + G::AHEAD);
+    // this wave's share of stage s has landed; after the barrier everyone's
+    // has, and nobody reads the stage that the loads just issued overwrite
+    wait_vmcnt<G::AHEAD * G::PER>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* stage = ring + (s % G::STAGES) * G::SB;
+    u32x4 A[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const int row = 64 * vg + 16 * a + n;
+      A[a] = *reinterpret_cast<const u32x4*>(stage + row * 64 + 16 * ring_piece(row, qg));
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (mt0 + t < mtiles) {
+        const int row = 16 * (mt0 + t) + n;  // hidden row = its row in the hidden part of the stage
+        const u32x4 B = *reinterpret_cast<const u32x4*>(stage + kRingWch * 1024 + row * 64 + 16 * ring_piece(row, qg));
+#pragma unroll
+        for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a], B, acc[a][t]);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // nothing may land after the ring is reused below
+  __syncthreads();
+  int mrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) mrow[t] = 16 * (mt0 + t);
+  uint64_t best[NT];
+  epilogue<NA, NT>(P, acc, vwg + 64 * vg, mrow, lane, best);
+  // reduce over the 4 vocab groups of each row through LDS (the ring is idle)
+  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [4][Mp]
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (qg == 0 && mt0 + t < mtiles) red[vg * P.Mp + 16 * (mt0 + t) + n] = best[t];
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 64 * kRingWaves) {
+    uint64_t k = red[m];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+  }
+}
+
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
   const int m = blockIdx.x;
   uint64_t k = 0;
@@ -587,6 +755,7 @@ struct VocabPlan {
   int ms;     // stream: m-tiles
   int nmt;    // staged: m-tiles template bound
   int tiled;  // tiled: m-tiles per wave (0 = not tiled)
+  int ring;   // ring: row tiles per row group (0 = not the ring kernel)
   int nwg;
   int Mp;
 };
@@ -604,6 +773,11 @@ VocabPlan vocab_plan(int M, int K, int V) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
     p.nwg = (V + kTRows - 1) / kTRows;
+  } else if (mt <= 26) {
+    // the two row groups of NT tiles cover every row tile
+    p.stream = false;
+    p.ring = mt <= 4 ? 2 : mt <= 10 ? 5 : mt <= 18 ? 9 : 13;
+    p.nwg = (V + kRingRows - 1) / kRingRows;
   } else {
     p.stream = false;
     p.nmt = mt <= 4 ? 4 : mt <= 8 ? 8 : mt <= 12 ? 12 : mt <= 18 ? 18 : mt <= 24 ? 24 : 28;
@@ -635,6 +809,7 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.K = K;
   P.V = V;
   P.nwg = plan.nwg;
+  P.hb_sliced = plan.ring ? 1 : 0;
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
   hipEvent_t mstart = main_only ? tm.start : nullptr, mstop = main_only ? tm.stop : nullptr;
@@ -651,6 +826,14 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
     hipEvent_t start = (main_only || convert) ? mstart : tm.start;
     if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
     else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
+  } else if (plan.ring) {
+    const dim3 grid(plan.nwg), block(64 * kRingWaves);
+    switch (plan.ring) {
+      case 2: launch_ev(vocab_ring_kernel<2>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 5: launch_ev(vocab_ring_kernel<5>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 9: launch_ev(vocab_ring_kernel<9>, grid, block, 0, stream, mstart, mstop, P); break;
+      default: launch_ev(vocab_ring_kernel<13>, grid, block, 0, stream, mstart, mstop, P); break;
+    }
   } else if (plan.tiled) {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);

@@ -373,16 +373,18 @@ def test_verify_parity(L, case):
 
 TILED_FAULT = ("the tiled vocab kernel (compiled out: kTiledEnabled = false) made the GPU report an illegal "
                "memory access on this shape (M = 33, K = 1024, V = 5000), also after a fix. The plan can no "
-               "longer select that kernel, so unskipped this case would run the staged kernel (M = 33..64 "
-               "band, covered by the M = 48 and M = 64 cases); the shape stays off the GPU until the tiled "
-               "kernel's cause is found")
-# (M, K, V): the stream kernel (M <= 32: one and two m-tiles) and every
-# template of the staged kernel the plan selects: NMT 4 (M 33..64), 8, 12,
-# 18, 24 (M 289..384) and 28; ragged vocabularies and K up to 8192
+               "longer select that kernel, so unskipped this case would run the ring kernel (M = 33..64 "
+               "band, covered by the M = 33 at K = 8192, M = 48 and M = 64 cases); the shape stays off the GPU "
+               "until the tiled kernel's cause is found")
+# (M, K, V): the stream kernel (M <= 32: one and two m-tiles), every template
+# of the ring kernel the plan selects (NT 2: M 33..64, NT 5: 65..160, NT 9:
+# 161..288, NT 13: 289..416) and the staged kernel above 416 rows; ragged
+# vocabularies (a last workgroup with few rows) and K up to 8192
 VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097), (20, 512, 3000),
                pytest.param((33, 1024, 5000), marks=pytest.mark.skip(reason=TILED_FAULT)), (264, 4096, 8192),
                (416, 1024, 3001), (164, 512, 2048), (48, 1024, 5000), (64, 8192, 3001), (100, 512, 2051),
-               (300, 1024, 3000), (1, 8192, 20011), (180, 256, 1000)]
+               (300, 1024, 3000), (1, 8192, 20011), (180, 256, 1000), (440, 512, 2000), (33, 8192, 4099),
+               (160, 1024, 1025)]
 
 
 @pytest.mark.parametrize("case", VOCAB_CASES, ids=[f"vocab{i}" for i in range(len(VOCAB_CASES))])
@@ -430,7 +432,7 @@ def test_vocab_parity(L, case):
 def test_vocab_tiled_parity(L):
     """Meant for the tiled vocab kernel (M up to 288: W and hidden slices
     through a 4-stage LDS ring) on the shape it faulted on. That kernel is
-    compiled out, so this would run the staged kernel on the same shape."""
+    compiled out, so this would run the ring kernel on the same shape."""
     test_vocab_parity(L, (33, 1024, 5000))
 
 

@@ -10,7 +10,7 @@
 // (the B operand uses the same permutation).
 //
 // Three kernels share the epilogue:
-//  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 64 vocab
+//  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 16*NA vocab
 //    rows; W goes straight from HBM to registers, h (tiny) from L2: fp32
 //    rounded to bf16 in registers for one m-tile, else the bf16 copy.
 //    A workgroup of 8 waves fills a CU and its waves are paced.
@@ -130,12 +130,13 @@ __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc
 // older first and finish the younger late) and the waves are paced.
 constexpr int kStreamWaves = 8;
 
-template <int MS>
+// NA vocab tiles of 16 rows per wave (the plan picks NA per vocabulary size
+// so that the workgroups fill the CUs in as few rounds as possible).
+template <int MS, int NA>
 __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(const VocabParams P) {
-  constexpr int NA = 4;  // vocab tiles per wave
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
-  const int vbase = (blockIdx.x * kStreamWaves + wave) * 64;
+  const int vbase = (blockIdx.x * kStreamWaves + wave) * 16 * NA;
   __shared__ __attribute__((aligned(16))) int progress[8];  // k-steps of 256 each wave has started
   if (threadIdx.x < 8) progress[threadIdx.x] = 0;
   __syncthreads();
@@ -753,12 +754,16 @@ void launch_staged(const VocabParams& P, hipStream_t s, hipEvent_t start, hipEve
 struct VocabPlan {
   bool stream;
   int ms;     // stream: m-tiles
+  int na;     // stream: vocab tiles of 16 rows per wave
   int nmt;    // staged: m-tiles template bound
   int tiled;  // tiled: m-tiles per wave (0 = not tiled)
   int ring;   // ring: row tiles per row group (0 = not the ring kernel)
   int nwg;
   int Mp;
 };
+
+// Compute units the stream plan fills (MI355X).
+constexpr long kVocabCUs = 256;
 
 VocabPlan vocab_plan(int M, int K, int V) {
   (void)K;
@@ -768,7 +773,23 @@ VocabPlan vocab_plan(int M, int K, int V) {
   if (mt <= 2) {
     p.stream = true;
     p.ms = mt;
-    p.nwg = (V + 64 * kStreamWaves - 1) / (64 * kStreamWaves);
+    // vocab tiles per wave: the fewest rounds of workgroups over the 256 CUs
+    // times the rows each wave streams (a vocabulary of 152064 rows takes 297
+    // workgroups of 512 rows, two rounds, but 238 of 640 rows, one round);
+    // five tiles only with one m-tile (registers); on a tie the larger tile
+    // count (fewer workgroups) wins
+    const int cand[4] = {5, 4, 2, 1};
+    long best = -1;
+    for (int na : cand) {
+      if (na == 5 && mt != 1) continue;
+      const long nwg = (V + 16L * na * kStreamWaves - 1) / (16L * na * kStreamWaves);
+      const long cost = (nwg + kVocabCUs - 1) / kVocabCUs * na;
+      if (best < 0 || cost < best) {
+        best = cost;
+        p.na = na;
+        p.nwg = (int)nwg;
+      }
+    }
   } else if (kTiledEnabled && mt <= 18) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
@@ -824,8 +845,21 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   if (plan.stream) {
     const dim3 block(64 * kStreamWaves);
     hipEvent_t start = (main_only || convert) ? mstart : tm.start;
-    if (plan.ms == 1) launch_ev(vocab_stream_kernel<1>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
-    else launch_ev(vocab_stream_kernel<2>, dim3(plan.nwg), block, 0, stream, start, mstop, P);
+    const dim3 grid(plan.nwg);
+    if (plan.ms == 1) {
+      switch (plan.na) {
+        case 1: launch_ev(vocab_stream_kernel<1, 1>, grid, block, 0, stream, start, mstop, P); break;
+        case 2: launch_ev(vocab_stream_kernel<1, 2>, grid, block, 0, stream, start, mstop, P); break;
+        case 4: launch_ev(vocab_stream_kernel<1, 4>, grid, block, 0, stream, start, mstop, P); break;
+        default: launch_ev(vocab_stream_kernel<1, 5>, grid, block, 0, stream, start, mstop, P); break;
+      }
+    } else {
+      switch (plan.na) {
+        case 1: launch_ev(vocab_stream_kernel<2, 1>, grid, block, 0, stream, start, mstop, P); break;
+        case 2: launch_ev(vocab_stream_kernel<2, 2>, grid, block, 0, stream, start, mstop, P); break;
+        default: launch_ev(vocab_stream_kernel<2, 4>, grid, block, 0, stream, start, mstop, P); break;
+      }
+    }
   } else if (plan.ring) {
     const dim3 grid(plan.nwg), block(64 * kRingWaves);
     switch (plan.ring) {

@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--extra", default="llama-70b-layer-1m",
                     help="comma-separated workloads measured after the main one (3 rounds each) and reported "
                          "under extra_workloads; 'none' for none")
+    ap.add_argument("--p1", default="llama-70b-layer-1m,llama-70b-layer-256k,llama-70b-layer-256k-1buf",
+                    help="host-resident workloads on which the P1 scheduler's two staggered request groups are "
+                         "measured against one group (3 rounds each); 'none' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -407,6 +410,31 @@ def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
     return out
 
 
+def p1_staggering(cfg, rounds, q):
+    """Two request groups of a host-resident layer under the P1 scheduler
+    (drafting staggered across groups, each group's full cache crossing the
+    host link on its own copy stream) against one group alone: committed
+    tokens per second, and the busy fractions of the host link and of
+    drafting over the run."""
+    from lossless_speculative_kv_amd.scheduler import StaggeredGroups
+    log(f"p1 scheduler on {cfg.name}: two groups", q)
+    sched = StaggeredGroups(cfg, 2, rounds_cap=1 + 2 * rounds)
+    sched.run(1)  # warm-up round of both groups
+    one = sched.run(rounds, trace=True, n_groups=1)
+    two = sched.run(rounds, trace=True)
+    log(f"p1 scheduler on {cfg.name}: one group {one.group_rounds_s:.2f} rounds/s, two groups "
+        f"{two.group_rounds_s:.2f} group-rounds/s", q)
+    del sched
+    return {"one_group": one.as_dict(), "two_groups": two.as_dict(),
+            "speedup": two.group_rounds_s / one.group_rounds_s,
+            "context": cfg.context, "chunk_tokens": cfg.chunk, "device_chunk_buffers": cfg.stage_buffers,
+            "draft_k": cfg.k,
+            "note": "speedup = group-rounds per second with two staggered groups / rounds per second of one group "
+                    "(committed tokens also depend on each group's acceptance, so they are reported but not "
+                    "compared); link = host-to-device chunk copies (union of their intervals), draft = the "
+                    "groups' draft-step phases"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -488,6 +516,12 @@ def main():
         gc.collect()
         torch.cuda.empty_cache()
     result["extra_workloads"] = extras
+    p1 = {}
+    for name in [x for x in args.p1.split(",") if x and x != "none"]:
+        p1[name] = p1_staggering(configs.BY_NAME[name], 3, q)
+        gc.collect()
+        torch.cuda.empty_cache()
+    result["p1_scheduler"] = p1
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, result["accept"]["accepted_per_round"], q)
     else:

@@ -24,7 +24,7 @@ class RoundConfig:
     outliers: bool = False
     staged: bool = False      # full cache in pinned host memory, streamed in chunks
     chunk: int = 65536
-    stage_buffers: int = 4    # device chunk buffers; the first ones fill while the round drafts
+    stage_buffers: int = 4    # device chunk buffers (>= 1); the first ones fill while the round drafts
     seed: int = 1
 
     @property
@@ -48,4 +48,11 @@ LLAMA_70B = RoundConfig("llama-70b-layer-1m", 1, 64, 8, 128, 1048576, 128256, 32
                         staged=True, chunk=65536, seed=5)
 
 ALL = [TINY, LLAMA3_8B, MISTRAL_24B, QWEN_32B, LLAMA_70B]
-BY_NAME = {c.name: c for c in ALL}
+# the Llama-70B layer with a 256K-token host-resident context: its drafting
+# and its staging take similar time, the case where staggering two request
+# groups can pay off
+LLAMA_70B_256K = LLAMA_70B.scaled(name="llama-70b-layer-256k", context=262144)
+# the same with one device chunk buffer (device memory for staging scarce):
+# one group cannot keep the link busy while it drafts
+LLAMA_70B_256K_1BUF = LLAMA_70B_256K.scaled(name="llama-70b-layer-256k-1buf", stage_buffers=1)
+BY_NAME = {c.name: c for c in ALL + [LLAMA_70B_256K, LLAMA_70B_256K_1BUF]}

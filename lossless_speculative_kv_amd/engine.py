@@ -43,10 +43,17 @@ def _round32(x: int) -> int:
 class Engine:
     """Owns the caches and round buffers of one batch of sequences."""
 
-    def __init__(self, cfg: RoundConfig, rounds_cap: int = 4, device: str = "cuda"):
-        self.cfg = c = cfg
+    def __init__(self, cfg: RoundConfig, rounds_cap: int = 4, device: str = "cuda",
+                 stream: "torch.cuda.Stream | None" = None):
+        """stream: the compute stream of this engine's calls (default: the
+        current stream); set-up work runs on it too."""
         self.dev = torch.device(device)
-        self.stream = torch.cuda.current_stream(self.dev)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.dev)
+        with torch.cuda.stream(self.stream):
+            self._setup(cfg, rounds_cap)
+
+    def _setup(self, cfg: RoundConfig, rounds_cap: int):
+        self.cfg = c = cfg
         sh = self.shape = L.vc_attn_shape(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim)
         B, Hq, Hkv, D, k = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.k
         self.rounds_cap = rounds_cap
@@ -55,6 +62,9 @@ class Engine:
         # torch events recorded by the timed calls' own kernel dispatches
         self.events = None
         self._ev_pool = []
+        # optional copy tracing (staged caches): when a list, (start, end,
+        # bytes) of every chunk copy, events recorded on the copy stream
+        self.copy_events = None
         s = self.stream.cuda_stream
         bf = torch.bfloat16
 
@@ -160,7 +170,7 @@ class Engine:
         self.full_v[:, :, :T].copy_(big_v)
         torch.cuda.synchronize(self.dev)
         self._big = (big_k, big_v)
-        nbuf = max(2, c.stage_buffers)
+        nbuf = max(1, c.stage_buffers)
         self.chunk_k = [torch.empty((B, Hkv, c.chunk, D), dtype=torch.bfloat16, device=self.dev) for _ in range(nbuf)]
         self.chunk_v = [torch.empty_like(self.chunk_k[0]) for _ in range(nbuf)]
         self.copy_stream = torch.cuda.Stream(self.dev)
@@ -302,11 +312,18 @@ class Engine:
     def _stage_chunk(self, i, t0, n):
         cs = self.copy_stream
         buf = i % len(self.chunk_k)
+        tracing = self.copy_events is not None
+        if tracing:
+            a = torch.cuda.Event(enable_timing=True)
+            a.record(cs)
         L.vc_stage_full_kv(self.shape, self.full_k.data_ptr(), self.full_v.data_ptr(), self.full_cap, t0, n,
                            self.chunk_k[buf].data_ptr(), self.chunk_v[buf].data_ptr(), self.cfg.chunk,
                            cs.cuda_stream, None)
-        ev = torch.cuda.Event()
+        ev = torch.cuda.Event(enable_timing=tracing)
         ev.record(cs)
+        if tracing:
+            c = self.cfg
+            self.copy_events.append((a, ev, 2 * c.batch * c.n_kv_heads * n * c.head_dim * 2))
         self._staged_ready[i] = ev
 
     def verify_staged(self):

@@ -152,3 +152,16 @@ def test_planted_wrong_draft_gives_accept_length_j(j):
     assert r["m"] == j
     assert r["committed"][j] == ref[j]      # the correction is the full-cache token
     assert states[0].x0 == ref[j]
+
+
+def test_scheduler_interval_arithmetic():
+    """Busy-time helpers of the P1 scheduler (host logic): the union of
+    overlapping intervals and the overlap of two interval sets, by hand."""
+    from lossless_speculative_kv_amd.scheduler import intersection_length, merge, union_length
+    xs = [(0.0, 2.0), (1.0, 3.0), (5.0, 6.0)]
+    assert merge(xs) == [(0.0, 3.0), (5.0, 6.0)]
+    assert union_length(xs) == 4.0
+    ys = [(2.5, 5.5), (2.0, 2.7)]
+    # xs covers [0,3] u [5,6]; ys covers [2,5.5]: overlap [2,3] u [5,5.5]
+    assert intersection_length(xs, ys) == 1.5
+    assert union_length([]) == 0.0

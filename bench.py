@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--p1", default="llama-70b-layer-1m,llama-70b-layer-256k,llama-70b-layer-256k-1buf",
                     help="host-resident workloads on which the P1 scheduler's two staggered request groups are "
                          "measured against one group (3 rounds each); 'none' for none")
+    ap.add_argument("--pipeline", default="llama-70b-layer-1m",
+                    help="host-resident workload on which pipelined drafting is timed against plain rounds; 'none' "
+                         "for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -435,6 +438,34 @@ def p1_staggering(cfg, rounds, q):
                     "groups' draft-step phases"}
 
 
+def pipelined_drafting(cfg, rounds, q):
+    """Rounds of a host-resident layer with pipelined drafting (the drafter
+    continues k + 1 steps on a side stream while verification waits for the
+    full cache) against the same rounds without: wall time per round, and
+    how many continued drafts the next rounds could use."""
+    import torch
+
+    from lossless_speculative_kv_amd import engine
+    out = {}
+    for label, pipe in (("off", 0), ("on", cfg.k + 1)):
+        log(f"pipelined drafting on {cfg.name}: {label}", q)
+        e = engine.Engine(cfg.scaled(pipeline=pipe), rounds_cap=rounds + 1)
+        e.round()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            e.round()
+        torch.cuda.synchronize()
+        out[label] = {"round_ms": (time.perf_counter() - t0) / rounds * 1e3, "drafts_reused": e.reused_drafts,
+                      "mean_m": float(e.n_accept[1:rounds + 1].float().mean())}
+        del e
+        torch.cuda.empty_cache()
+    out["note"] = ("continued drafts are reused only after a round that accepted all k drafts whose bonus token "
+                   "equals the first continued draft; with the synthetic data's low acceptance none is, so this "
+                   "measures the cost of drafting during verification")
+    return out
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -522,6 +553,10 @@ def main():
         gc.collect()
         torch.cuda.empty_cache()
     result["p1_scheduler"] = p1
+    if args.pipeline != "none":
+        result["pipelined_drafting"] = {args.pipeline: pipelined_drafting(configs.BY_NAME[args.pipeline], 3, q)}
+        gc.collect()
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, result["accept"]["accepted_per_round"], q)
     else:

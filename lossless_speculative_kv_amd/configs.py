@@ -25,6 +25,7 @@ class RoundConfig:
     staged: bool = False      # full cache in pinned host memory, streamed in chunks
     chunk: int = 65536
     stage_buffers: int = 4    # device chunk buffers (>= 1); the first ones fill while the round drafts
+    pipeline: int = 0         # staged only: draft steps continued on a side stream during verification (<= k + 1)
     seed: int = 1
 
     @property

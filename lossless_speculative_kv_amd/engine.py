@@ -85,7 +85,10 @@ class Engine:
             self._fill_context(self.full_k, self.full_v, self.full_cap)
 
         # draft cache
-        self.tail_cap = _round32(max(c.residual, 0) + rounds_cap * (k + 1) + 32)
+        if c.pipeline and (not c.staged or c.pipeline > k + 1):
+            raise ValueError("pipelined drafting needs a staged configuration and at most k + 1 steps")
+        # (pipelined drafting appends up to `pipeline` more rows before commit)
+        self.tail_cap = _round32(max(c.residual, 0) + rounds_cap * (k + 1) + 32 + c.pipeline)
         self.body_len = torch.zeros((B,), dtype=torch.int32, device=self.dev)
         self.tail_len = torch.zeros((B,), dtype=torch.int32, device=self.dev)
         self.kv = L.vc_draft_kv()
@@ -120,6 +123,10 @@ class Engine:
 
         # round buffers (position-major [k+1][B])
         self.xs = torch.zeros((k + 1, B), dtype=torch.int32, device=self.dev)
+        # pipelined drafting: continued drafts s_1..s_J in rows 1..J
+        self.xs_spec = torch.zeros((c.pipeline + 1, B), dtype=torch.int32, device=self.dev)
+        self.reuse = 0            # leading drafts of the next round already known
+        self.reused_drafts = 0    # drafts reused over all rounds
         self.xs[0] = torch.from_numpy(synth.start_tokens(c.seed, B, c.vocab).astype(np.int32)).to(self.dev)
         self.y = torch.zeros((k + 1, B), dtype=torch.int32, device=self.dev)
         self.n_accept = torch.zeros((rounds_cap, B), dtype=torch.int32, device=self.dev)
@@ -222,12 +229,18 @@ class Engine:
         self.scores = scores
 
     # --------------------------------------------------------------- steps
+    def _embed_draft(self, tok_ptr: int, stream: int):
+        """Query of the given tokens, and their keys / values appended to the
+        draft tail (tail_len grows by one)."""
+        c = self.cfg
+        sdev.embed_draft(c.seed, tok_ptr, 1, c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                         _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
+                         self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), stream)
+
     def draft_step(self, j: int):
         c = self.cfg
         s = self.stream.cuda_stream
-        sdev.embed_draft(c.seed, self.xs[j].data_ptr(), 1, c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim,
-                         _ptr(self.key_mult), self.q_draft.data_ptr(), self.tail_k.data_ptr(),
-                         self.tail_v.data_ptr(), self.tail_cap, c.kind == "kivi", self.tail_len.data_ptr(), s)
+        self._embed_draft(self.xs[j].data_ptr(), s)
         self.draft_attention(j)
         # even steps time the whole call, odd steps the vocab product alone
         name, scope = ("draft_vocab", L.VC_TIME_CALL) if j % 2 == 0 else ("draft_vocab_main", L.VC_TIME_MAIN_KERNEL)
@@ -326,11 +339,12 @@ class Engine:
             self.copy_events.append((a, ev, 2 * c.batch * c.n_kv_heads * n * c.head_dim * 2))
         self._staged_ready[i] = ev
 
-    def verify_staged(self):
+    def verify_staged(self, after_chunk=None):
         """Stream the host-resident full cache through the device chunk buffers:
         chunks not already staged ahead are copied on the side stream once
         their buffer is free, overlapping the verification of earlier chunks
-        on the compute stream."""
+        on the compute stream. after_chunk(i, n_chunks), if given, enqueues
+        more work on the compute stream after chunk i's verification."""
         c = self.cfg
         comp = self.stream
         cs = self.copy_stream
@@ -363,6 +377,8 @@ class Engine:
                              self.ws_verify.numel(), comp.cuda_stream)
             free[buf] = torch.cuda.Event()
             free[buf].record(comp)
+            if after_chunk is not None:
+                after_chunk(i, len(plan))
         self._staged_ready = {}
 
     def verify_vocab(self):
@@ -395,13 +411,75 @@ class Engine:
             self.stage_ahead()
 
     def round(self):
+        c = self.cfg
         self.begin_round()
-        for j in range(self.cfg.k):
-            self.draft_step(j)
+        for j in range(c.k):
+            if j < self.reuse:
+                # x_{j+1} was drafted during the previous verification: only
+                # x_j's keys and values join the tail
+                self._embed_draft(self.xs[j].data_ptr(), self.stream.cuda_stream)
+            else:
+                self.draft_step(j)
         self.embed_block()
-        self.verify_attention()
+        if c.pipeline:
+            self.verify_staged(after_chunk=self._speculate_between)
+        else:
+            self.verify_attention()
         self.verify_vocab()
+        if c.pipeline:
+            # the continued drafts' tail rows are dropped again before commit
+            with torch.cuda.stream(self.stream):
+                self.tail_len.sub_(c.pipeline)
         self.accept_commit()
+        if c.pipeline:
+            self.reuse = self.decide_reuse()
+
+    def _speculate_between(self, i: int, n_chunks: int):
+        """Pipelined drafting (the drafter keeps writing while the verifier
+        fetches the full cache, then is corrected): the drafter continues
+        from x_k, s_1 = draft(x_k), s_{i+1} = draft(s_i), for `pipeline`
+        steps in all, a share of them after the verification of each chunk
+        but the last, on the compute stream. A chunk's verification has then
+        released its buffer, and the steps run while the next chunk is still
+        crossing the host link. (On a stream of their own they took the
+        compute units from the chunk verifications, which delayed the buffer
+        releases the copies wait for.) The steps append their inputs to the
+        draft tail like any draft step; round() drops those rows before
+        commit."""
+        c = self.cfg
+        parts = max(1, n_chunks - 1)
+        if i >= parts:
+            return
+        lo, hi = i * c.pipeline // parts, (i + 1) * c.pipeline // parts
+        s = self.stream.cuda_stream
+        for st in range(lo, hi):
+            tok_in = self.xs[c.k] if st == 0 else self.xs_spec[st]
+            self._embed_draft(tok_in.data_ptr(), s)
+            L.vc_draft_decode_attn(self.shape, self.q_draft.data_ptr(), self.kv, self.o_draft.data_ptr(),
+                                   self.ws_draft.data_ptr(), self.ws_draft.numel(), s)
+            L.vc_vocab_logits(c.batch, c.hidden, c.vocab, self.o_draft.data_ptr(), self.W.data_ptr(),
+                              self.xs_spec[st + 1].data_ptr(), None, None, self.ws_vocab_d.data_ptr(),
+                              self.ws_vocab_d.numel(), s)
+
+    def decide_reuse(self) -> int:
+        """After commit (host synchronisation): when every sequence accepted all
+        k drafts and its bonus token y_{k+1} equals the first continued draft
+        s_1, the continued drafts s_2..s_J are the drafter's proposals after
+        the new pending token, so they become x_1..x_{J-1} of the next round;
+        otherwise they are discarded. Returns the number reused. Whatever the
+        drafts, verification keeps the committed stream equal to full-cache
+        greedy decoding."""
+        c = self.cfg
+        r = self.round_idx - 1
+        with torch.cuda.stream(self.stream):
+            ok = bool(((self.n_accept[r] == c.k) & (self.y[c.k] == self.xs_spec[1])).all().item())
+            if not ok:
+                return 0
+            n = min(c.pipeline - 1, c.k)
+            if n > 0:
+                self.xs[1:n + 1].copy_(self.xs_spec[2:n + 2])
+        self.reused_drafts += n
+        return n
 
     def capture_round(self) -> "torch.cuda.CUDAGraph":
         """Capture one whole round (k draft steps with their embeddings and

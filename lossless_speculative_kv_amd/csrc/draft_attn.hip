@@ -762,7 +762,15 @@ __device__ __forceinline__ void merge_waves(const DraftParams& P, int b, int hk,
 // the count to S merges the S partials of its (sequence, KV head) in split
 // order (so the result does not depend on the order in which workgroups
 // ran), writes the output and sets the count back to zero for the next
-// call. The partials are read with device-coherent loads.
+// call. The partials are written and read with agent-scope atomic accesses
+// (device-coherent: they bypass the per-XCD L2s), and every thread waits for
+// its stores to complete (vmcnt(0)) before the workgroup barrier that
+// precedes the counter atomic, so the partials are in coherent memory before
+// the count can reach S. A release on the counter atomic and an acquire
+// fence in the merging workgroup would state that ordering in the memory
+// model, but at agent scope on MI355X they write back and invalidate the
+// L2: measured, the draft kernel went from 41.2 to 54.2 us per launch on the
+// Llama-3-8B layer and from 135.2 to 146.8 us on the Qwen-32B layer.
 template <int D>
 __device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk, int nthreads, int* lds_flag) {
   constexpr int kBatch = 8;  // splits whose loads are issued together

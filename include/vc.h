@@ -216,7 +216,14 @@ vc_status vc_verify_workspace_bytes(const vc_attn_shape *shape, int32_t n_rows, 
 /* Position-major block arrays: q: bf16 [n_rows][B][Hq][D]; k_new, v_new:
  * bf16 [n_rows][B][Hkv][D] (the block tokens' keys/values); ctx_len: [B];
  * out: fp32 [n_rows][B][Hq][D], written by the END call. n_rows <= 64 and
- * n_rows * g <= 288. */
+ * n_rows * g <= 288.
+ * Arithmetic: scores q.k from the exact bf16 operands in fp32; the softmax
+ * probabilities are rounded to fp16 (11 significant bits) for P x V and for
+ * the row sums alike, and the values are taken to fp16 for that product,
+ * which is exact for |v| in [2^-17, 65504] (smaller values round to
+ * multiples of 2^-24); values must not exceed 65504 in magnitude. The
+ * relative error of a row is then of order 2^-12 (measured rel-L2 about
+ * 2e-4 against fp64 on random data, for any context length). */
 vc_status vc_verify_attn(const vc_attn_shape *shape, int32_t n_rows, const void *q, const void *k_new,
                          const void *v_new, const vc_kv_chunk *ctx, const int32_t *ctx_len, int32_t flags,
                          float *out, void *ws, size_t ws_bytes, hipStream_t stream);

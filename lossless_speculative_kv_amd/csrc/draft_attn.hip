@@ -16,7 +16,8 @@
 // order.
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
-// for bf16 rows). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
+// for the scores of bf16 rows, fp16 for every P x V: probabilities in fp16,
+// bf16 value rows converted exactly). NG = D/32 channel groups, W groups per MFMA row, NR = NG/W
 // row groups per head, HS = 16/NR query heads per head set, HPL = 4/NR heads
 // per lane row. The KIVI kernel takes the narrowest W with HS >= g (one head
 // set); the row kernel uses W = 1 and several head sets when g > HS.
@@ -181,7 +182,8 @@ constexpr int p_area_words() {
 }
 
 // Online softmax over one 32-token block of head set h and hand-over of the
-// probabilities to the PV operand layout.
+// probabilities, rounded to fp16 (11 significant bits), to the PV operand
+// layout.
 //   s[u][i]: score of head HPL*q + u, token 16i + t (log2 units, -inf for
 //            invalid tokens), bias[u] added on top;
 //   P[r]   : on return, the (token 4q' + r, token 4q' + r + 16) probability
@@ -189,7 +191,7 @@ constexpr int p_area_words() {
 // The max only moves when a score exceeds it by more than kRescaleThreshold
 // (so p <= 2^8), which makes the rescale of the accumulators rare; the
 // result is the same softmax.
-template <int D, int W, int NHS, bool BF16>
+template <int D, int W, int NHS>
 __device__ __forceinline__ void soft_block(DState<D, W, NHS>& st, int h, const float (&s)[Geo<D, W>::HPL][2],
                                            const float (&bias)[Geo<D, W>::HPL], int lane, uint32_t* lds_p,
                                            uint32_t (&P)[4]) {
@@ -232,7 +234,7 @@ __device__ __forceinline__ void soft_block(DState<D, W, NHS>& st, int h, const f
     const float mb = st.m[h][u] - bias[u];
     const float p0 = fast_exp2(s[u][0] - mb), p1 = fast_exp2(s[u][1] - mb);
     st.l[h][u] += p0 + p1;
-    lds_p[(h * HS + HPL * qg + u) * 16 + t] = pack16<BF16>(p0, p1);
+    lds_p[(h * HS + HPL * qg + u) * 16 + t] = pack_f16(p0, p1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -528,7 +530,7 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
   float s[HPL][2];
   row_scores<D, W>(c, Q.qscale, s);
   uint32_t Pp[4];
-  soft_block<D, W, 1, false>(st, 0, s, bias, lane, lds_p, Pp);
+  soft_block<D, W, 1>(st, 0, s, bias, lane, lds_p, Pp);
   // value scales into P~ (one per channel group of the column), value zero
   // points into zt
   uint32_t Pv[W][4];
@@ -560,7 +562,9 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
 // scaled by log2(e)/sqrt(D) after the MFMA.
 // lds: this wave's staging area for the value rows, 32 rows of D halfs with
 // a stride of D + 4 (so a block takes one trip to memory: keys and values
-// are loaded together, the V^T operand is then read from LDS).
+// are loaded together, the V^T operand is then read from LDS). Values are
+// staged in fp16 (bf16 rows converted on the way), so P x V runs on the f16
+// MFMA with fp16 probabilities.
 template <int D, int W, int NHS, bool BF16, typename RowFn>
 __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lane, float qscale,
                                           const uint32_t (&Aqm)[NHS][D / 32][4], DState<D, W, NHS>& st,
@@ -582,6 +586,12 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
       const int t = lane / CPR + RPI * u, c = lane % CPR;
       u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows.v(min(t, nvalid - 1), u) + 8 * c));
       if (t >= nvalid) v = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (BF16) {
+        // bf16 values to fp16 for the fp16 probabilities' product: exact
+        // for magnitudes 2^-17 .. 65504 (smaller ones round to 2^-24 steps)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pack_f16(__uint_as_float(v[e] << 16), __uint_as_float(v[e] & 0xFFFF0000u));
+      }
       uint32_t* d = reinterpret_cast<uint32_t*>(lds + t * LSTR + 8 * c);
       *reinterpret_cast<u32x2*>(d) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(d + 2) = u32x2{v[2], v[3]};
@@ -625,7 +635,7 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
       if (16 + n >= nvalid) s[u][1] = kNegInf;
     }
     const float bias[HPL] = {};
-    soft_block<D, W, NHS, BF16>(st, h, s, bias, lane, lds_p, Pv[h]);
+    soft_block<D, W, NHS>(st, h, s, bias, lane, lds_p, Pv[h]);
   }
 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -641,8 +651,8 @@ __device__ __forceinline__ void row_block(const RowFn& rows, int nvalid, int lan
     }
 #pragma unroll
     for (int h = 0; h < NHS; ++h)
-      st.acc[h][m] = mfma16<BF16>(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Pv[h][0], Pv[h][1], Pv[h][2], Pv[h][3]},
-                                  st.acc[h][m]);
+      st.acc[h][m] = mfma_f16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Pv[h][0], Pv[h][1], Pv[h][2], Pv[h][3]},
+                              st.acc[h][m]);
   }
 }
 

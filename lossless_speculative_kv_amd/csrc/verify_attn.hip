@@ -20,11 +20,19 @@
 //       rows XOR-swizzled in 16-byte units so the 16 rows of a read hit
 //       distinct banks), B = 16 query rows (registers, exact bf16).
 //   softmax: log2 domain; the 1/sqrt(D) * log2(e) scale is folded into the
-//       exponent's FMA; the row sums come from one more MFMA of P^T with a
-//       ones operand (the same bf16 probabilities as the numerator).
-//   PV: O^T[channel][row] += V^T[channel][token] * P^T[token][row]; the V^T
-//       operand comes straight from the row-major V tile through the gfx950
-//       transposing LDS read (four token slots of one channel per lane).
+//       exponent's FMA; the probabilities go to fp16 (11 significant bits;
+//       bf16's 8 leave a relative error of about 1e-3 in the output), and
+//       the row sums come from one more MFMA of P^T with a ones operand (the
+//       same fp16 probabilities as the numerator).
+//   PV: O^T[channel][row] += V^T[channel][token] * P^T[token][row] on
+//       v_mfma_f32_16x16x32_f16; the V^T operand comes straight from the
+//       row-major V tile through the gfx950 transposing LDS read (four token
+//       slots of one channel per lane). V tiles go to a ring of their own
+//       and are converted to fp16 in place once landed: by the two
+//       producers, which load V one step ahead of K so that the conversion
+//       has a whole step to finish, or with no producers by the waves that
+//       loaded them. The conversion's VALU work is what this costs (measured
+//       about 7% of the kernel with producers, 16% without).
 // The draft block (x_0..x_k's own keys/values) follows the context tiles of
 // the last split of the END call, with the causal mask (row j sees block
 // rows 0..j). Per-split partials (max, sum, unnormalised output) are folded
@@ -91,12 +99,12 @@ struct Segment {
 __device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Issue the direct-to-LDS load of 1 KB chunk c of the K (half 0) or V
-// (half 1) part of one tile. Lane l of chunk c fills LDS unit 64c + l, i.e.
+// (half 1) part of one tile into that half's ring slot dst. Lane l of chunk c fills LDS unit 64c + l, i.e.
 // row RPC*c + l / UPR, unit l % UPR, with the global unit that the swizzle
 // puts there. Every operand that is wave-uniform is made visibly so (the
 // buffer resource must sit in scalar registers).
 template <int D>
-__device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int tile, int lane, int half, int c) {
+__device__ __forceinline__ void issue_chunk(char* dst, const Segment& sg, int tile, int lane, int half, int c) {
   using T = Tile<D>;
   const uint64_t a = reinterpret_cast<uint64_t>(half ? sg.v : sg.k);
   const uint64_t au = ((uint64_t)uni((uint32_t)(a >> 32)) << 32) | uni((uint32_t)a);
@@ -104,7 +112,6 @@ __device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int 
       __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(au), (short)0, (int)uni(sg.bytes), 0x00020000);
   const int rb = (int)uni((uint32_t)sg.row_bytes), t0 = (int)uni((uint32_t)(tile * kTT));
   const int rl = lane / T::UPR, ul = lane % T::UPR;
-  char* dst = stage + half * T::KB;
   const int row = T::RPC * c + rl;
   const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 1024), 16, voff, 0, 0, kStreamPolicy);
@@ -117,7 +124,7 @@ __device__ __forceinline__ void issue_chunk(char* stage, const Segment& sg, int 
 // orders the data with explicit vmcnt waits and a barrier. M0 takes the
 // stage address (one wait state before the load reads it) and is restored.
 template <int D>
-__device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, int tile, int lane, int half,
+__device__ __forceinline__ void issue_chunk_asm(char* dst, const Segment& sg, int tile, int lane, int half,
                                                 int c) {
   using T = Tile<D>;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -130,7 +137,7 @@ __device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, 
   const int rl = lane / T::UPR, ul = lane % T::UPR;
   const int row = T::RPC * c + rl;
   const int voff = (t0 + row) * rb + swz<D>(row, ul) * 16;
-  const uint32_t m0 = uni(lds_addr(stage + half * T::KB + c * 1024));
+  const uint32_t m0 = uni(lds_addr(dst + c * 1024));
   // M0 is reserved to the compiler (a clobber of it is not honoured), so the
   // statement puts its value back after the load has read it
   uint32_t saved;
@@ -145,16 +152,33 @@ __device__ __forceinline__ void issue_chunk_asm(char* stage, const Segment& sg, 
       : "memory");
 }
 
-// A whole half of a tile: one producer wave per half.
+// A whole half of a tile: one producer wave per half. The producers also
+// convert landed V tiles in LDS while later loads are in flight, so they
+// issue the asm form (no wait for pending loads before their LDS accesses).
 template <int D>
-__device__ __forceinline__ void issue_half(char* stage, const Segment& sg, int tile, int lane, int half) {
+__device__ __forceinline__ void issue_half(char* dst, const Segment& sg, int tile, int lane, int half) {
 #pragma unroll
-  for (int c = 0; c < Tile<D>::CHUNKS; ++c) issue_chunk<D>(stage, sg, tile, lane, half, c);
+  for (int c = 0; c < Tile<D>::CHUNKS; ++c) issue_chunk_asm<D>(dst, sg, tile, lane, half, c);
 }
+
+// One landed 1 KB chunk of V rows to fp16 in place (16 bytes per lane). A
+// bf16 value converts exactly when 2^-17 <= |v| <= 65504; smaller ones
+// round to fp16's 2^-24 grid, larger ones become infinite.
+__device__ __forceinline__ void chunk_to_f16(char* chunk, int lane) {
+  u32x4* p = reinterpret_cast<u32x4*>(chunk + lane * 16);
+  const u32x4 w = *p;
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_f16(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u));
+  *p = o;
+}
+
+// lgkmcnt(0): this wave's LDS accesses have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Online-softmax state of RT row tiles. The row sums live in an MFMA
 // accumulator (lsum): P^T contracted with a ones operand, so each sum is
-// complete after the MFMA (no cross-lane reduction) and uses the same bf16
+// complete after the MFMA (no cross-lane reduction) and uses the same fp16
 // probabilities as the numerator.
 template <int RT, int MT>
 struct VState {
@@ -173,9 +197,15 @@ struct VState {
 };
 
 // Raw scores s (unscaled q.k, -inf where masked) of one tile become
-// p = 2^(s * qscale - m). The running max moves only when the tile's max
-// exceeds it by more than kRescaleThreshold (so p <= 2^8), which keeps the
-// accumulator rescale rare; the result is the same softmax.
+// p = 2^(s * qscale - m + kProbShift). The running max moves only when the
+// tile's max exceeds it by more than kRescaleThreshold, which keeps the
+// accumulator rescale rare; the result is the same softmax. The shift puts
+// the largest p (2^15) just inside fp16's range, so the fp16 probabilities
+// lose only terms below 2^-24, i.e. 2^-31 of the running max or less, and
+// keep 11 significant bits down to 2^-14 (2^-21 of the max). Numerator and
+// row sums carry the same factor 2^kProbShift, on every split alike.
+constexpr float kProbShift = 7.0f;
+static_assert(kRescaleThreshold + kProbShift <= 15.0f, "largest probability inside fp16's range");
 // Maximum that propagates NaN (v_maximum3_f32): unlike fmaxf it needs no
 // canonicalising of operands that come from the MFMA or a lane permute.
 // Scores are finite or -inf on every row whose result is kept.
@@ -213,7 +243,7 @@ __device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT
   for (int rt = 0; rt < RT; ++rt) {
     // a row that has seen no visible token yet (max still -inf) gets p = 0
     // from its -inf scores instead of 2^(-inf + inf)
-    const float nm = st.m[rt] == kNegInf ? 0.f : -st.m[rt];
+    const float nm = (st.m[rt] == kNegInf ? 0.f : -st.m[rt]) + kProbShift;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -221,22 +251,22 @@ __device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT
   }
 }
 
-// One 32-token tile for this wave's RT row tiles. nvalid masks tokens for
+// One 32-token tile for this wave's RT row tiles (K and V rows at kstage and
+// vstage; between() runs once the products are issued). nvalid masks tokens for
 // all rows; token t is visible to row tile rt's rows only when t <= lim[rt]
 // (the causal limit in the draft block, relative to the tile's first token;
 // large for context tiles).
-template <int D, int RT, bool MASK>
-__device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int lane,
+template <int D, int RT, bool MASK, typename Between>
+__device__ __forceinline__ void tile_compute(const char* kstage, const char* vstage, int nvalid, int lane,
                                              const uint32_t (&Bq)[RT][D / 32][4], const int (&lim)[RT],
-                                             float qscale, VState<RT, D / 16>& st) {
+                                             float qscale, VState<RT, D / 16>& st, Between&& between) {
   constexpr int NG = D / 32, MT = D / 16;
-  using T = Tile<D>;
   const int n = lane & 15, qg = lane >> 4;
   float s[RT][2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * i + n;
-    const char* kr = stage + row * (D * 2);
+    const char* kr = kstage + row * (D * 2);
     u32x4 A[NG];
 #pragma unroll
     for (int kk = 0; kk < NG; ++kk)
@@ -262,12 +292,12 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r >> 1, rr = 2 * (r & 1);
-      Bp[rt][r] = pack_bf16(s[rt][i][rr], s[rt][i][rr + 1]);
+      Bp[rt][r] = pack_f16(s[rt][i][rr], s[rt][i][rr + 1]);  // p <= 2^15
     }
   // V^T operand: lane n of slot group qg reads token 16h + 4qg + (n >> 2),
   // channels 16m + 4(n & 3) .. + 3; the transposing read hands lane n the
-  // four token slots of channel 16m + n.
-  const char* vbase = stage + T::KB;
+  // four token slots of channel 16m + n (V rows already in fp16).
+  const char* vbase = vstage;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     uint32_t A[4];
@@ -283,14 +313,15 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       st.acc[rt][m] =
-          mfma_bf16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]}, st.acc[rt][m]);
+          mfma_f16(u32x4{A[0], A[1], A[2], A[3]}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]}, st.acc[rt][m]);
     }
   }
-  constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+  constexpr uint32_t kOnes = 0x3C003C00u;  // two fp16 1.0
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
-    st.lsum[rt] = mfma_bf16(u32x4{kOnes, kOnes, kOnes, kOnes}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]},
-                            st.lsum[rt]);
+    st.lsum[rt] = mfma_f16(u32x4{kOnes, kOnes, kOnes, kOnes}, u32x4{Bp[rt][0], Bp[rt][1], Bp[rt][2], Bp[rt][3]},
+                           st.lsum[rt]);
+  between();  // work that can overlap the products still in flight
 }
 
 // Consumer waves compute, the last two waves load. Without PAIR, consumer
@@ -305,18 +336,30 @@ __device__ __forceinline__ void tile_compute(const char* stage, int nvalid, int 
 // wave issues a fixed share of each step's loads itself, AHEAD steps ahead,
 // and waits for its share of the current step before the step's barrier: the
 // two producer slots go to a fourth pair of row groups.
+//
+// V tiles travel one step ahead of the K tiles (AHEAD + 1 steps in flight),
+// in a ring one step deeper than the K ring: a slot that a step's V loads
+// overwrite held V that was read two steps earlier. The V producer waits
+// for the V of step st + 1 before the barrier of step st; between the
+// barriers of steps st - 1 and st both producers convert half of step st's
+// V chunks each to fp16 (an opening barrier covers step 0). With SELF, each
+// wave converts the V chunks of step sp + 1 that it loaded right after the
+// barrier of step sp.
 template <int D, int RT, bool PAIR, bool SELF>
 __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   static_assert(!SELF || PAIR, "consumer-issued loads come with wave pairs");
   constexpr int NG = D / 32, MT = D / 16;
   constexpr int TPS = PAIR ? 2 : 1;          // tiles per barrier step
-  constexpr int STAGES = PAIR ? 8 : 6;       // LDS ring depth in tiles
-  constexpr int AHEAD = STAGES / TPS - 2;    // steps in flight ahead of the one computed
+  constexpr int STAGES = PAIR ? 8 : 6;       // K ring depth in tiles
+  constexpr int VSTAGES = STAGES + TPS;      // V ring depth in tiles
+  constexpr int AHEAD = STAGES / TPS - 2;    // K steps in flight ahead of the one computed
   using T = Tile<D>;
   constexpr int SELF_WAVES = 8;
   constexpr int PER = TPS * 2 * T::CHUNKS / SELF_WAVES;  // 1 KB loads per consumer per step (SELF)
   static_assert(!SELF || PER * SELF_WAVES == TPS * 2 * T::CHUNKS, "even share of a step's loads");
-  __shared__ __attribute__((aligned(16))) char ring[STAGES * 2 * T::KB];
+  __shared__ __attribute__((aligned(16))) char ring[(STAGES + VSTAGES) * T::KB];
+  auto kslot = [&](int t) { return ring + (t % STAGES) * T::KB; };
+  auto vslot = [&](int t) { return ring + (STAGES + t % VSTAGES) * T::KB; };
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ncons = SELF ? SELF_WAVES : blockDim.x / 64 - 2;
   const int nw = ncons / TPS;  // row groups
@@ -347,37 +390,77 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   const int ntiles = s0.ntiles + s1.ntiles;
   const int nsteps = (ntiles + TPS - 1) / TPS;
 
-  // SELF: this wave's share of the loads of one step (chunk q of the step's
-  // tiles goes to wave q / PER); past the last tile the last one is loaded
-  // again into a stage no step reads
-  auto issue_share = [&](int step) {
+  // SELF: this wave's share of one step's loads: waves 4 ti .. 4 ti + 3
+  // load tile ti of the step, wave w the same PER / 2 consecutive chunks of
+  // its K rows and of its V rows, so every wave converts as many V chunks.
+  // A call for step s issues the K chunks of step s and the V chunks of step
+  // s + 1 (with V_ONLY, the V chunks of step s alone); past the last tile the
+  // last one is loaded again into a slot no step reads
+  static_assert(!SELF || (TPS == 2 && PER % 2 == 0 && (PER / 2) * 4 == T::CHUNKS), "SELF chunk shares");
+  auto share_chunk = [&](int i, int& ti, int& half, int& c) {
+    ti = wave >> 2;
+    half = i / (PER / 2);
+    c = (wave & 3) * (PER / 2) + i % (PER / 2);
+  };
+  auto issue_share = [&](int step, bool v_only) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int q = wave * PER + i;
-      const int ti = q / (2 * T::CHUNKS), half = (q / T::CHUNKS) % 2, c = q % T::CHUNKS;
-      int t = step * TPS + ti;
-      char* stage = ring + (t % STAGES) * 2 * T::KB;
+      int ti, half, c;
+      share_chunk(i, ti, half, c);
+      if (v_only && half == 0) continue;
+      int t = (step + (half && !v_only ? 1 : 0)) * TPS + ti;
+      char* dst = half ? vslot(t) : kslot(t);
       t = min(t, ntiles - 1);
-      if (t < s0.ntiles) issue_chunk_asm<D>(stage, s0, t, lane, half, c);
-      else issue_chunk_asm<D>(stage, s1, t - s0.ntiles, lane, half, c);
+      if (t < s0.ntiles) issue_chunk_asm<D>(dst, s0, t, lane, half, c);
+      else issue_chunk_asm<D>(dst, s1, t - s0.ntiles, lane, half, c);
+    }
+  };
+  // SELF: this wave's V chunks of a landed step to fp16
+  auto convert_share = [&](int step) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int ti, half, c;
+      share_chunk(i, ti, half, c);
+      const int t = step * TPS + ti;
+      if (half == 1 && t < ntiles) chunk_to_f16(vslot(t) + c * 1024, lane);
     }
   };
 
   if (!SELF && wave >= ncons) {
-    // producer: K (first) or V (second) halves, AHEAD steps ahead
+    // producer: K (first) or V (second) halves, AHEAD (K) or AHEAD + 1 (V)
+    // steps ahead
     const int half = wave - ncons;
     auto issue = [&](int t) {
-      char* stage = ring + (t % STAGES) * 2 * T::KB;
-      t = min(t, ntiles - 1);  // past the end: reload the last tile into an unused stage
-      if (t < s0.ntiles) issue_half<D>(stage, s0, t, lane, half);
-      else issue_half<D>(stage, s1, t - s0.ntiles, lane, half);
+      char* dst = half ? vslot(t) : kslot(t);
+      t = min(t, ntiles - 1);  // past the end: reload the last tile into an unused slot
+      if (t < s0.ntiles) issue_half<D>(dst, s0, t, lane, half);
+      else issue_half<D>(dst, s1, t - s0.ntiles, lane, half);
     };
     if (ntiles > 0) {
-      for (int t = 0; t < AHEAD * TPS; ++t) issue(t);
+      // K: steps 0 .. AHEAD - 1; V: steps 0 .. AHEAD, and V of step 0 landed
+      // before an opening barrier
+      for (int t = 0; t < (AHEAD + half) * TPS; ++t) issue(t);
+      if (half == 1) wait_vm<AHEAD * TPS * T::CHUNKS>();
+      __builtin_amdgcn_s_barrier();
       for (int st = 0; st < nsteps; ++st) {
 #pragma unroll
-        for (int i = 0; i < TPS; ++i) issue((st + AHEAD) * TPS + i);
-        wait_vm<AHEAD * TPS * T::CHUNKS>();  // step st landed
+        for (int i = 0; i < TPS; ++i) issue((st + AHEAD + half) * TPS + i);
+        // this producer's half of the chunks of step st's V tiles to fp16
+        // (they landed before the previous barrier)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+          const int t = st * TPS + i;
+          if (t < ntiles) {
+#pragma unroll
+            for (int c = half * (T::CHUNKS / 2); c < (half + 1) * (T::CHUNKS / 2); ++c)
+              chunk_to_f16(vslot(t) + c * 1024, lane);
+          }
+        }
+        // K of step st, or V of step st + 1, landed
+        wait_vm<AHEAD * TPS * T::CHUNKS>();
+        wait_lds();
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
       }
       wait_vm<0>();  // nothing may land after the workgroup has gone
@@ -412,6 +495,9 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
     }
   }
 
+  // consumers before producers at the instruction arbiter: the producers'
+  // V conversion has a whole step to finish and fills the issue gaps
+  if constexpr (!SELF) __builtin_amdgcn_s_setprio(1);
   VState<RT, MT> st;
   st.init();
   if constexpr (SELF) {
@@ -419,8 +505,13 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
     // does not see the ring's asm loads) has nothing left to wait for in the
     // loop
     wait_vm<0>();
-    if (ntiles > 0)
-      for (int sp = 0; sp < AHEAD; ++sp) issue_share(sp);
+    if (ntiles > 0) {
+      issue_share(0, true);
+      for (int sp = 0; sp < AHEAD; ++sp) issue_share(sp, false);
+      wait_vm<AHEAD * PER>();  // the V chunks of step 0
+      asm volatile("" ::: "memory");
+      convert_share(0);
+    }
   }
   // One step's barrier. SELF: issue step sp + AHEAD, wait until this wave's
   // share of step sp has landed, then a bare barrier (a workgroup fence would
@@ -428,10 +519,14 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   // keep the step's LDS reads below the barrier). Otherwise it pairs with the
   // producers' bare barrier; the fence keeps this step's LDS reads below it
   // (consumers have no loads in flight, so it costs nothing).
+  // In step sp, SELF converts its V chunks of step sp + 1 (landed with the K
+  // chunks of step sp) while the step's products run; those LDS accesses end
+  // before the next barrier.
   auto step_sync = [&](int sp) {
     if constexpr (SELF) {
-      issue_share(sp + AHEAD);
+      issue_share(sp + AHEAD, false);
       wait_vm<AHEAD * PER>();
+      wait_lds();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -439,6 +534,11 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
       __syncthreads();
     }
   };
+  auto convert_next = [&](int sp) {
+    if constexpr (SELF) convert_share(sp + 1);
+  };
+  if constexpr (!SELF)
+    if (ntiles > 0) __syncthreads();  // the producers' opening barrier
   // steps made of full context tiles need no mask; the partial last context
   // tile and the causal draft-block tiles follow in a second loop
   const int nfull_steps = (nval / kTT) / TPS;
@@ -448,20 +548,21 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   for (int sp = 0; sp < nfull_steps; ++sp) {
     step_sync(sp);
     const int t = sp * TPS + parity;
-    tile_compute<D, RT, false>(ring + (t % STAGES) * 2 * T::KB, kTT, lane, Bq, lim_all, P.qscale, st);
+    tile_compute<D, RT, false>(kslot(t), vslot(t), kTT, lane, Bq, lim_all, P.qscale, st, [&] { convert_next(sp); });
   }
   for (int sp = nfull_steps; sp < nsteps; ++sp) {
     step_sync(sp);
     const int t = sp * TPS + parity;
     if (t < ntiles) {
-      const char* stage = ring + (t % STAGES) * 2 * T::KB;
       const bool blk = t >= s0.ntiles;
       const int tb = t - s0.ntiles;
       int lim[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) lim[rt] = blk ? rowj[rt] - tb * kTT : kTT;
       const int nv = blk ? min(kTT, P.NR - tb * kTT) : min(kTT, nval - t * kTT);
-      tile_compute<D, RT, true>(stage, nv, lane, Bq, lim, P.qscale, st);
+      tile_compute<D, RT, true>(kslot(t), vslot(t), nv, lane, Bq, lim, P.qscale, st, [&] { convert_next(sp); });
+    } else {
+      convert_next(sp);
     }
   }
 

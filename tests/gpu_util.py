@@ -42,15 +42,23 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def assert_attention_close(gpu, ref, what=""):
+# Verification attention and the draft over bf16 rows (token drop, dense)
+# round their probabilities to fp16 (11 significant bits) and take bf16
+# values to fp16 exactly, so their rel-L2 error is of order 2^-12 (about
+# 1.5e-4 .. 2.3e-4 measured at every size); their checks use half the
+# general bound.
+FP16P_RL2 = 1e-3
+
+
+def assert_attention_close(gpu, ref, what="", rl2_max=2e-3):
     """Tolerance of the attention outputs: max |d| <= 1e-2 and rel-L2 <= 2e-3
-    against the fp64 oracle (bf16 inputs, fp32 accumulation)."""
+    (rl2_max) against the fp64 oracle (bf16 inputs, fp32 accumulation)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     mad = float(np.abs(gpu - ref).max())
     rl2 = rel_l2(gpu, ref)
-    assert mad <= 1e-2 and rl2 <= 2e-3, f"{what}: max|d| {mad:.3e} rel-L2 {rl2:.3e}"
+    assert mad <= 1e-2 and rl2 <= rl2_max, f"{what}: max|d| {mad:.3e} rel-L2 {rl2:.3e}"
     return mad, rl2
 
 
@@ -106,5 +114,5 @@ def check_verify_unit(eng, b: int, hk: int, rows_per_pass: int = 32):
     ref = np.concatenate([oracle.attend_prefix(Q[r0:r0 + rows_per_pass], K, V, nvis[r0:r0 + rows_per_pass])
                           for r0 in range(0, Q.shape[0], rows_per_pass)])
     worst = max(rel_l2(got[r], ref[r]) for r in range(Q.shape[0]))
-    mad, rl2 = assert_attention_close(got, ref, f"verify unit ({b}, {hk}) of {c.name}")
+    mad, rl2 = assert_attention_close(got, ref, f"verify unit ({b}, {hk}) of {c.name}", rl2_max=FP16P_RL2)
     return mad, rl2, worst

@@ -20,7 +20,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from tests.gpu_util import assert_attention_close, check_argmax_chunked, check_verify_unit, log  # noqa: E402
+from tests.gpu_util import (FP16P_RL2, assert_attention_close, check_argmax_chunked, check_verify_unit,  # noqa: E402
+                            log)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +97,7 @@ def test_verify_attention(eng):
         log(f"full size verify: sequence {b} head {h} row {j}, context {n}")
         Ka, Va = np.concatenate([K, kn[:j + 1]]), np.concatenate([V, vn[:j + 1]])
         ref = oracle.attend(bf16_to_f64(eng.qv[j, b, h]), Ka, Va)
-        assert_attention_close(o[j, b, h], ref, f"verify ({b}, {h}, row {j})")
+        assert_attention_close(o[j, b, h], ref, f"verify ({b}, {h}, row {j})", rl2_max=FP16P_RL2)
 
 
 def test_draft_vocab_argmax(eng):

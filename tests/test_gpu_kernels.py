@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from tests.gpu_util import (assert_attention_close, bf16_tensor, ctx_rows, f16_dev, log,  # noqa: E402
-                            to_dev)
+                            to_dev, FP16P_RL2)
 
 pytestmark = pytest.mark.gpu
 
@@ -288,7 +288,7 @@ def test_draft_rows_parity(L, case):
     out = run_draft(L, sh, kv, bf16_tensor(q)).cpu().numpy()
     g = Hq // Hkv
     ref = np.stack([np.stack([oracle.attend(q[b, h], *vis[b, h // g]) for h in range(Hq)]) for b in range(B)])
-    mad, rl2 = assert_attention_close(out, ref, f"rows {case}")
+    mad, rl2 = assert_attention_close(out, ref, f"rows {case}", rl2_max=FP16P_RL2)
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
 
 
@@ -365,7 +365,7 @@ def test_verify_parity(L, case):
             for j in range(NR):
                 vis[j, ctx[b]:ctx[b] + j + 1] = True
             ref[:, b, h] = oracle.attend_masked(q[:, b, h], Kall, Vall, vis)
-    mad, rl2 = assert_attention_close(got, ref, f"verify {case}")
+    mad, rl2 = assert_attention_close(got, ref, f"verify {case}", rl2_max=FP16P_RL2)
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
 
 

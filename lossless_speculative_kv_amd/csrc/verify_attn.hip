@@ -32,7 +32,7 @@
 //       producers, which load V one step ahead of K so that the conversion
 //       has a whole step to finish, or with no producers by the waves that
 //       loaded them. The conversion's VALU work is what this costs (measured
-//       about 7% of the kernel with producers, 16% without).
+//       about 6% of the kernel with producers, 16% without).
 // The draft block (x_0..x_k's own keys/values) follows the context tiles of
 // the last split of the END call, with the causal mask (row j sees block
 // rows 0..j). Per-split partials (max, sum, unnormalised output) are folded
@@ -360,8 +360,18 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   __shared__ __attribute__((aligned(16))) char ring[(STAGES + VSTAGES) * T::KB];
   auto kslot = [&](int t) { return ring + (t % STAGES) * T::KB; };
   auto vslot = [&](int t) { return ring + (STAGES + t % VSTAGES) * T::KB; };
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ncons = SELF ? SELF_WAVES : blockDim.x / 64 - 2;
+  // Roles. With eight waves the producers take waves 0 and 4, which share a
+  // SIMD when waves go round-robin to the four SIMDs: the other three SIMDs
+  // then hold two consumers each (the most any SIMD holds anyway) and the
+  // producers' V conversion runs beside no consumer; waves 1, 2, 3 are
+  // consumers 0, 1, 2 and waves 5, 6, 7 consumers 4, 5, 3, so the two waves
+  // of a SIMD belong to different row groups. Otherwise the producers are
+  // the last two waves. wave: the consumer index 0 .. ncons - 1.
+  const bool eight = !SELF && ncons == 6;
+  const bool producer = eight ? (hw & 3) == 0 : (!SELF && hw >= ncons);
+  const int wave = !eight ? hw : hw < 4 ? hw - 1 : 3 + (hw - 4) % 3;
   const int nw = ncons / TPS;  // row groups
   const int grp = wave % nw, parity = wave / nw;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -426,10 +436,10 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
     }
   };
 
-  if (!SELF && wave >= ncons) {
+  if (producer) {
     // producer: K (first) or V (second) halves, AHEAD (K) or AHEAD + 1 (V)
     // steps ahead
-    const int half = wave - ncons;
+    const int half = eight ? hw >> 2 : hw - ncons;
     auto issue = [&](int t) {
       char* dst = half ? vslot(t) : kslot(t);
       t = min(t, ntiles - 1);  // past the end: reload the last tile into an unused slot

@@ -427,8 +427,10 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
 // from HBM once at full rate while the MFMA work per byte of LDS stays high.
 // Switched off: on its first run (M = 33, three row tiles) this kernel made
 // the GPU report an illegal memory access, and again after the reads of
-// rows-less waves were removed; the cause is not found yet, so the plan never
-// selects it and the staged kernel serves every M above 32.
+// rows-less waves were removed; the cause is not found (every address it
+// forms for that shape is in range, and its built loop reuses no register of
+// an in-flight LDS read before the wait), so the plan never selects it: the
+// ring kernel serves M 33 .. 416.
 constexpr bool kTiledEnabled = false;
 constexpr int kTiledWaves = 8;
 constexpr int kTVG = 4;              // vocab groups of 64 rows

@@ -14,7 +14,7 @@ so bench.py reports them only while the source is unchanged):
     rocprofv3 --pmc WRITE_SIZE -d <runs>/pmc_write_<w> -o run -- python3 -u bench.py <args>
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
               SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE -d <runs>/pmc_mfma_<w> -o run -- python3 -u bench.py <args>
-    <args> = --workload <w> --steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none
+    <args> = --workload <w> --steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none --p1 none --pipeline none
 
 The counters are scaled by a plain device copy of known size (bench.py
 --copy-calibration 256, one FETCH_SIZE and one WRITE_SIZE pass into
@@ -33,13 +33,13 @@ import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
-BENCH_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none"
+BENCH_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none --p1 none --pipeline none"
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
                  "GRBM_GUI_ACTIVE")
 # hot-path kernels and the source file each is built from
 SOURCES = {"draft_kivi_kernel": "draft_attn.hip", "draft_rows_kernel": "draft_attn.hip",
            "verify_kernel": "verify_attn.hip", "verify_merge_kernel": "verify_attn.hip",
-           "vocab_staged_kernel": "vocab.hip", "vocab_stream_kernel": "vocab.hip",
+           "vocab_staged_kernel": "vocab.hip", "vocab_stream_kernel": "vocab.hip", "vocab_ring_kernel": "vocab.hip",
            "vocab_reduce_kernel": "vocab.hip", "kivi_quantize_kernel": "round_ops.hip"}
 HEADER = ("Run from the repository root on one MI355X (after `cd /tmp && export TMPDIR=/tmp`, with absolute paths to "
           "the repository); summarised by `python -m lossless_speculative_kv_amd.profsum --workload {w}`:\n\n")
@@ -78,8 +78,8 @@ def counters(runs: str, d: str, cname: str) -> dict:
     return out
 
 
-def summarise(w: str, runs: str) -> None:
-    os.makedirs(PROFILES, exist_ok=True)
+def summarise(w: str, runs: str, out: str = PROFILES) -> None:
+    os.makedirs(out, exist_ok=True)
     args = f"--workload {w} {BENCH_ARGS}"
     head = HEADER.format(w=w)
     # ---- kernel trace
@@ -94,13 +94,14 @@ def summarise(w: str, runs: str) -> None:
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{k}` | {len(v)} | {sum(v):.1f} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
                      f"{min(v):.2f} | {max(v):.2f} | {100 * sum(v) / tot:.2f} |\n")
-    with open(os.path.join(PROFILES, f"kernels_{w}.md"), "w") as f:
+    with open(os.path.join(out, f"kernels_{w}.md"), "w") as f:
         f.write("".join(lines))
     trace_avg = {k: statistics.mean(v) for k, v in by.items()}
 
     # ---- HBM traffic
-    tpath = os.path.join(PROFILES, "traffic.json")
-    table = json.load(open(tpath)) if os.path.exists(tpath) else {"kernels": {}}
+    tpath = os.path.join(out, "traffic.json")
+    tsrc = tpath if os.path.exists(tpath) else os.path.join(PROFILES, "traffic.json")
+    table = json.load(open(tsrc)) if os.path.exists(tsrc) else {"kernels": {}}
     copy_bytes = 256 * 1024 * 1024
     try:
         cf, cw = counters(runs, "pmc_cfetch", "FETCH_SIZE"), counters(runs, "pmc_cwrite", "WRITE_SIZE")
@@ -140,7 +141,7 @@ def summarise(w: str, runs: str) -> None:
                                            "fetch_bytes": rb, "write_bytes": wb, "launches": len(fe[k])}
     with open(tpath, "w") as f:
         json.dump(table, f, indent=1)
-    with open(os.path.join(PROFILES, f"hbm_traffic_{w}.md"), "w") as f:
+    with open(os.path.join(out, f"hbm_traffic_{w}.md"), "w") as f:
         f.write("".join(lines))
 
     # ---- MFMA utilisation
@@ -174,7 +175,7 @@ def summarise(w: str, runs: str) -> None:
         t = trace_avg.get(k)
         tf = fl / (t * 1e-6) / 1e12 if t else float("nan")
         lines.append(f"| `{k}` | {fl / 1e9:.2f} G | {cyc:.0f} | {100 * busy:.1f}% | {tf:.0f} | {100 * tf / 2500:.1f}% |\n")
-    with open(os.path.join(PROFILES, f"mfma_{w}.md"), "w") as f:
+    with open(os.path.join(out, f"mfma_{w}.md"), "w") as f:
         f.write("".join(lines))
 
 
@@ -182,8 +183,9 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--runs", default=os.path.join(ROOT, "gpurun_out"))
+    ap.add_argument("--out", default=PROFILES, help="folder for the summaries and traffic.json (default profiles/)")
     a = ap.parse_args()
-    summarise(a.workload, a.runs)
+    summarise(a.workload, a.runs, a.out)
     print(f"profiles for {a.workload} written")
 
 

@@ -9,20 +9,16 @@
 // 16-byte pieces): lane group qg takes k = k0 + 32*kk + 8*qg + s in K-step kk
 // (the B operand uses the same permutation).
 //
-// Three kernels share the epilogue:
-//  * vocab_stream: M <= 16*MS rows (draft steps). Each wave owns 16*NA vocab
-//    rows; W goes straight from HBM to registers, h (tiny) from L2: fp32
-//    rounded to bf16 in registers for one m-tile, else the bf16 copy.
-//    A workgroup of 8 waves fills a CU and its waves are paced.
-//  * vocab_ring: 33 <= M <= 416 (verification). 8 waves = 4 vocab groups x
-//    2 row groups; W and hidden rows pass through an LDS ring of
+// Two kernels share the epilogue:
+//  * vocab_stream: M <= 32 rows (draft steps). Each workgroup takes an equal
+//    share of the vocabulary tiles (one per CU), each wave up to NA tiles of
+//    16 rows; W goes straight from HBM to registers, h (tiny) from L2: fp32
+//    rounded to bf16 in registers up to 8 rows, else the bf16 copy. A
+//    workgroup of 8 waves fills a CU and its waves are paced.
+//  * vocab_ring: 33 <= M <= 448 (verification). 8 waves = VG vocab groups x
+//    8 / VG row groups; W and hidden rows pass through an LDS ring of
 //    direct-to-LDS loads that every wave issues its share of.
-//  * vocab_staged: M above 416. Each wave owns 32 vocab rows and all M rows; the
-//    hidden rows are staged in LDS in 32-wide k chunks (double-buffered) and
-//    shared by the 8 waves of the workgroup, so W is read from HBM exactly
-//    once. Up to 18 row tiles the loads run ahead: the next W chunk and the
-//    hidden chunk after it are in registers while the current one is
-//    multiplied.
+// (A third, switched-off kernel is kept below: vocab_tiled.)
 // Argmax: each workgroup reduces (logit, index) to one 64-bit key per row,
 // key = ordered(logit) << 32 | ~index, whose maximum is the largest logit with
 // the lowest index (-0 is folded to +0); a second kernel takes the max over
@@ -88,10 +84,11 @@ __global__ __launch_bounds__(256) void hidden_to_bf16_kernel(const VocabParams P
 
 // Reduce the per-wave candidates (vocab tile a, m-tile mt) into keys per row
 // and write the optional logits. acc[a][mt][r]: logit of vocab row
-// vbase + 16*a + 4*qg + r and hidden row 16*mt_row + n.
+// vbase + 16*a + 4*qg + r and hidden row 16*mt_row + n; vocab rows from vlim
+// on (past the vocabulary, or past the caller's share of it) are skipped.
 template <int NA, int NMT>
 __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc)[NA][NMT], int vbase,
-                                         const int (&mrow)[NMT], int lane, uint64_t (&best)[NMT]) {
+                                         const int (&mrow)[NMT], int lane, uint64_t (&best)[NMT], int vlim) {
   const int n = lane & 15, qg = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
@@ -102,7 +99,7 @@ __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = vbase + 16 * a + 4 * qg + r;
-        if (v < P.V) {
+        if (v < vlim) {
           const uint64_t k = make_key(acc[a][mt][r], v);
           bk = k > bk ? k : bk;
         }
@@ -113,12 +110,12 @@ __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc
       for (int a = 0; a < NA; ++a) {
         const int v0 = vbase + 16 * a + 4 * qg;
         float* dst = P.logits + (size_t)m * P.V + v0;
-        if (v0 + 3 < P.V && (P.V & 3) == 0) {
+        if (v0 + 3 < vlim && (P.V & 3) == 0) {
           *reinterpret_cast<f32x4*>(dst) = acc[a][mt];
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (v0 + r < P.V) dst[r] = acc[a][mt][r];
+            if (v0 + r < vlim) dst[r] = acc[a][mt][r];
         }
       }
     }
@@ -132,11 +129,20 @@ constexpr int kStreamWaves = 8;
 
 // NA vocab tiles of 16 rows per wave (the plan picks NA per vocabulary size
 // so that the workgroups fill the CUs in as few rounds as possible).
-template <int MS, int NA>
+template <int MS, int NA, bool ROUND>
 __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(const VocabParams P) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
-  const int vbase = (blockIdx.x * kStreamWaves + wave) * 16 * NA;
+  // this workgroup's share of the vocabulary tiles of 16 rows: tiles
+  // [t_lo, t_hi), an equal share (within one tile) of every workgroup's, so
+  // the grid can match the compute units; wave w takes NA of them from
+  // t_lo + NA w (slots past t_hi load tile t_hi - 1 again, an L2 hit, and
+  // store nothing)
+  const long ntv = (P.V + 15) / 16;
+  const int t_lo = (int)(blockIdx.x * ntv / gridDim.x), t_hi = (int)((blockIdx.x + 1) * ntv / gridDim.x);
+  const int tfirst = t_lo + wave * NA;
+  const int vbase = tfirst * 16;
+  const int vlim = min(P.V, t_hi * 16);
   __shared__ __attribute__((aligned(16))) int progress[8];  // k-steps of 256 each wave has started
   if (threadIdx.x < 8) progress[threadIdx.x] = 0;
   __syncthreads();
@@ -150,15 +156,19 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
   bool wok[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const int v = vbase + 16 * a + n;
+    const int v = min(tfirst + a, t_hi - 1) * 16 + n;
     wok[a] = v < P.V;
     wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K + 8 * qg;
   }
-  // With one m-tile the hidden rows are read as fp32 (L2 hits: every wave
-  // reads them) and rounded to bf16 (nearest even) in registers; a row past
-  // M reads row M - 1 and only feeds keys and logits that are never written.
-  // Two m-tiles read the bf16 copy (the fp32 registers would spill).
-  constexpr bool kRound = MS == 1;
+  // ROUND (one m-tile, at most 8 rows): the hidden rows are read as fp32
+  // (L2 hits: every wave reads them) and rounded to bf16 (nearest even) in
+  // registers, which saves the conversion kernel; a row past M reads row
+  // M - 1 and only feeds keys and logits that are never written. Otherwise
+  // the bf16 copy is read: half the bytes of fp32 per wave, which at 16 rows
+  // is worth the conversion (Qwen-32B draft step, M = 16: 309 -> 283 us) and
+  // with two m-tiles keeps the registers from spilling.
+  static_assert(!ROUND || MS == 1, "rounding in registers with one m-tile");
+  constexpr bool kRound = ROUND;
   using HRaw = std::conditional_t<kRound, f32x4[MS][4][2], u32x4[MS][4]>;
   const float* hrow[MS];
   const uint16_t* hrow16[MS];
@@ -222,9 +232,9 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
   };
   u32x4 Aa[NA][4], Ab[NA][4], B[MS][4];
   HRaw H;
-  // a wave past the last vocab row has nothing to stream (and must not lead
-  // the pacing)
-  if (vbase < P.V) {
+  // a wave past its workgroup's share has nothing to stream (and must not
+  // lead the pacing)
+  if (tfirst < t_hi) {
     load(Aa, 0);
     int k0 = 0;
     // (the scheduling barriers keep the W loads issued before the hidden
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
 #pragma unroll
   for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
   uint64_t best[MS];
-  epilogue<NA, MS>(P, acc, vbase, mrow, lane, best);
+  epilogue<NA, MS>(P, acc, vbase, mrow, lane, best, vlim);
   __shared__ uint64_t red[kStreamWaves][16 * MS];
 #pragma unroll
   for (int t = 0; t < MS; ++t)
@@ -263,156 +273,6 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
     uint64_t k = red[0][m];
 #pragma unroll
     for (int w = 1; w < kStreamWaves; ++w) k = red[w][m] > k ? red[w][m] : k;
-    P.keys[(size_t)blockIdx.x * P.M + m] = k;
-  }
-}
-
-// Staged kernel: 8 waves x 32 vocab rows; all m-tiles (NMT >= ceil(M/16)).
-constexpr int kStagedWaves = 8;
-constexpr int kKC = 32;  // k per LDS stage (one MFMA K-step)
-
-template <int NMT>
-__global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) {
-  constexpr int NA = 2, HSTR = kKC + 8;  // halfs per staged hidden row (16-byte aligned, skewed)
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  uint16_t* hs = reinterpret_cast<uint16_t*>(smem_raw);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, qg = lane >> 4;
-  const int mtiles = P.Mp / 16;
-  const int vbase = (blockIdx.x * kStagedWaves + wave) * 32;
-  f32x4 acc[NA][NMT];
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int t = 0; t < NMT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wrow[NA];
-  bool wok[NA];
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    const int v = vbase + 16 * a + n;
-    wok[a] = v < P.V;
-    wrow[a] = P.w + (size_t)(wok[a] ? v : 0) * P.K;
-  }
-  const int stage_halfs = P.Mp * HSTR;
-  // cooperative copy of hidden chunk [Mp][kKC] into LDS buffer `buf`
-  auto stage = [&](int k0, int buf) {
-    uint16_t* dst = hs + buf * stage_halfs;
-    const int chunks = P.Mp * (kKC / 8);
-    for (int c = threadIdx.x; c < chunks; c += 64 * kStagedWaves) {
-      const int m = c / (kKC / 8), x = c % (kKC / 8);
-      *reinterpret_cast<u32x4*>(dst + m * HSTR + 8 * x) =
-          *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x);
-    }
-  };
-  // W for one chunk: lane group qg of K-step kk reads k0 + 32*kk + 8*qg (with the other lane
-  // groups, 64 contiguous bytes of each row per instruction)
-  constexpr int KS = kKC / 32;  // K-steps per chunk
-  // (unconditional loads: a row past the vocabulary reads row 0 and only
-  // feeds logits the epilogue skips; a load under a per-lane condition, or
-  // masked right after it, is waited for at once)
-  auto load_w = [&](u32x4 (&A)[NA][KS], int k0) {
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) A[a][kk] = *reinterpret_cast<const u32x4*>(wrow[a] + k0 + 32 * kk + 8 * qg);
-  };
-  auto compute = [&](const u32x4 (&A)[NA][KS], const uint16_t* cur) {
-#pragma unroll
-    for (int t = 0; t < NMT; ++t) {
-      if (t < mtiles) {
-        const uint16_t* hr = cur + (16 * t + n) * HSTR + 8 * qg;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const u32x4 B = *reinterpret_cast<const u32x4*>(hr + 32 * kk);
-#pragma unroll
-          for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a][kk], B, acc[a][t]);
-        }
-      }
-    }
-  };
-  const int nk = P.K / kKC;
-  if constexpr (NMT <= 18) {
-    // Pipelined: W chunks double-buffered in registers, and the hidden chunk
-    // two ahead loaded into registers while the current one is multiplied,
-    // then written to its LDS buffer one iteration later (so neither load's
-    // latency sits between two barriers).
-    constexpr int HPT = (16 * NMT * (kKC / 8) + 64 * kStagedWaves - 1) / (64 * kStagedWaves);
-    u32x4 hreg[HPT];
-    const int chunks = P.Mp * (kKC / 8);
-    // (a slot past the chunk loads the chunk's last unit and is not stored)
-    auto hload = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        const int c = min((int)threadIdx.x + i * 64 * kStagedWaves, chunks - 1);
-        const int m = c / (kKC / 8), x = c % (kKC / 8);
-        hreg[i] = *reinterpret_cast<const u32x4*>(P.hb + (size_t)m * P.K + k0 + 8 * x);
-      }
-    };
-    auto hstore = [&](int buf) {
-      uint16_t* dst = hs + buf * stage_halfs;
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        const int c = threadIdx.x + i * 64 * kStagedWaves;
-        const int m = c / (kKC / 8), x = c % (kKC / 8);
-        if (c < chunks) *reinterpret_cast<u32x4*>(dst + m * HSTR + 8 * x) = hreg[i];
-      }
-    };
-    // W chunks in three register sets, loaded two chunks ahead (one chunk
-    // ahead left the kernel bound by the loads' latency)
-    // The loads of a chunk go out hidden first, then W: waiting for a hidden
-    // chunk one iteration later (vector-memory loads complete in issue
-    // order) then leaves that chunk's W loads in flight.
-    u32x4 Aa[NA][KS], Ab[NA][KS], Ac[NA][KS];
-    hload(0);
-    hstore(0);
-    if (nk > 1) hload(kKC);
-    load_w(Aa, 0);
-    if (nk > 1) load_w(Ab, kKC);
-    __syncthreads();
-    // iteration kc: hidden kc + 1 -> LDS; hidden and W of kc + 2 issued; W of
-    // kc + 1 still in flight
-    auto iter = [&](const u32x4 (&Acur)[NA][KS], u32x4 (&Aload)[NA][KS], int kc) {
-      if (kc + 1 < nk) hstore((kc + 1) & 1);
-      if (kc + 2 < nk) {
-        hload((kc + 2) * kKC);
-        load_w(Aload, (kc + 2) * kKC);
-      }
-      compute(Acur, hs + (kc & 1) * stage_halfs);
-      __syncthreads();
-    };
-    int kc = 0;
-    for (; kc + 3 <= nk; kc += 3) {
-      iter(Aa, Ac, kc);
-      iter(Ab, Aa, kc + 1);
-      iter(Ac, Ab, kc + 2);
-    }
-    if (kc < nk) iter(Aa, Ac, kc);
-    if (kc + 1 < nk) iter(Ab, Aa, kc + 1);
-  } else {
-    stage(0, 0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-      u32x4 A[NA][KS];
-      load_w(A, kc * kKC);
-      if (kc + 1 < nk) stage((kc + 1) * kKC, (kc + 1) & 1);
-      compute(A, hs + (kc & 1) * stage_halfs);
-      __syncthreads();
-    }
-  }
-  int mrow[NMT];
-#pragma unroll
-  for (int t = 0; t < NMT; ++t) mrow[t] = 16 * t;
-  uint64_t best[NMT];
-  epilogue<NA, NMT>(P, acc, vbase, mrow, lane, best);
-  // cross-wave reduction through LDS (reuses the staging area)
-  uint64_t* red = reinterpret_cast<uint64_t*>(smem_raw);
-#pragma unroll
-  for (int t = 0; t < NMT; ++t)
-    if (qg == 0 && t < mtiles) red[wave * P.Mp + 16 * t + n] = best[t];
-  __syncthreads();
-  for (int m = threadIdx.x; m < P.M; m += 64 * kStagedWaves) {
-    uint64_t k = red[m];
-    for (int w = 1; w < kStagedWaves; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
     P.keys[(size_t)blockIdx.x * P.M + m] = k;
   }
 }
@@ -430,7 +290,7 @@ __global__ __launch_bounds__(512) void vocab_staged_kernel(const VocabParams P) 
 // rows-less waves were removed; the cause is not found (every address it
 // forms for that shape is in range, and its built loop reuses no register of
 // an in-flight LDS read before the wait), so the plan never selects it: the
-// ring kernel serves M 33 .. 416.
+// ring kernel serves M 33 .. 448.
 constexpr bool kTiledEnabled = false;
 constexpr int kTiledWaves = 8;
 constexpr int kTVG = 4;              // vocab groups of 64 rows
@@ -546,7 +406,7 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
 #pragma unroll
   for (int t = 0; t < NMT2; ++t) mrow[t] = 16 * (mg * NMT2 + t);
   uint64_t best[NMT2];
-  epilogue<NA, NMT2>(P, acc, vwg + 64 * vg, mrow, lane, best);
+  epilogue<NA, NMT2>(P, acc, vwg + 64 * vg, mrow, lane, best, P.V);
   // reduce over the 4 vocab groups of each row through LDS (the ring is idle)
   uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [kTVG][Mp]
 #pragma unroll
@@ -561,19 +421,24 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
   }
 }
 
-// Ring kernel (up to 26 row tiles): the verification product, MFMA-bound at
-// large M. 8 waves = 4 vocab groups of 64 rows x 2 row groups of NT row
-// tiles; a workgroup covers 256 vocab rows and all Mp hidden rows, so each W
-// row is read from HBM once, and W and the hidden rows move in 32-wide k
-// slices through a ring of STAGES = AHEAD + 2 LDS stages. Every wave issues
-// a fixed share of each stage's direct-to-LDS loads (1 KB each: 16 rows x
-// 64 bytes), AHEAD stages ahead, waits for its share of the current stage
-// and meets the others at a bare barrier. The loads are asm statements
+// Ring kernel (up to 28 row tiles): the verification product, MFMA-bound at
+// large M. 8 waves = VG vocab groups of 64 rows x 8 / VG row groups of NT
+// row tiles; a workgroup covers 64 VG vocab rows and all Mp hidden rows, so
+// each W row is read from HBM once, and W and the hidden rows move in
+// 32-wide k slices through a ring of STAGES = AHEAD + 1 LDS stages. Every
+// wave issues a fixed share of each stage's direct-to-LDS loads (1 KB each:
+// 16 rows x 64 bytes), AHEAD stages ahead: it waits for its share of the
+// current stage, meets the others at a bare barrier and then issues the
+// loads of stage s + AHEAD into the slot of stage s - 1, which everyone has
+// finished reading (one stage more in flight than issuing before the
+// barrier: M = 416 815 -> 779 us). The loads are asm statements
 // (the compiler does not count them as pending LDS writes, so it inserts no
 // vmcnt(0) before the ring reads) and the ring is read with plain LDS loads
 // (16 bytes per lane, one row per lane, XOR-swizzled pieces so that each
 // eight lanes hit distinct banks). Per stage a wave multiplies its 4 vocab
 // tiles by its NT row tiles: 4 + NT operand reads for 4 * NT MFMAs.
+// Counters (M = 416): 8 LDS-active cycles per 16-byte read instruction, half
+// of them counted as bank conflicts, whatever the swizzle; MFMA busy 32%.
 // A stage reads 64 bytes of each 128-byte line of a W row; the loads keep the
 // default cache policy, so the line's other half is an L2 hit one stage
 // later (with non-temporal W loads each line was fetched from HBM twice:
@@ -581,17 +446,18 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
 // rows sit in a k-slice-major copy, so a stage's hidden part is one
 // contiguous block.
 constexpr int kRingWaves = 8;
-constexpr int kRingRows = 256;  // vocab rows per workgroup
-constexpr int kRingWch = 16;    // W chunks per stage
-
-template <int NT>
+// VG vocab groups of 64 rows x (8 / VG) row groups of NT row tiles
+template <int NT, int VG>
 struct RingGeo {
-  static constexpr int HCH = 2 * NT;                          // hidden chunks per stage
-  static constexpr int NCH = kRingWch + HCH;                  // chunks per stage
+  static constexpr int RG = kRingWaves / VG;                  // row groups
+  static constexpr int ROWS = 64 * VG;                        // vocab rows per workgroup
+  static constexpr int WCH = 4 * VG;                          // W chunks per stage
+  static constexpr int HCH = RG * NT;                         // hidden chunks per stage
+  static constexpr int NCH = WCH + HCH;                       // chunks per stage
   static constexpr int PER = (NCH + kRingWaves - 1) / kRingWaves;  // loads per wave per stage
   static constexpr int SB = NCH * 1024;                       // bytes per stage
-  static constexpr int AHEAD = NT <= 2 ? 4 : NT <= 5 ? 3 : NT <= 9 ? 2 : 1;
-  static constexpr int STAGES = AHEAD + 2;
+  static constexpr int STAGES = (150 * 1024) / SB < 8 ? (150 * 1024) / SB : 8;
+  static constexpr int AHEAD = STAGES - 1;
   static_assert(STAGES * SB <= 150 * 1024, "ring fits the LDS");
   static_assert(AHEAD * PER < 64, "vmcnt range");
 };
@@ -618,15 +484,15 @@ __device__ __forceinline__ void ring_dma(const int (&rsrc)[4], uint32_t m0, int 
       : "memory");
 }
 
-template <int NT>
+template <int NT, int VG>
 __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const VocabParams P) {
-  using G = RingGeo<NT>;
+  using G = RingGeo<NT, VG>;
   constexpr int NA = 4;
   __shared__ __attribute__((aligned(1024))) char ring[G::STAGES * G::SB];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
-  const int vg = wave % 4, mg = wave / 4;
-  const int vwg = blockIdx.x * kRingRows;
+  const int vg = wave % VG, mg = wave / VG;
+  const int vwg = blockIdx.x * G::ROWS;
   const int mtiles = P.Mp / 16;
   const int nk = P.K / 32;
   const int mt0 = mg * NT;  // first row tile of this wave's row group
@@ -634,7 +500,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   // workgroup's W rows (rows past the vocabulary read as zero) and the
   // padded bf16 hidden rows
   const uint64_t wb = reinterpret_cast<uint64_t>(P.w) + (uint64_t)vwg * (uint64_t)P.K * 2u;
-  const uint32_t wrows = (uint32_t)min(kRingRows, P.V - vwg);
+  const uint32_t wrows = (uint32_t)min(G::ROWS, P.V - vwg);
   const int rw[4] = {(int)__builtin_amdgcn_readfirstlane((uint32_t)wb),
                      (int)(__builtin_amdgcn_readfirstlane((uint32_t)(wb >> 32)) & 0xFFFFu),
                      (int)__builtin_amdgcn_readfirstlane(wrows * (uint32_t)P.K * 2u), 0x00020000};
@@ -658,13 +524,13 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
 #pragma unroll
     for (int i = 0; i < G::PER; ++i) {
       const int q = min(wave * G::PER + i, G::NCH - 1);  // wave-uniform
-      const int hsrc = min(q - kRingWch, mtiles - 1);     // hidden chunk whose rows are read
-      const int row = 16 * (q < kRingWch ? q : hsrc) + lrow;
+      const int hsrc = min(q - G::WCH, mtiles - 1);       // hidden chunk whose rows are read
+      const int row = 16 * (q < G::WCH ? q : hsrc) + lrow;
       // W rows are row-major; the hidden copy is k-slice-major ([K/32][Mp][32])
       const int voff =
-          (q < kRingWch ? (row * P.K + k0) * 2 : ((k0 / 32) * P.Mp + row) * 64) + 16 * ring_piece(row, lpos);
+          (q < G::WCH ? (row * P.K + k0) * 2 : ((k0 / 32) * P.Mp + row) * 64) + 16 * ring_piece(row, lpos);
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + (uint32_t)q * 1024u);
-      if (q < kRingWch) ring_dma(rw, m0, voff);
+      if (q < G::WCH) ring_dma(rw, m0, voff);
       else ring_dma(rh, m0, voff);
     }
   };
@@ -676,13 +542,14 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
 #pragma unroll
   for (int s = 0; s < G::AHEAD; ++s) issue(s);
   for (int s = 0; s < nk; ++s) {
-    issue(s + G::AHEAD);
     // this wave's share of stage s has landed; after the barrier everyone's
-    // has, and nobody reads the stage that the loads just issued overwrite
-    wait_vmcnt<G::AHEAD * G::PER>();
+    // has, and everyone has finished reading stage s - 1, whose slot the
+    // loads of stage s + AHEAD then take
+    wait_vmcnt<(G::AHEAD - 1) * G::PER>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    issue(s + G::AHEAD);
     const char* stage = ring + (s % G::STAGES) * G::SB;
     u32x4 A[NA];
 #pragma unroll
@@ -690,14 +557,17 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
       const int row = 64 * vg + 16 * a + n;
       A[a] = *reinterpret_cast<const u32x4*>(stage + row * 64 + 16 * ring_piece(row, qg));
     }
+    // every row tile of the group, real or not: the stage's hidden chunks
+    // past the real ones hold copies of the last one, so the products of a
+    // padding tile are finite and never stored, and the loop has no branch
+    // that would keep the reads of one tile from overlapping the products
+    // of another
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (mt0 + t < mtiles) {
-        const int row = 16 * (mt0 + t) + n;  // hidden row = its row in the hidden part of the stage
-        const u32x4 B = *reinterpret_cast<const u32x4*>(stage + kRingWch * 1024 + row * 64 + 16 * ring_piece(row, qg));
+      const int row = 16 * (mt0 + t) + n;  // hidden row = its row in the hidden part of the stage
+      const u32x4 B = *reinterpret_cast<const u32x4*>(stage + G::WCH * 1024 + row * 64 + 16 * ring_piece(row, qg));
 #pragma unroll
-        for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a], B, acc[a][t]);
-      }
+      for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a], B, acc[a][t]);
     }
   }
   wait_vmcnt<0>();  // nothing may land after the ring is reused below
@@ -706,9 +576,9 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
 #pragma unroll
   for (int t = 0; t < NT; ++t) mrow[t] = 16 * (mt0 + t);
   uint64_t best[NT];
-  epilogue<NA, NT>(P, acc, vwg + 64 * vg, mrow, lane, best);
-  // reduce over the 4 vocab groups of each row through LDS (the ring is idle)
-  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [4][Mp]
+  epilogue<NA, NT>(P, acc, vwg + 64 * vg, mrow, lane, best, P.V);
+  // reduce over the VG vocab groups of each row through LDS (the ring is idle)
+  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [VG][Mp]
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     if (qg == 0 && mt0 + t < mtiles) red[vg * P.Mp + 16 * (mt0 + t) + n] = best[t];
@@ -716,7 +586,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   for (int m = threadIdx.x; m < P.M; m += 64 * kRingWaves) {
     uint64_t k = red[m];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
+    for (int w = 1; w < VG; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
     P.keys[(size_t)blockIdx.x * P.M + m] = k;
   }
 }
@@ -741,15 +611,6 @@ __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) 
   }
 }
 
-template <int NMT>
-void launch_staged(const VocabParams& P, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  const size_t lds = (size_t)2 * P.Mp * (kKC + 8) * 2;
-  const size_t red = (size_t)kStagedWaves * P.Mp * 8;
-  const size_t bytes = lds > red ? lds : red;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&vocab_staged_kernel<NMT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  launch_ev(vocab_staged_kernel<NMT>, dim3(P.nwg), dim3(64 * kStagedWaves), (uint32_t)bytes, s, start, stop, P);
-}
 
 }  // namespace
 
@@ -757,9 +618,10 @@ struct VocabPlan {
   bool stream;
   int ms;     // stream: m-tiles
   int na;     // stream: vocab tiles of 16 rows per wave
-  int nmt;    // staged: m-tiles template bound
+  bool round; // stream: hidden rows rounded in registers (one m-tile, M <= 8)
   int tiled;  // tiled: m-tiles per wave (0 = not tiled)
   int ring;   // ring: row tiles per row group (0 = not the ring kernel)
+  int rvg;    // ring: vocab groups of 64 rows
   int nwg;
   int Mp;
 };
@@ -775,36 +637,47 @@ VocabPlan vocab_plan(int M, int K, int V) {
   if (mt <= 2) {
     p.stream = true;
     p.ms = mt;
-    // vocab tiles per wave: the fewest rounds of workgroups over the 256 CUs
-    // times the rows each wave streams (a vocabulary of 152064 rows takes 297
-    // workgroups of 512 rows, two rounds, but 238 of 640 rows, one round);
-    // five tiles only with one m-tile (registers); on a tie the larger tile
-    // count (fewer workgroups) wins
-    const int cand[4] = {5, 4, 2, 1};
-    long best = -1;
-    for (int na : cand) {
-      if (na == 5 && mt != 1) continue;
-      const long nwg = (V + 16L * na * kStreamWaves - 1) / (16L * na * kStreamWaves);
-      const long cost = (nwg + kVocabCUs - 1) / kVocabCUs * na;
-      if (best < 0 || cost < best) {
-        best = cost;
-        p.na = na;
-        p.nwg = (int)nwg;
-      }
-    }
+    // Workgroups take equal shares of the vocabulary tiles (16 rows), as
+    // many rounds of the 256 CUs as the largest tile count per wave needs
+    // (five with one m-tile, four with two: registers), so every CU streams
+    // about the same number of W rows (a vocabulary of 152064 rows: 256
+    // workgroups of 37 or 38 tiles instead of 238 of 40 and 18 idle CUs);
+    // then the fewest tiles per wave that hold a share.
+    const long ntv = (V + 15) / 16;
+    const int na_max = mt == 1 ? 5 : 4;
+    const long rounds = (ntv + 8L * na_max * kVocabCUs - 1) / (8L * na_max * kVocabCUs);
+    const long nwg = std::min(rounds * kVocabCUs, ntv);
+    const long share = (ntv + nwg - 1) / nwg;  // tiles of the largest share
+    const long need = (share + kStreamWaves - 1) / kStreamWaves;
+    p.na = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 5;
+    p.nwg = (int)nwg;
+    p.round = M <= 8;
   } else if (kTiledEnabled && mt <= 18) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
     p.nwg = (V + kTRows - 1) / kTRows;
-  } else if (mt <= 26) {
-    // the two row groups of NT tiles cover every row tile
-    p.stream = false;
-    p.ring = mt <= 4 ? 2 : mt <= 10 ? 5 : mt <= 18 ? 9 : 13;
-    p.nwg = (V + kRingRows - 1) / kRingRows;
   } else {
+    // the row groups of NT tiles cover every row tile (the padding tiles'
+    // products are wasted): four vocab groups of 64 rows up to 18 and for 21
+    // to 26 row tiles, two vocab groups (a workgroup of 128 vocab rows and
+    // four row groups) for 19, 20, 27 and 28 (measured: M = 300 654 us
+    // against 765 us with four groups of 13; M = 416 753 us with four groups
+    // of 13 against 793 us with two of 7)
     p.stream = false;
-    p.nmt = mt <= 4 ? 4 : mt <= 8 ? 8 : mt <= 12 ? 12 : mt <= 18 ? 18 : mt <= 24 ? 24 : 28;
-    p.nwg = (V + 32 * kStagedWaves - 1) / (32 * kStagedWaves);
+    if (mt <= 18) {
+      p.ring = mt <= 4 ? 2 : mt <= 10 ? 5 : 9;
+      p.rvg = 4;
+    } else if (mt <= 20) {
+      p.ring = 5;
+      p.rvg = 2;
+    } else if (mt <= 26) {
+      p.ring = 13;
+      p.rvg = 4;
+    } else {
+      p.ring = 7;
+      p.rvg = 2;
+    }
+    p.nwg = (V + 64 * p.rvg - 1) / (64 * p.rvg);
   }
   return p;
 }
@@ -836,9 +709,9 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
   hipEvent_t mstart = main_only ? tm.start : nullptr, mstop = main_only ? tm.stop : nullptr;
-  // the stream kernel with one m-tile rounds the hidden rows itself; the
-  // others read the bf16 copy
-  const bool convert = !plan.stream || plan.ms != 1;
+  // the stream kernel may round the hidden rows itself; the others read the
+  // bf16 copy
+  const bool convert = !plan.stream || !plan.round;
   if (convert) {
     const size_t n = (size_t)plan.Mp * K;
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
@@ -848,42 +721,42 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
     const dim3 block(64 * kStreamWaves);
     hipEvent_t start = (main_only || convert) ? mstart : tm.start;
     const dim3 grid(plan.nwg);
-    if (plan.ms == 1) {
+    if (plan.ms == 1 && plan.round) {
       switch (plan.na) {
-        case 1: launch_ev(vocab_stream_kernel<1, 1>, grid, block, 0, stream, start, mstop, P); break;
-        case 2: launch_ev(vocab_stream_kernel<1, 2>, grid, block, 0, stream, start, mstop, P); break;
-        case 4: launch_ev(vocab_stream_kernel<1, 4>, grid, block, 0, stream, start, mstop, P); break;
-        default: launch_ev(vocab_stream_kernel<1, 5>, grid, block, 0, stream, start, mstop, P); break;
+        case 1: launch_ev(vocab_stream_kernel<1, 1, true>, grid, block, 0, stream, start, mstop, P); break;
+        case 2: launch_ev(vocab_stream_kernel<1, 2, true>, grid, block, 0, stream, start, mstop, P); break;
+        case 4: launch_ev(vocab_stream_kernel<1, 4, true>, grid, block, 0, stream, start, mstop, P); break;
+        default: launch_ev(vocab_stream_kernel<1, 5, true>, grid, block, 0, stream, start, mstop, P); break;
+      }
+    } else if (plan.ms == 1) {
+      switch (plan.na) {
+        case 1: launch_ev(vocab_stream_kernel<1, 1, false>, grid, block, 0, stream, start, mstop, P); break;
+        case 2: launch_ev(vocab_stream_kernel<1, 2, false>, grid, block, 0, stream, start, mstop, P); break;
+        case 4: launch_ev(vocab_stream_kernel<1, 4, false>, grid, block, 0, stream, start, mstop, P); break;
+        default: launch_ev(vocab_stream_kernel<1, 5, false>, grid, block, 0, stream, start, mstop, P); break;
       }
     } else {
       switch (plan.na) {
-        case 1: launch_ev(vocab_stream_kernel<2, 1>, grid, block, 0, stream, start, mstop, P); break;
-        case 2: launch_ev(vocab_stream_kernel<2, 2>, grid, block, 0, stream, start, mstop, P); break;
-        default: launch_ev(vocab_stream_kernel<2, 4>, grid, block, 0, stream, start, mstop, P); break;
+        case 1: launch_ev(vocab_stream_kernel<2, 1, false>, grid, block, 0, stream, start, mstop, P); break;
+        case 2: launch_ev(vocab_stream_kernel<2, 2, false>, grid, block, 0, stream, start, mstop, P); break;
+        default: launch_ev(vocab_stream_kernel<2, 4, false>, grid, block, 0, stream, start, mstop, P); break;
       }
     }
   } else if (plan.ring) {
     const dim3 grid(plan.nwg), block(64 * kRingWaves);
-    switch (plan.ring) {
-      case 2: launch_ev(vocab_ring_kernel<2>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 5: launch_ev(vocab_ring_kernel<5>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 9: launch_ev(vocab_ring_kernel<9>, grid, block, 0, stream, mstart, mstop, P); break;
-      default: launch_ev(vocab_ring_kernel<13>, grid, block, 0, stream, mstart, mstop, P); break;
+    switch (plan.ring * 16 + plan.rvg) {
+      case 2 * 16 + 4: launch_ev(vocab_ring_kernel<2, 4>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 5 * 16 + 4: launch_ev(vocab_ring_kernel<5, 4>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 9 * 16 + 4: launch_ev(vocab_ring_kernel<9, 4>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 13 * 16 + 4: launch_ev(vocab_ring_kernel<13, 4>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 5 * 16 + 2: launch_ev(vocab_ring_kernel<5, 2>, grid, block, 0, stream, mstart, mstop, P); break;
+      default: launch_ev(vocab_ring_kernel<7, 2>, grid, block, 0, stream, mstart, mstop, P); break;
     }
-  } else if (plan.tiled) {
+  } else {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);
     else if (plan.tiled == 6) launch_ev(vocab_tiled_kernel<6>, grid, block, 0, stream, mstart, mstop, P);
     else launch_ev(vocab_tiled_kernel<9>, grid, block, 0, stream, mstart, mstop, P);
-  } else {
-    switch (plan.nmt) {
-      case 4: launch_staged<4>(P, stream, mstart, mstop); break;
-      case 8: launch_staged<8>(P, stream, mstart, mstop); break;
-      case 12: launch_staged<12>(P, stream, mstart, mstop); break;
-      case 18: launch_staged<18>(P, stream, mstart, mstop); break;
-      case 24: launch_staged<24>(P, stream, mstart, mstop); break;
-      default: launch_staged<28>(P, stream, mstart, mstop); break;
-    }
   }
   vc_status st = check_launch("vocab projection");
   if (st != VC_OK) return st;

@@ -376,16 +376,20 @@ TILED_FAULT = ("the tiled vocab kernel (compiled out: kTiledEnabled = false) mad
                "longer select that kernel, so unskipped this case would run the ring kernel (M = 33..64 "
                "band, covered by the M = 33 at K = 8192, M = 48 and M = 64 cases); the shape stays off the GPU "
                "until the tiled kernel's cause is found")
-# (M, K, V): the stream kernel (M <= 32: one and two m-tiles, with 1, 2, 4 and
-# 5 vocab tiles per wave, as the plan picks them per vocabulary), every template
-# of the ring kernel the plan selects (NT 2: M 33..64, NT 5: 65..160, NT 9:
-# 161..288, NT 13: 289..416) and the staged kernel above 416 rows; ragged
-# vocabularies (a last workgroup with few rows) and K up to 8192
+# (M, K, V): the stream kernel (M <= 32: one m-tile with the hidden rows
+# rounded in registers up to 8 rows and read from the bf16 copy above, two
+# m-tiles; 1, 2, 4 and 5 vocab tiles per wave as the plan picks them per
+# vocabulary, with equal shares of the vocabulary per workgroup), every
+# template of the ring kernel the plan selects (four vocab groups with NT 2:
+# M 33..64, NT 5: 65..160, NT 9: 161..288, NT 13: 321..416; two vocab groups
+# with NT 5: 289..320, NT 7: 417..448); ragged vocabularies (a last
+# workgroup with few rows) and K up to 8192
 VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097), (20, 512, 3000),
                pytest.param((33, 1024, 5000), marks=pytest.mark.skip(reason=TILED_FAULT)), (264, 4096, 8192),
                (416, 1024, 3001), (164, 512, 2048), (48, 1024, 5000), (64, 8192, 3001), (100, 512, 2051),
                (300, 1024, 3000), (1, 8192, 20011), (180, 256, 1000), (440, 512, 2000), (33, 8192, 4099),
-               (160, 1024, 1025), (1, 256, 152064), (8, 512, 128256), (20, 256, 65536), (24, 256, 128256)]
+               (160, 1024, 1025), (1, 256, 152064), (8, 512, 128256), (20, 256, 65536), (24, 256, 128256),
+               (4, 256, 65536), (16, 256, 152064), (12, 256, 128256), (16, 256, 65536), (448, 256, 1000)]
 
 
 @pytest.mark.parametrize("case", VOCAB_CASES, ids=[f"vocab{i}" for i in range(len(VOCAB_CASES))])

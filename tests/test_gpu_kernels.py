@@ -231,21 +231,29 @@ def test_draft_workspace_reuse(L):
         assert_attention_close(out.cpu().numpy(), ref, f"reuse call {call}")
 
 
+# values over 2^-16 .. 2^13 times N(0,1) per channel (the range where the fp16
+# values of P x V are exact, and below it), as in test_verify_value_range
+VALUE_SCALE = np.exp2(-16.0 + (np.arange(128) % 30)).astype(np.float32)
+
 ROW_CASES = [
-    # kind, B, Hq, Hkv, D, T, keep / body lens, tail lens
+    # kind, B, Hq, Hkv, D, T, keep / body lens, tail lens[, scaled values]
     ("tokdrop", 2, 32, 8, 128, 4096, 0.25, [41, 7]),
     ("tokdrop", 1, 8, 8, 64, 2048, 0.5, [1]),
     ("dense", 2, 32, 8, 128, 3001, [1000, 3001], [3, 0]),
     ("dense", 1, 40, 8, 128, 700, [700], [26]),
+    ("tokdrop", 1, 32, 8, 128, 2048, 0.25, [19], True),
 ]
 
 
 @pytest.mark.parametrize("case", ROW_CASES, ids=[f"rows{i}" for i in range(len(ROW_CASES))])
 def test_draft_rows_parity(L, case):
-    kind, B, Hq, Hkv, D, T, sel, tail = case
+    kind, B, Hq, Hkv, D, T, sel, tail = case[:8]
+    scaled = len(case) > 8 and case[8]
     log(f"draft rows {case}")
     seed = 200 + T
     K, V = ctx_rows(seed, B, Hkv, T + 64, D)   # rows T.. serve as tail rows
+    if scaled:
+        V = (V * VALUE_SCALE[:D]).astype(np.float32)
     src_cap = r32(T) + 32
     src_k = np.zeros((B, Hkv, src_cap, D), np.float32)
     src_v = np.zeros_like(src_k)
@@ -288,6 +296,17 @@ def test_draft_rows_parity(L, case):
     out = run_draft(L, sh, kv, bf16_tensor(q)).cpu().numpy()
     g = Hq // Hkv
     ref = np.stack([np.stack([oracle.attend(q[b, h], *vis[b, h // g]) for h in range(Hq)]) for b in range(B)])
+    if scaled:
+        # per channel: the fp16-probability bound relative to the channel's
+        # size plus half the 2^-24 grid per output (values below 2^-17)
+        worst = 0.0
+        for c in range(D):
+            d = out[..., c].astype(np.float64) - ref[..., c]
+            bound = FP16P_RL2 * np.linalg.norm(ref[..., c]) + 2.0 ** -25 * np.sqrt(d.size)
+            worst = max(worst, np.linalg.norm(d) / bound)
+            assert np.linalg.norm(d) <= bound, f"channel {c}: |d| {np.linalg.norm(d):.2e} > bound {bound:.2e}"
+        log(f"  worst channel error / bound {worst:.2e}")
+        return
     mad, rl2 = assert_attention_close(out, ref, f"rows {case}", rl2_max=FP16P_RL2)
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
 
@@ -367,6 +386,69 @@ def test_verify_parity(L, case):
             ref[:, b, h] = oracle.attend_masked(q[:, b, h], Kall, Vall, vis)
     mad, rl2 = assert_attention_close(got, ref, f"verify {case}", rl2_max=FP16P_RL2)
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
+
+
+@pytest.mark.parametrize("NR", [9, 41], ids=["producers", "self-issuing"])
+def test_verify_value_range(L, NR):
+    """Values over 2^-16 .. 2^13 times N(0,1) per channel (down to 2^-17 and
+    up to about 2^15 in magnitude): the fp16 values of P x V are exact there,
+    so every channel keeps the fp16-probability accuracy; channels whose
+    values fall below 2^-17 round to fp16's 2^-24 grid, which the absolute
+    bound covers."""
+    B, Hq, Hkv, D, ctx = 1, 32, 8, 128, 1500
+    seed = 900 + NR
+    K, V = ctx_rows(seed, B, Hkv, ctx, D)
+    scale = np.exp2(-16.0 + (np.arange(D) % 30)).astype(np.float32)  # exact in bf16
+    V = (V * scale).astype(np.float32)
+    t_cap = r32(ctx) + 32
+    fk = np.zeros((B, Hkv, t_cap, D), np.float32)
+    fv = np.zeros_like(fk)
+    fk[:, :, :ctx], fv[:, :, :ctx] = K, V
+    toks = (np.arange(NR * B).reshape(NR, B) * 37 + 5) % 4096
+    q, kn, vn = synth.embed(seed, toks, Hq, Hkv, D)
+    vn = (vn * scale).astype(np.float32)
+    log(f"verify value range: R = {NR * Hq // Hkv}, |v| up to {np.abs(V).max():.0f}")
+    assert np.abs(V).max() < 65504 and np.abs(vn).max() < 65504
+    sh = L.vc_attn_shape(B, Hq, Hkv, D)
+    dq, dkn, dvn = bf16_tensor(q), bf16_tensor(kn), bf16_tensor(vn)
+    dk, dv = bf16_tensor(fk), bf16_tensor(fv)
+    cl = to_dev(np.array([ctx], np.int32))
+    ws = torch.empty(L.vc_verify_workspace_bytes(sh, NR, t_cap), dtype=torch.uint8, device="cuda")
+    out = torch.full((NR, B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ctxd = L.vc_kv_chunk(dk.data_ptr(), dv.data_ptr(), t_cap, 0, t_cap)
+    L.vc_verify_attn(sh, NR, dq.data_ptr(), dkn.data_ptr(), dvn.data_ptr(), ctxd, cl.data_ptr(),
+                     L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, out.data_ptr(), ws.data_ptr(), ws.numel(), stream())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # the bf16 values the kernel reads
+    Kb = dk.float().cpu().numpy()[0].astype(np.float64)
+    Vb = dv.float().cpu().numpy()[0].astype(np.float64)
+    qb = dq.float().cpu().numpy().astype(np.float64)
+    knb, vnb = dkn.float().cpu().numpy().astype(np.float64), dvn.float().cpu().numpy().astype(np.float64)
+    g = Hq // Hkv
+    ref = np.zeros_like(got)
+    for h in range(Hq):
+        hk = h // g
+        Kall = np.concatenate([Kb[hk, :ctx], knb[:, 0, hk]])
+        Vall = np.concatenate([Vb[hk, :ctx], vnb[:, 0, hk]])
+        vis = np.zeros((NR, ctx + NR), bool)
+        vis[:, :ctx] = True
+        for j in range(NR):
+            vis[j, ctx:ctx + j + 1] = True
+        ref[:, 0, h] = oracle.attend_masked(qb[:, 0, h], Kall, Vall, vis)
+    assert np.isfinite(got).all()
+    worst = 0.0
+    for c in range(D):
+        d = got[..., c] - ref[..., c]
+        # the fp16-probability bound relative to the channel's size, plus half
+        # the 2^-24 grid per output element for values below 2^-17 (an output
+        # is a weighted mean of the values, so its rounding error is at most
+        # the largest value's)
+        bound = FP16P_RL2 * np.linalg.norm(ref[..., c]) + 2.0 ** -25 * np.sqrt(d.size)
+        err = np.linalg.norm(d) / bound
+        worst = max(worst, err)
+        assert err <= 1.0, f"channel {c} (scale 2^{-16 + c % 30}): |d| {np.linalg.norm(d):.2e} > bound {bound:.2e}"
+    log(f"  worst channel error / bound {worst:.2e}")
 
 
 # ------------------------------------------------------------------ vocab --

@@ -737,37 +737,112 @@ __device__ __forceinline__ void dump_state(int lane, DState<D, W, NHS>& st, bool
   }
 }
 
-// Merge NWV wave states (written by dump_state; wave w's at o_of(w), ml_of(w))
-// and store the split's partial (running max, sum and unnormalised output per
-// query head of the unit). Called by all threads of the workgroup (nthreads).
-template <int D, typename OFn, typename MLFn>
-__device__ __forceinline__ void merge_waves(const DraftParams& P, int b, int hk, int split, int nwv, int nthreads,
-                                            const OFn& o_of, const MLFn& ml_of) {
-  for (int idx = threadIdx.x; idx < P.g * D; idx += nthreads) {
-    const int head = idx / D, c = idx % D;
-    float M = kNegInf;
-    for (int w = 0; w < nwv; ++w) M = fmaxf(M, ml_of(w)[head * 2]);
-    float O = 0.f, L = 0.f;
-    if (M != kNegInf) {
-      for (int w = 0; w < nwv; ++w) {
-        const float mw = ml_of(w)[head * 2];
-        if (mw != kNegInf) {
-          const float a = fast_exp2(mw - M);
-          O += o_of(w)[(size_t)head * D + c] * a;
-          L += ml_of(w)[head * 2 + 1] * a;
-        }
+// Merge layout of a workgroup's wave states: a wave's output in its own lane
+// order. Slot q = (h * 2W + mm) * 64 + lane (16 bytes) holds channels
+// 16 (2W jr + mm) + 4 qg + 0..3 of query head h * HS + hl for lane (hl, jr, qg),
+// so the waves write it, and the merge reads it, with 16-byte accesses of
+// consecutive lanes (a head-major layout puts 16 lanes of a store on one LDS
+// bank). The ml area stays head-major: [NH][2] floats (max, sum).
+
+// Reorder a wave's head-major output area [NH][D] of one head set (as
+// dump_state writes it) into the slot layout of W, in place. One wave: it
+// issues every read before the first write, so each read sees the head-major
+// data.
+template <int D, int W>
+__device__ __forceinline__ void head_major_to_slots(int lane, float* o) {
+  constexpr int NR = Geo<D, W>::NR;
+  const int n = lane & 15, qg = lane >> 4, jr = n % NR, hl = n / NR;
+  f32x4 v[2 * W];
+#pragma unroll
+  for (int mm = 0; mm < 2 * W; ++mm)
+    v[mm] = *reinterpret_cast<const f32x4*>(o + hl * D + 16 * (2 * W * jr + mm) + 4 * qg);
+#pragma unroll
+  for (int mm = 0; mm < 2 * W; ++mm) *reinterpret_cast<f32x4*>(o + (mm * 64 + lane) * 4) = v[mm];
+}
+
+// A wave's state in the slot layout: the values dump_state writes.
+template <int D, int W, int NHS>
+__device__ __forceinline__ void dump_slots(int lane, DState<D, W, NHS>& st, bool has_zero, float* o, float* ml) {
+  using G = Geo<D, W>;
+  constexpr int NR = G::NR, HS = G::HS, HPL = G::HPL;
+  const int n = lane & 15, qg = lane >> 4, jr = n % NR;
+#pragma unroll
+  for (int h = 0; h < NHS; ++h) {
+#pragma unroll
+    for (int mm = 0; mm < 2 * W; ++mm) {
+      const float zt = has_zero ? sum_q(st.zt[h][mm >> 1]) : 0.f;
+      f32x4 v = st.acc[h][mm];
+#pragma unroll
+      for (int jj = 1; jj < NR; ++jj) {
+        const f32x4 x = st.acc[h][2 * W * jj + mm];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (jr == jj) ? x[r] : v[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = v[r] + zt;
+      *reinterpret_cast<f32x4*>(o + ((h * 2 * W + mm) * 64 + lane) * 4) = v;
+    }
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      const float l = row_sum16(st.l[h][u]);
+      const int hb = h * HS + HPL * qg + u;
+      if (n == 0) {
+        ml[hb * 2] = st.m[h][u];
+        ml[hb * 2 + 1] = l;
       }
     }
+  }
+}
+
+// Merge NWV wave states in the slot layout (wave w's at o_of(w), ml_of(w))
+// and store the split's partial (running max, sum and unnormalised output
+// per query head of the unit). One thread per slot, every LDS load issued
+// before the arithmetic. Called by all threads of the workgroup (nthreads).
+template <int D, int W, int NHS, int NWV, typename OFn, typename MLFn>
+__device__ __forceinline__ void merge_slots(const DraftParams& P, int b, int hk, int split, int nthreads,
+                                            const OFn& o_of, const MLFn& ml_of) {
+  using G = Geo<D, W>;
+  constexpr int NR = G::NR, HS = G::HS;
+  for (int q = threadIdx.x; q < NHS * 2 * W * 64; q += nthreads) {
+    const int lane = q & 63, mm = (q >> 6) % (2 * W), h = q / (2 * W * 64);
+    const int n = lane & 15, qg = lane >> 4, jr = n % NR, head = h * HS + n / NR;
+    if (head >= P.g) continue;  // padding heads of the last head set
+    f32x4 ow[NWV];
+    float mw[NWV], lw[NWV];
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      ow[w] = *reinterpret_cast<const f32x4*>(o_of(w) + q * 4);
+      mw[w] = ml_of(w)[head * 2];
+      lw[w] = ml_of(w)[head * 2 + 1];
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mw[w]);
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        const bool ok = mw[w] != kNegInf;
+        const float a = ok ? fast_exp2(mw[w] - M) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[r] = ok ? O[r] + ow[w][r] * a : O[r];
+        L = ok ? L + lw[w] * a : L;
+      }
+    }
+    const int c0 = 16 * (2 * W * jr + mm) + 4 * qg;
     const size_t row = ((size_t)b * P.Hq + (size_t)hk * P.g + head) * P.S + split;
-    __hip_atomic_store(&P.part_o[row * D + c], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(&P.part_o[row * D + c0 + r], O[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c0 == 0) {
       __hip_atomic_store(&P.part_ml[row * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&P.part_ml[row * 2 + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Called by every thread after merge_waves. The workgroup's partial stores
+// Called by every thread after merge_slots. The workgroup's partial stores
 // complete, then one thread counts the split in; the workgroup that brings
 // the count to S merges the S partials of its (sequence, KV head) in split
 // order (so the result does not depend on the order in which workgroups
@@ -781,9 +856,68 @@ __device__ __forceinline__ void merge_waves(const DraftParams& P, int b, int hk,
 // model, but at agent scope on MI355X they write back and invalidate the
 // L2: measured, the draft kernel went from 41.2 to 54.2 us per launch on the
 // Llama-3-8B layer and from 135.2 to 146.8 us on the Qwen-32B layer.
+// The split merge of finish_unit over outputs idx, idx + nthreads, ...,
+// NI of them per pass so that their loads are in flight together, the
+// partials of BATCH splits at a time per output. An output past the end
+// takes the first one's addresses and is not stored.
+template <int D, int NI, int BATCH>
+__device__ __forceinline__ void merge_splits(const DraftParams& P, int b, int hk, int nthreads) {
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  for (int idx = threadIdx.x; idx < P.g * D; idx += NI * nthreads) {
+    int hq[NI], c[NI];
+    bool on[NI];
+    size_t row0[NI];
+    float M[NI], L[NI], O[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      on[j] = idx + j * nthreads < P.g * D;
+      const int ij = on[j] ? idx + j * nthreads : idx;
+      hq[j] = hk * P.g + ij / D;
+      c[j] = ij % D;
+      row0[j] = ((size_t)b * P.Hq + hq[j]) * P.S;
+      M[j] = kNegInf;
+      L[j] = 0.f;
+      O[j] = 0.f;
+    }
+    for (int s0 = 0; s0 < P.S; s0 += BATCH) {
+      float ms[NI][BATCH], ls[NI][BATCH], os[NI][BATCH];
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const size_t r = row0[j] + min(s0 + i, P.S - 1);
+          const bool in = s0 + i < P.S;
+          ms[j][i] = in ? ld(&P.part_ml[r * 2]) : kNegInf;
+          ls[j][i] = in ? ld(&P.part_ml[r * 2 + 1]) : 0.f;
+          os[j][i] = in ? ld(&P.part_o[r * D + c[j]]) : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        float mx = M[j];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) mx = fmaxf(mx, ms[j][i]);
+        if (mx == kNegInf) continue;  // nothing visible so far
+        const float a = M[j] == kNegInf ? 0.f : fast_exp2(M[j] - mx);
+        O[j] *= a;
+        L[j] *= a;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const bool ok = ms[j][i] != kNegInf;
+          const float w = ok ? fast_exp2(ms[j][i] - mx) : 0.f;
+          O[j] = ok ? fmaf(os[j][i], w, O[j]) : O[j];
+          L[j] = ok ? fmaf(ls[j][i], w, L[j]) : L[j];
+        }
+        M[j] = mx;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      if (on[j]) P.out[((size_t)b * P.Hq + hq[j]) * D + c[j]] = (L[j] > 0.f) ? O[j] / L[j] : 0.f;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk, int nthreads, int* lds_flag) {
-  constexpr int kBatch = 8;  // splits whose loads are issued together
   const size_t unit = (size_t)b * P.Hkv + hk;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
   __syncthreads();
@@ -795,38 +929,12 @@ __device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk,
   __syncthreads();
   if (!*lds_flag) return;
   asm volatile("" ::: "memory");
-  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  for (int idx = threadIdx.x; idx < P.g * D; idx += nthreads) {
-    const int hq = hk * P.g + idx / D, c = idx % D;
-    const size_t row0 = ((size_t)b * P.Hq + hq) * P.S;
-    float M = kNegInf, L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < P.S; s0 += kBatch) {
-      float ms[kBatch], ls[kBatch], os[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const size_t r = row0 + min(s0 + i, P.S - 1);
-        ms[i] = s0 + i < P.S ? ld(&P.part_ml[r * 2]) : kNegInf;
-        ls[i] = ld(&P.part_ml[r * 2 + 1]);
-        os[i] = ld(&P.part_o[r * D + c]);
-      }
-      float mx = M;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) mx = fmaxf(mx, ms[i]);
-      if (mx == kNegInf) continue;  // nothing visible so far
-      const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
-      O *= a;
-      L *= a;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const bool ok = ms[i] != kNegInf;
-        const float w = ok ? fast_exp2(ms[i] - mx) : 0.f;
-        O = ok ? fmaf(os[i], w, O) : O;
-        L = ok ? fmaf(ls[i], w, L) : L;
-      }
-      M = mx;
-    }
-    P.out[((size_t)b * P.Hq + hq) * D + c] = (L > 0.f) ? O / L : 0.f;
-  }
+  // one output per thread when one pass covers the unit's outputs, else two
+  // per pass (fewer splits per load batch, to bound the registers)
+  if (P.g * D <= nthreads)
+    merge_splits<D, 1, 8>(P, b, hk, nthreads);
+  else
+    merge_splits<D, 2, 4>(P, b, hk, nthreads);
   if (threadIdx.x == 0) __hip_atomic_store(&P.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -841,10 +949,10 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
   float* lds_o = lds;
   float* lds_ml = lds + NW * NH * D;
   __syncthreads();
-  dump_state<D, 1, NHS>(lane, st, false, lds_o + (size_t)wave * NH * D, lds_ml + wave * NH * 2);
+  dump_slots<D, 1, NHS>(lane, st, false, lds_o + (size_t)wave * NH * D, lds_ml + wave * NH * 2);
   __syncthreads();
-  merge_waves<D>(
-      P, b, hk, split, NW, 64 * NW, [&](int w) { return lds_o + (size_t)w * NH * D; },
+  merge_slots<D, 1, NHS, NW>(
+      P, b, hk, split, 64 * NW, [&](int w) { return lds_o + (size_t)w * NH * D; },
       [&](int w) { return lds_ml + w * NH * 2; });
   __shared__ int last;
   finish_unit<D>(P, b, hk, 64 * NW, &last);
@@ -1136,14 +1244,15 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
       row_block<D, 1, NHS1, false>(rows, min(32, nt - blk * 32), lane, P.qscale, Aqm, st1, tail_rows, lds_p);
     }
     dump_state<D, 1, NHS1>(lane, st1, false, tail_merge, tail_merge + NH * D);
+    head_major_to_slots<D, W>(lane, tail_merge);
   }
   // the ring (and with it the body waves' merge area) is free once every body
   // wave has left its loop
   __syncthreads();
-  if (wave < NW) dump_state<D, W, 1>(lane, st, true, body_o + (size_t)wave * NH * D, body_ml + wave * NH * 2);
+  if (wave < NW) dump_slots<D, W, 1>(lane, st, true, body_o + (size_t)wave * NH * D, body_ml + wave * NH * 2);
   __syncthreads();
-  merge_waves<D>(
-      P, b, hk, split, NW + 1, LL::NW * 64 + 64,
+  merge_slots<D, W, 1, NW + 1>(
+      P, b, hk, split, LL::NW * 64 + 64,
       [&](int w) { return w < NW ? body_o + (size_t)w * NH * D : tail_merge; },
       [&](int w) { return w < NW ? body_ml + w * NH * 2 : tail_merge + NH * D; });
   __shared__ int last;

@@ -130,6 +130,8 @@ KIVI_CASES = [
     (1, 32, 2, 64, 2, [640], [40], False),               # g = 16 (rows of two channel groups at D = 64)
     (1, 64, 4, 128, 2, [1024], [50], False),             # g = 16 (rows of four channel groups)
     (2, 48, 4, 128, 4, [512, 224], [40, 7], True),       # g = 12, 4-bit, padding heads in the set
+    (2, 40, 8, 128, 2, [0, 96], [17, 3], False),         # five-stage ring: empty body, fewer blocks than stages
+    (1, 40, 8, 128, 4, [992], [20], False),              # g = 5, 4-bit (two channel groups per row)
 ]
 
 

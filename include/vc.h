@@ -234,7 +234,8 @@ vc_status vc_verify_attn(const vc_attn_shape *shape, int32_t n_rows, const void 
 /* Greedy decoding picks the largest logit (VeriCache summary, "Experimental
  * results": identical output under greedy decoding). h: fp32 [m_rows][hidden],
  * rounded to bf16 (nearest even) on load; w: bf16 [vocab][hidden].
- * argmax [m_rows]: first index of the largest fp32 logit (-0 == +0).
+ * argmax [m_rows]: first index of the largest fp32 logit (-0 == +0; NaN
+ * logits are not ordered: a row that holds one has no defined argmax).
  * max_logit [m_rows] (optional, may be NULL): that logit.
  * logits [m_rows][vocab] (optional, may be NULL): all logits.
  * hidden must be a multiple of 128; m_rows <= 448; vocab < 2^31. */

@@ -39,6 +39,11 @@ struct VocabParams {
   float* logits;      // [M][V] or null
   int M, Mp, K, V, nwg;
   int hb_sliced;  // hb layout: 0 row-major [Mp][K]; 1 k-slice-major [K/32][Mp][32]
+  // ring kernel: slices [0, full) are done whole, each later one in `split`
+  // parts of the k range whose products go to `part` (workspace,
+  // [part][wave][4][NT][64 lanes] f32x4) for vocab_fixup_kernel
+  float* part;
+  int full, split;
 };
 
 __device__ __forceinline__ uint64_t make_key(float v, int idx) {
@@ -83,28 +88,49 @@ __global__ __launch_bounds__(256) void hidden_to_bf16_kernel(const VocabParams P
 }
 
 // Reduce the per-wave candidates (vocab tile a, m-tile mt) into keys per row
-// and write the optional logits. acc[a][mt][r]: logit of vocab row
+// (sink(mt, key): the wave's best of row mrow[mt] + lane % 16, in every lane of
+// the row) and write the optional logits. acc[a][mt][r]: logit of vocab row
 // vbase + 16*a + 4*qg + r and hidden row 16*mt_row + n; vocab rows from vlim
 // on (past the vocabulary, or past the caller's share of it) are skipped.
-template <int NA, int NMT>
+template <int NA, int NMT, typename Sink>
 __device__ __forceinline__ void epilogue(const VocabParams& P, const f32x4 (&acc)[NA][NMT], int vbase,
-                                         const int (&mrow)[NMT], int lane, uint64_t (&best)[NMT], int vlim) {
+                                         const int (&mrow)[NMT], int lane, int vlim, const Sink& sink) {
   const int n = lane & 15, qg = lane >> 4;
+  // every vocab row of the wave below vlim (all workgroups but the last): the
+  // lane's best is a plain float maximum in increasing index order, the first
+  // index kept among equal values (-0 == +0; NaN never compares greater), and
+  // becomes a key once per row tile; otherwise each element is tested
+  const bool whole = vbase + 16 * NA <= vlim;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int m = mrow[mt] + n;
     uint64_t bk = 0;
+    if (whole) {
+      float bx = -__builtin_huge_valf();
+      int bi = vbase + 4 * qg;
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = vbase + 16 * a + 4 * qg + r;
-        if (v < vlim) {
-          const uint64_t k = make_key(acc[a][mt][r], v);
-          bk = k > bk ? k : bk;
+        for (int r = 0; r < 4; ++r) {
+          const float x = acc[a][mt][r];
+          const bool gt = x > bx;
+          bx = gt ? x : bx;
+          bi = gt ? vbase + 16 * a + 4 * qg + r : bi;
         }
-      }
-    best[mt] = max_q_u64(bk);
+      bk = make_key(bx, bi);
+    } else {
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = vbase + 16 * a + 4 * qg + r;
+          if (v < vlim) {
+            const uint64_t k = make_key(acc[a][mt][r], v);
+            bk = k > bk ? k : bk;
+          }
+        }
+    }
+    sink(mt, max_q_u64(bk));
     if (P.logits != nullptr && m < P.M) {
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
@@ -263,7 +289,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 2) void vocab_stream_kernel(cons
 #pragma unroll
   for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
   uint64_t best[MS];
-  epilogue<NA, MS>(P, acc, vbase, mrow, lane, best, vlim);
+  epilogue<NA, MS>(P, acc, vbase, mrow, lane, vlim, [&](int t, uint64_t k) { best[t] = k; });
   __shared__ uint64_t red[kStreamWaves][16 * MS];
 #pragma unroll
   for (int t = 0; t < MS; ++t)
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
 #pragma unroll
   for (int t = 0; t < NMT2; ++t) mrow[t] = 16 * (mg * NMT2 + t);
   uint64_t best[NMT2];
-  epilogue<NA, NMT2>(P, acc, vwg + 64 * vg, mrow, lane, best, P.V);
+  epilogue<NA, NMT2>(P, acc, vwg + 64 * vg, mrow, lane, P.V, [&](int t, uint64_t k) { best[t] = k; });
   // reduce over the 4 vocab groups of each row through LDS (the ring is idle)
   uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [kTVG][Mp]
 #pragma unroll
@@ -444,7 +470,11 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
 // later (with non-temporal W loads each line was fetched from HBM twice:
 // M = 264 went 452 -> 366 us, M = 33 at K = 8192 535 -> 417 us). The hidden
 // rows sit in a k-slice-major copy, so a stage's hidden part is one
-// contiguous block.
+// contiguous block. A workgroup fills a CU, so the slices run in rounds of
+// the 256 CUs; when the last round would leave half of them or more idle,
+// each of its slices is cut into parts of the k range that fill them, and
+// vocab_fixup_kernel adds a slice's parts in part order and finishes it
+//.
 constexpr int kRingWaves = 8;
 // VG vocab groups of 64 rows x (8 / VG) row groups of NT row tiles
 template <int NT, int VG>
@@ -484,6 +514,35 @@ __device__ __forceinline__ void ring_dma(const int (&rsrc)[4], uint32_t m0, int 
       : "memory");
 }
 
+// The end of a slice (64 VG vocab rows, all hidden rows): the per-row best of
+// each wave's products (epilogue), then the best over the VG vocab groups
+// through LDS (lds: at least VG * Mp keys, free), stored as the slice's keys.
+template <int NT, int VG>
+__device__ __forceinline__ void ring_finish(const VocabParams& P, const f32x4 (&acc)[4][NT], int slice, char* lds,
+                                            int lane, int wave) {
+  using G = RingGeo<NT, VG>;
+  const int n = lane & 15, qg = lane >> 4;
+  const int vg = wave % VG, mg = wave / VG;
+  const int mtiles = P.Mp / 16;
+  const int mt0 = mg * NT;
+  int mrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) mrow[t] = 16 * (mt0 + t);
+  // each row tile's best goes to LDS as soon as it is known; then the best
+  // over the VG vocab groups of each row
+  uint64_t* red = reinterpret_cast<uint64_t*>(lds);  // [VG][Mp]
+  epilogue<4, NT>(P, acc, slice * G::ROWS + 64 * vg, mrow, lane, P.V, [&](int t, uint64_t k) {
+    if (qg == 0 && mt0 + t < mtiles) red[vg * P.Mp + 16 * (mt0 + t) + n] = k;
+  });
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 64 * kRingWaves) {
+    uint64_t k = red[m];
+#pragma unroll
+    for (int w = 1; w < VG; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
+    P.keys[(size_t)slice * P.M + m] = k;
+  }
+}
+
 template <int NT, int VG>
 __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const VocabParams P) {
   using G = RingGeo<NT, VG>;
@@ -492,9 +551,20 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, qg = lane >> 4;
   const int vg = wave % VG, mg = wave / VG;
-  const int vwg = blockIdx.x * G::ROWS;
   const int mtiles = P.Mp / 16;
   const int nk = P.K / 32;
+  // this workgroup's slice and k slices [kb, ke): slices below P.full whole,
+  // every later one in P.split parts (part >= 0: this workgroup's index
+  // among the parts)
+  int slice = blockIdx.x, kb = 0, ke = nk, part = -1;
+  if ((int)blockIdx.x >= P.full) {
+    const int j = blockIdx.x - P.full, pp = j % P.split;
+    slice = P.full + j / P.split;
+    kb = pp * nk / P.split;
+    ke = (pp + 1) * nk / P.split;
+    part = j;
+  }
+  const int vwg = slice * G::ROWS;
   const int mt0 = mg * NT;  // first row tile of this wave's row group
   // buffer descriptors (base, stride 0, extent in bytes, flags): this
   // workgroup's W rows (rows past the vocabulary read as zero) and the
@@ -520,7 +590,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   // the last k slice is loaded again into a stage no step reads
   auto issue = [&](int s) {
     const uint32_t slot = ring0 + (uint32_t)((s % G::STAGES) * G::SB);
-    const int k0 = min(s, nk - 1) * 32;
+    const int k0 = min(s, ke - 1) * 32;
 #pragma unroll
     for (int i = 0; i < G::PER; ++i) {
       const int q = min(wave * G::PER + i, G::NCH - 1);  // wave-uniform
@@ -540,8 +610,8 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < G::AHEAD; ++s) issue(s);
-  for (int s = 0; s < nk; ++s) {
+  for (int s = 0; s < G::AHEAD; ++s) issue(kb + s);
+  for (int s = kb; s < ke; ++s) {
     // this wave's share of stage s has landed; after the barrier everyone's
     // has, and everyone has finished reading stage s - 1, whose slot the
     // loads of stage s + AHEAD then take
@@ -570,25 +640,50 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
       for (int a = 0; a < NA; ++a) acc[a][t] = mfma_bf16(A[a], B, acc[a][t]);
     }
   }
-  wait_vmcnt<0>();  // nothing may land after the ring is reused below
-  __syncthreads();
-  int mrow[NT];
+  wait_vmcnt<0>();  // nothing may land after the ring is reused below (or the workgroup has gone)
+  if (part >= 0) {
+    // a part of a slice: its products go to the workspace, lane-major, as
+    // buffer stores (one lane offset, a scalar offset per tile: per-store
+    // 64-bit addresses would take a hundred registers)
+    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<f32x4*>(P.part) + ((size_t)part * kRingWaves + wave) * NA * NT * 64, (short)0,
+        NA * NT * 64 * 16, 0x00020000);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) mrow[t] = 16 * (mt0 + t);
-  uint64_t best[NT];
-  epilogue<NA, NT>(P, acc, vwg + 64 * vg, mrow, lane, best, P.V);
-  // reduce over the VG vocab groups of each row through LDS (the ring is idle)
-  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [VG][Mp]
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    if (qg == 0 && mt0 + t < mtiles) red[vg * P.Mp + 16 * (mt0 + t) + n] = best[t];
-  __syncthreads();
-  for (int m = threadIdx.x; m < P.M; m += 64 * kRingWaves) {
-    uint64_t k = red[m];
-#pragma unroll
-    for (int w = 1; w < VG; ++w) k = red[w * P.Mp + m] > k ? red[w * P.Mp + m] : k;
-    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 v = acc[a][t];
+        const u32x4 bits = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(bits, dst, lane * 16, (a * NT + t) * 1024, 0);
+      }
+    return;
   }
+  __syncthreads();
+  ring_finish<NT, VG>(P, acc, slice, ring, lane, wave);
+}
+
+// K-split slices: sum the P.split parts of slice P.full + blockIdx.x in part
+// order and finish it as the ring kernel finishes a whole slice.
+template <int NT, int VG>
+__global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_fixup_kernel(const VocabParams P) {
+  constexpr int NA = 4;
+  __shared__ __attribute__((aligned(16))) char red[VG * 448 * sizeof(uint64_t)];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t pstride = (size_t)kRingWaves * NA * NT * 64;  // f32x4 per part
+  const f32x4* src =
+      reinterpret_cast<const f32x4*>(P.part) + (size_t)blockIdx.x * P.split * pstride + (size_t)wave * NA * NT * 64 + lane;
+  f32x4 acc[NA][NT];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[a][t] = src[(a * NT + t) * 64];
+  for (int p = 1; p < P.split; ++p) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[a][t] = acc[a][t] + src[p * pstride + (a * NT + t) * 64];
+  }
+  ring_finish<NT, VG>(P, acc, P.full + blockIdx.x, red, lane, wave);
 }
 
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
@@ -622,6 +717,8 @@ struct VocabPlan {
   int tiled;  // tiled: m-tiles per wave (0 = not tiled)
   int ring;   // ring: row tiles per row group (0 = not the ring kernel)
   int rvg;    // ring: vocab groups of 64 rows
+  int full;   // ring: slices done whole (the rest in `split` k parts each)
+  int split;  // ring: k parts of each slice from `full` on (1: none)
   int nwg;
   int Mp;
 };
@@ -678,15 +775,52 @@ VocabPlan vocab_plan(int M, int K, int V) {
       p.rvg = 2;
     }
     p.nwg = (V + 64 * p.rvg - 1) / (64 * p.rvg);
+    // A workgroup fills a CU, so the slices run in rounds of the 256 CUs.
+    // When the last round would leave half of them or more idle, each of
+    // its slices is cut into split parts of the k range (at least 8 k
+    // slices each) that fill the CUs, and a fixup kernel sums the parts
+    // (M = 416: 594 slices, the third round's 82 take 246 workgroups).
+    const int left = (int)(p.nwg % kVocabCUs), nk = K / 32;
+    p.full = p.nwg;
+    p.split = 1;
+    if (left > 0 && 2 * left <= kVocabCUs) {
+      const int sp = std::min((int)(kVocabCUs / left), nk / 8);
+      if (sp >= 2) {
+        p.full = p.nwg - left;
+        p.split = sp;
+      }
+    }
   }
   return p;
+}
+
+// Bytes of the ring kernel's k-split parts (their fp32 products).
+static size_t vocab_part_bytes(const VocabPlan& p) {
+  if (!p.ring || p.split < 2) return 0;
+  return (size_t)(p.nwg - p.full) * p.split * kRingWaves * 4 * p.ring * 64 * sizeof(f32x4);
 }
 
 int vocab_max_rows() { return 28 * 16; }
 
 size_t vocab_ws_bytes(int M, int K, int V) {
   const VocabPlan p = vocab_plan(M, K, V);
-  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256);
+  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256) + align_up(vocab_part_bytes(p), 256);
+}
+
+// The ring kernel over whole slices and k parts, then (with parts) the fixup
+// kernel; start / stop (may be null) bracket both.
+template <int NT, int VG>
+static vc_status launch_ring(const VocabPlan& plan, const VocabParams& P, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop) {
+  const bool parts = plan.split > 1;
+  const dim3 block(64 * kRingWaves);
+  const dim3 grid(plan.full + (plan.nwg - plan.full) * plan.split);
+  launch_ev(vocab_ring_kernel<NT, VG>, grid, block, 0, stream, start, parts ? nullptr : stop, P);
+  if (!parts) return VC_OK;
+  const vc_status st = check_launch("vocab projection");
+  if (st != VC_OK) return st;
+  launch_ev(vocab_fixup_kernel<NT, VG>, dim3(plan.nwg - plan.full), block, 0, stream, nullptr, stop, P);
+  return check_launch("vocab k-part fixup");
 }
 
 vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32_t* argmax, float* max_logit,
@@ -696,6 +830,10 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.h = h;
   P.hb = static_cast<uint16_t*>(ws);
   P.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256));
+  P.part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256) +
+                                    align_up((size_t)plan.nwg * M * 8, 256));
+  P.full = plan.full;
+  P.split = plan.split;
   P.w = static_cast<const uint16_t*>(w);
   P.argmax = argmax;
   P.max_logit = max_logit;
@@ -708,6 +846,7 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.hb_sliced = plan.ring ? 1 : 0;
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;
+  vc_status st = VC_OK;
   hipEvent_t mstart = main_only ? tm.start : nullptr, mstop = main_only ? tm.stop : nullptr;
   // the stream kernel may round the hidden rows itself; the others read the
   // bf16 copy
@@ -743,22 +882,22 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
       }
     }
   } else if (plan.ring) {
-    const dim3 grid(plan.nwg), block(64 * kRingWaves);
     switch (plan.ring * 16 + plan.rvg) {
-      case 2 * 16 + 4: launch_ev(vocab_ring_kernel<2, 4>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 5 * 16 + 4: launch_ev(vocab_ring_kernel<5, 4>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 9 * 16 + 4: launch_ev(vocab_ring_kernel<9, 4>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 13 * 16 + 4: launch_ev(vocab_ring_kernel<13, 4>, grid, block, 0, stream, mstart, mstop, P); break;
-      case 5 * 16 + 2: launch_ev(vocab_ring_kernel<5, 2>, grid, block, 0, stream, mstart, mstop, P); break;
-      default: launch_ev(vocab_ring_kernel<7, 2>, grid, block, 0, stream, mstart, mstop, P); break;
+      case 2 * 16 + 4: st = launch_ring<2, 4>(plan, P, stream, mstart, mstop); break;
+      case 5 * 16 + 4: st = launch_ring<5, 4>(plan, P, stream, mstart, mstop); break;
+      case 9 * 16 + 4: st = launch_ring<9, 4>(plan, P, stream, mstart, mstop); break;
+      case 13 * 16 + 4: st = launch_ring<13, 4>(plan, P, stream, mstart, mstop); break;
+      case 5 * 16 + 2: st = launch_ring<5, 2>(plan, P, stream, mstart, mstop); break;
+      default: st = launch_ring<7, 2>(plan, P, stream, mstart, mstop); break;
     }
+    if (st != VC_OK) return st;
   } else {
     const dim3 grid(plan.nwg), block(64 * kTiledWaves);
     if (plan.tiled == 3) launch_ev(vocab_tiled_kernel<3>, grid, block, 0, stream, mstart, mstop, P);
     else if (plan.tiled == 6) launch_ev(vocab_tiled_kernel<6>, grid, block, 0, stream, mstart, mstop, P);
     else launch_ev(vocab_tiled_kernel<9>, grid, block, 0, stream, mstart, mstop, P);
   }
-  vc_status st = check_launch("vocab projection");
+  st = check_launch("vocab projection");
   if (st != VC_OK) return st;
   launch_ev(vocab_reduce_kernel, dim3(M), dim3(256), 0, stream, nullptr, main_only ? nullptr : tm.stop, P);
   return check_launch("vocab argmax reduce");

@@ -138,6 +138,18 @@ def test_qwen_kivi_draft():
     for b, hk in [(0, 0), (c.batch - 1, c.n_kv_heads - 1), (9, 4)]:
         check_kivi_unit(eng, b, hk)
     check_verify(eng, [(5, 2, (0, 12, c.k))], units=[(0, 0), (c.batch - 1, c.n_kv_heads - 1)])
+    # the verification argmax over the 152064-entry vocabulary (M = 416 rows:
+    # 512 whole ring slices, the last 82 in k parts summed by the fixup
+    # kernel) on sampled rows
+    eng.verify_vocab()
+    torch.cuda.synchronize()
+    M = (c.k + 1) * c.batch
+    rows = [0, 1, 100, 207, 208, 333, M - 2, M - 1]
+    h = oracle.to_bf16(eng.o_ver.reshape(M, -1)[rows].cpu().numpy())
+    got = eng.y.reshape(-1)[rows].cpu().numpy()
+    log(f"full size verify vocab ({c.name}): rows {rows} of {M} x {c.vocab} x {c.hidden}")
+    excused = check_argmax_chunked(eng.W, h, got)
+    log(f"  near-tie excused rows: {excused}/{len(rows)}")
     release(eng)
 
 

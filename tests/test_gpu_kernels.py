@@ -473,7 +473,9 @@ VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097
                (416, 1024, 3001), (164, 512, 2048), (48, 1024, 5000), (64, 8192, 3001), (100, 512, 2051),
                (300, 1024, 3000), (1, 8192, 20011), (180, 256, 1000), (440, 512, 2000), (33, 8192, 4099),
                (160, 1024, 1025), (1, 256, 152064), (8, 512, 128256), (20, 256, 65536), (24, 256, 128256),
-               (4, 256, 65536), (16, 256, 152064), (12, 256, 128256), (16, 256, 65536), (448, 256, 1000)]
+               (4, 256, 65536), (16, 256, 152064), (12, 256, 128256), (16, 256, 65536), (448, 256, 1000),
+               # 258 ring slices: 256 whole, the last two (one partial) in four k parts
+               (48, 1024, 65948)]
 
 
 @pytest.mark.parametrize("case", VOCAB_CASES, ids=[f"vocab{i}" for i in range(len(VOCAB_CASES))])

@@ -33,7 +33,7 @@ struct VocabParams {
   const float* h;     // fp32 [M][K]
   uint16_t* hb;       // bf16 [Mp][K] (workspace)
   const uint16_t* w;  // bf16 [V][K]
-  uint64_t* keys;     // [nwg][M] (workspace)
+  uint64_t* keys;     // [nwg key slots][M] (workspace)
   int32_t* argmax;    // [M]
   float* max_logit;   // [M] or null
   float* logits;      // [M][V] or null
@@ -662,28 +662,45 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   ring_finish<NT, VG>(P, acc, slice, ring, lane, wave);
 }
 
-// K-split slices: sum the P.split parts of slice P.full + blockIdx.x in part
-// order and finish it as the ring kernel finishes a whole slice.
+// K-split slices: one wave per (slice P.full + j, ring wave w) adds the
+// P.split parts of that wave's products in part order and takes the best of
+// each of its rows, as the ring kernel's epilogue does; its keys go to key
+// slot P.full + j * VG + w % VG (rows of its row group only; the VG vocab
+// groups of a slice each have a slot, and the reduce kernel takes the best
+// over all slots).
 template <int NT, int VG>
-__global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_fixup_kernel(const VocabParams P) {
+__global__ __launch_bounds__(64) void vocab_fixup_kernel(const VocabParams P) {
+  using G = RingGeo<NT, VG>;
   constexpr int NA = 4;
-  __shared__ __attribute__((aligned(16))) char red[VG * 448 * sizeof(uint64_t)];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x, n = lane & 15, qg = lane >> 4;
+  const int j = blockIdx.x / kRingWaves, w = blockIdx.x % kRingWaves, vg = w % VG, mg = w / VG;
+  const int slice = P.full + j, mt0 = mg * NT, mtiles = P.Mp / 16;
   const size_t pstride = (size_t)kRingWaves * NA * NT * 64;  // f32x4 per part
-  const f32x4* src =
-      reinterpret_cast<const f32x4*>(P.part) + (size_t)blockIdx.x * P.split * pstride + (size_t)wave * NA * NT * 64 + lane;
+  const f32x4* src = reinterpret_cast<const f32x4*>(P.part) + (size_t)j * P.split * pstride + (size_t)w * NA * NT * 64 + lane;
   f32x4 acc[NA][NT];
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[a][t] = src[(a * NT + t) * 64];
   for (int p = 1; p < P.split; ++p) {
+    f32x4 nxt[NA][NT];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[a][t] = acc[a][t] + src[p * pstride + (a * NT + t) * 64];
+      for (int t = 0; t < NT; ++t) nxt[a][t] = src[p * pstride + (a * NT + t) * 64];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[a][t] = acc[a][t] + nxt[a][t];
   }
-  ring_finish<NT, VG>(P, acc, P.full + blockIdx.x, red, lane, wave);
+  int mrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) mrow[t] = 16 * (mt0 + t);
+  uint64_t* keys = P.keys + (size_t)(P.full + j * VG + vg) * P.M;
+  epilogue<NA, NT>(P, acc, slice * G::ROWS + 64 * vg, mrow, lane, P.V, [&](int t, uint64_t k) {
+    const int m = 16 * (mt0 + t) + n;
+    if (qg == 0 && mt0 + t < mtiles && m < P.M) keys[m] = k;
+  });
 }
 
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
@@ -719,6 +736,7 @@ struct VocabPlan {
   int rvg;    // ring: vocab groups of 64 rows
   int full;   // ring: slices done whole (the rest in `split` k parts each)
   int split;  // ring: k parts of each slice from `full` on (1: none)
+  int nkeys;  // key slots per row: nwg, or full + (nwg - full) * rvg with k parts
   int nwg;
   int Mp;
 };
@@ -791,6 +809,7 @@ VocabPlan vocab_plan(int M, int K, int V) {
       }
     }
   }
+  p.nkeys = p.ring && p.split > 1 ? p.full + (p.nwg - p.full) * p.rvg : p.nwg;
   return p;
 }
 
@@ -804,7 +823,7 @@ int vocab_max_rows() { return 28 * 16; }
 
 size_t vocab_ws_bytes(int M, int K, int V) {
   const VocabPlan p = vocab_plan(M, K, V);
-  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nwg * M * 8, 256) + align_up(vocab_part_bytes(p), 256);
+  return align_up((size_t)p.Mp * K * 2, 256) + align_up((size_t)p.nkeys * M * 8, 256) + align_up(vocab_part_bytes(p), 256);
 }
 
 // The ring kernel over whole slices and k parts, then (with parts) the fixup
@@ -819,7 +838,8 @@ static vc_status launch_ring(const VocabPlan& plan, const VocabParams& P, hipStr
   if (!parts) return VC_OK;
   const vc_status st = check_launch("vocab projection");
   if (st != VC_OK) return st;
-  launch_ev(vocab_fixup_kernel<NT, VG>, dim3(plan.nwg - plan.full), block, 0, stream, nullptr, stop, P);
+  launch_ev(vocab_fixup_kernel<NT, VG>, dim3((plan.nwg - plan.full) * kRingWaves), dim3(64), 0, stream, nullptr, stop,
+            P);
   return check_launch("vocab k-part fixup");
 }
 
@@ -831,7 +851,7 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.hb = static_cast<uint16_t*>(ws);
   P.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256));
   P.part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)plan.Mp * K * 2, 256) +
-                                    align_up((size_t)plan.nwg * M * 8, 256));
+                                    align_up((size_t)plan.nkeys * M * 8, 256));
   P.full = plan.full;
   P.split = plan.split;
   P.w = static_cast<const uint16_t*>(w);
@@ -842,7 +862,7 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   P.Mp = plan.Mp;
   P.K = K;
   P.V = V;
-  P.nwg = plan.nwg;
+  P.nwg = plan.nkeys;  // key slots the reduce kernel reads
   P.hb_sliced = plan.ring ? 1 : 0;
   const Timing tm = take_timing();
   const bool main_only = tm.scope == VC_TIME_MAIN_KERNEL;

@@ -286,6 +286,65 @@ def full_kv_decode(eng, n_calls=12):
     return times, nbytes
 
 
+def cache_states(eng, reps=10):
+    """Draft and verify attention calls timed alone, cold and warm: "cold"
+    writes a 1 GiB scratch buffer on the engine's stream before each call
+    (evicting the per-XCD L2s and the 256 MB memory-side cache), "warm"
+    repeats the call. Each call follows an idle gap of 2 ms (back-to-back
+    heavy calls run at lower clocks: verification calls took about 25%
+    longer), so both modes start from the same power state. The round above
+    times the calls inside the round, where the 1-1.6 GB vocabulary read of
+    each draft step sits between two draft calls. Calls are timed by their
+    own dispatches (vc_time_next_call); their outputs and workspaces are the
+    engine's, and nothing they write is read by a later round."""
+    import torch
+
+    import lossless_speculative_kv_amd._lib as L
+
+    s = eng.stream
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=eng.dev)
+    c = eng.cfg
+
+    def draft():
+        L.vc_draft_decode_attn(eng.shape, eng.q_draft.data_ptr(), eng.kv, eng.o_draft.data_ptr(),
+                               eng.ws_draft.data_ptr(), eng.ws_draft.numel(), s.cuda_stream)
+
+    def verify():
+        ctx = L.vc_kv_chunk(eng.full_k.data_ptr(), eng.full_v.data_ptr(), eng.full_cap, 0, eng.full_cap)
+        L.vc_verify_attn(eng.shape, c.k + 1, eng.qv.data_ptr(), eng.kn.data_ptr(), eng.vn.data_ptr(), ctx,
+                         eng.ctx_len.data_ptr(), L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, eng.o_ver.data_ptr(),
+                         eng.ws_verify.data_ptr(), eng.ws_verify.numel(), s.cuda_stream)
+
+    out = {}
+    for name, fn in (("draft_attn_call_us", draft), ("verify_attn_call_us", verify)):
+        res = {}
+        for mode in ("cold", "warm"):
+            ev = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                b.record(s)
+                ev.append((a, b))
+            torch.cuda.synchronize(eng.dev)
+            fn()  # warms the call itself (and, for "warm", the caches)
+            for i, (a, b) in enumerate(ev):
+                if mode == "cold":
+                    with torch.cuda.stream(s):
+                        scratch.fill_(i & 0xFF)
+                torch.cuda.synchronize(eng.dev)
+                time.sleep(0.002)
+                L.vc_time_next_call(a.cuda_event, b.cuda_event, L.VC_TIME_CALL)
+                fn()
+            torch.cuda.synchronize(eng.dev)
+            res[mode] = dist_us([a.elapsed_time(b) * 1e-3 for a, b in ev])
+        out[name] = res
+    del scratch
+    out["note"] = ("calls timed alone after a 2 ms idle gap: cold = a 1 GiB scratch write before each call (L2 and "
+                   "memory-side cache evicted), warm = the call repeated; the headline uses the calls as timed "
+                   "inside the round")
+    return out
+
+
 def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
     """Warm-up rounds, then `steps` timed rounds of one workload; returns the
     figures of the JSON line (without the CPU baseline). With graph_reps, a
@@ -388,6 +447,7 @@ def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
                          "timed region (one host call per kernel, timing events on)"}
         log(f"graph replay {graph['round_ms']:.3f} ms per round (eager {graph['eager_round_ms']:.3f} ms)", q)
         del g
+    cache = cache_states(eng) if not cfg.staged else None
     what_if = {str(a): B * a / ((a - 1) * t_draft + t_verify) for a in (25, 40)}
     ceiling = B * (k + 1) / per_round if per_round > 0 else 0.0
     out = {
@@ -399,7 +459,7 @@ def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
         "t_verify_kernel": dist_us(times.get("verify_attn_main", [])),
         "draft_bytes": draft_bytes, "draft_gbs": draft_gbs, "t_draft_main": t_draft_main, "t_draft": t_draft,
         "verify_bytes": verify_bytes, "verify_gbs": verify_gbs, "t_vmain": t_vmain, "t_verify": t_verify,
-        "mfma": mfma, "full": full, "graph": graph,
+        "mfma": mfma, "full": full, "graph": graph, "cache": cache,
         "what_if": {"all_accepted_m_eq_k": ceiling, "accepted_25_per_round": what_if["25"],
                     "accepted_40_per_round": what_if["40"],
                     "note": ("derived from the measured call times: B * a / ((a - 1) * t_draft + t_verify) for a "
@@ -522,6 +582,7 @@ def main():
         "accept": r["accept"],
         "round_tok_s": r["round_tok_s"],
         "graph_round": r["graph"],
+        "cache_states": r["cache"],
         "kernels": r["kernels"],
     }
     r = None

@@ -473,8 +473,7 @@ __global__ __launch_bounds__(512, 2) void vocab_tiled_kernel(const VocabParams P
 // contiguous block. A workgroup fills a CU, so the slices run in rounds of
 // the 256 CUs; when the last round would leave half of them or more idle,
 // each of its slices is cut into parts of the k range that fill them, and
-// vocab_fixup_kernel adds a slice's parts in part order and finishes it
-//.
+// vocab_fixup_kernel adds a slice's parts in part order and finishes it.
 constexpr int kRingWaves = 8;
 // VG vocab groups of 64 rows x (8 / VG) row groups of NT row tiles
 template <int NT, int VG>

@@ -388,6 +388,13 @@ def test_verify_parity(L, case):
             ref[:, b, h] = oracle.attend_masked(q[:, b, h], Kall, Vall, vis)
     mad, rl2 = assert_attention_close(got, ref, f"verify {case}", rl2_max=FP16P_RL2)
     log(f"  max|d| {mad:.2e} rel-L2 {rl2:.2e}")
+    if chunk is None:
+        # the splits are folded in split order: a second call is bit for bit the same
+        out2 = torch.full_like(out, float("nan"))
+        L.vc_verify_attn(sh, NR, dq.data_ptr(), dkn.data_ptr(), dvn.data_ptr(), ctxd, cl.data_ptr(),
+                         L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, out2.data_ptr(), ws.data_ptr(), ws.numel(), stream())
+        torch.cuda.synchronize()
+        assert np.array_equal(got, out2.cpu().numpy()), "verify attention is not deterministic"
 
 
 @pytest.mark.parametrize("NR", [9, 41], ids=["producers", "self-issuing"])
@@ -499,7 +506,13 @@ def test_vocab_parity(L, case):
     am2 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
     L.vc_vocab_logits(M, K, V, dh.data_ptr(), dW.data_ptr(), am2.data_ptr(), None, None, ws.data_ptr(), ws.numel(),
                       stream())
+    # a third call with every output: bit for bit the first (k parts are added in part order)
+    ml3 = torch.zeros_like(ml)
+    lg3 = torch.zeros_like(lg)
+    L.vc_vocab_logits(M, K, V, dh.data_ptr(), dW.data_ptr(), am2.data_ptr(), ml3.data_ptr(), lg3.data_ptr(),
+                      ws.data_ptr(), ws.numel(), stream())
     torch.cuda.synchronize()
+    assert torch.equal(lg3, lg) and torch.equal(ml3, ml), "vocab product is not deterministic"
     am, ml, lg, am2 = am.cpu().numpy(), ml.cpu().numpy(), lg.cpu().numpy(), am2.cpu().numpy()
     # argmax of the GPU's own fp32 logits (first index on ties): bit-exact
     assert np.array_equal(am, np.argmax(lg, axis=1))

@@ -584,23 +584,29 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void vocab_ring_kernel(const Vo
   // Hidden chunks past the row tiles (2 NT tiles allocated, Mp / 16 real)
   // would read the next slice's rows in the k-slice-major copy; they load the
   // last real chunk again instead (into their own, never-read stage rows).
-  // this wave's share of stage s: chunks wave * PER + i (past the last chunk:
+  // this wave's share of stage s: chunks wave + 8 i (past the last chunk:
   // the last one again, same data to the same place); past the last stage
-  // the last k slice is loaded again into a stage no step reads
+  // the last k slice is loaded again into a stage no step reads. The W
+  // chunks are the first WCH, a multiple of the 8 waves, so whether a chunk
+  // is W or hidden depends on i alone and the unrolled loop has no branch.
+  static_assert(G::WCH % kRingWaves == 0, "W chunks dealt evenly");
   auto issue = [&](int s) {
     const uint32_t slot = ring0 + (uint32_t)((s % G::STAGES) * G::SB);
     const int k0 = min(s, ke - 1) * 32;
 #pragma unroll
     for (int i = 0; i < G::PER; ++i) {
-      const int q = min(wave * G::PER + i, G::NCH - 1);  // wave-uniform
-      const int hsrc = min(q - G::WCH, mtiles - 1);       // hidden chunk whose rows are read
-      const int row = 16 * (q < G::WCH ? q : hsrc) + lrow;
-      // W rows are row-major; the hidden copy is k-slice-major ([K/32][Mp][32])
-      const int voff =
-          (q < G::WCH ? (row * P.K + k0) * 2 : ((k0 / 32) * P.Mp + row) * 64) + 16 * ring_piece(row, lpos);
+      const int q = min(wave + kRingWaves * i, G::NCH - 1);  // wave-uniform
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + (uint32_t)q * 1024u);
-      if (q < G::WCH) ring_dma(rw, m0, voff);
-      else ring_dma(rh, m0, voff);
+      if (i < G::WCH / kRingWaves) {
+        // W rows are row-major
+        const int row = 16 * q + lrow;
+        ring_dma(rw, m0, (row * P.K + k0) * 2 + 16 * ring_piece(row, lpos));
+      } else {
+        // the hidden copy is k-slice-major ([K/32][Mp][32]); chunks past the
+        // row tiles read the last real one
+        const int row = 16 * min(q - G::WCH, mtiles - 1) + lrow;
+        ring_dma(rh, m0, ((k0 / 32) * P.Mp + row) * 64 + 16 * ring_piece(row, lpos));
+      }
     }
   };
   f32x4 acc[NA][NT];

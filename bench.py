@@ -70,6 +70,8 @@ def parse():
                     help="host-resident workload on which pipelined drafting is timed against plain rounds; 'none' "
                          "for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-states", action="store_true",
+                    help="skip the cold / warm calls timed alone (kernel profiles then hold the round's calls only)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (5 times) and print its byte counts; the "
@@ -345,7 +347,7 @@ def cache_states(eng, reps=10):
     return out
 
 
-def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
+def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0, cache=True):
     """Warm-up rounds, then `steps` timed rounds of one workload; returns the
     figures of the JSON line (without the CPU baseline). With graph_reps, a
     round is then captured in a HIP graph and replayed that many times
@@ -447,7 +449,7 @@ def measure(cfg, steps, warmup, q, comparator=True, graph_reps=0):
                          "timed region (one host call per kernel, timing events on)"}
         log(f"graph replay {graph['round_ms']:.3f} ms per round (eager {graph['eager_round_ms']:.3f} ms)", q)
         del g
-    cache = cache_states(eng) if not cfg.staged else None
+    cache = cache_states(eng) if cache and not cfg.staged else None
     what_if = {str(a): B * a / ((a - 1) * t_draft + t_verify) for a in (25, 40)}
     ceiling = B * (k + 1) / per_round if per_round > 0 else 0.0
     out = {
@@ -545,7 +547,7 @@ def main():
 
     cfg = configs.BY_NAME[args.workload]
     q = args.quiet
-    r = measure(cfg, args.steps, args.warmup, q, graph_reps=args.steps)
+    r = measure(cfg, args.steps, args.warmup, q, graph_reps=args.steps, cache=not args.no_cache_states)
     full = r["full"]
     result = {
         "metric": "accepted tok/s/layer; draft & verify attn HBM GB/s as % of 8 TB/s peak",

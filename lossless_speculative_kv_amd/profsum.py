@@ -14,7 +14,7 @@ so bench.py reports them only while the source is unchanged):
     rocprofv3 --pmc WRITE_SIZE -d <runs>/pmc_write_<w> -o run -- python3 -u bench.py <args>
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
               SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE -d <runs>/pmc_mfma_<w> -o run -- python3 -u bench.py <args>
-    <args> = --workload <w> --steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none --p1 none --pipeline none
+    <args> = --workload <w> --steps 3 --warmup 1 --no-cpu-baseline --no-cache-states --quiet --extra none --p1 none --pipeline none
 
 The counters are scaled by a plain device copy of known size (bench.py
 --copy-calibration 256, one FETCH_SIZE and one WRITE_SIZE pass into
@@ -33,7 +33,7 @@ import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
-BENCH_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --quiet --extra none --p1 none --pipeline none"
+BENCH_ARGS = "--steps 3 --warmup 1 --no-cpu-baseline --no-cache-states --quiet --extra none --p1 none --pipeline none"
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
                  "GRBM_GUI_ACTIVE")
 # hot-path kernels and the source file each is built from

@@ -110,6 +110,43 @@ def test_verify_vocab_accept_checks():
     assert L.lib.vc_greedy_accept(2, 4, None, 0x10000, 0x10000, 0x10000, None, None) == L.VC_ERR_INVALID_ARG
 
 
+def _ring_plan(M, K, V):
+    """The ring kernel's plan, restated: row tiles per row group and vocab
+    groups per row-tile count, then the k split of the last round of 256
+    CUs (at least 8 k slices per part, only when that round would leave half
+    of the CUs or more idle)."""
+    mt = (M + 15) // 16
+    nt, vg = ((2, 4) if mt <= 4 else (5, 4) if mt <= 10 else (9, 4)) if mt <= 18 else \
+        (5, 2) if mt <= 20 else (13, 4) if mt <= 26 else (7, 2)
+    nwg = -(-V // (64 * vg))
+    left, full, split = nwg % 256, nwg, 1
+    if left and 2 * left <= 256 and min(256 // left, K // 32 // 8) >= 2:
+        split, full = min(256 // left, K // 32 // 8), nwg - left
+    return nt, vg, nwg, full, split
+
+
+def _align(x):
+    return -(-x // 256) * 256
+
+
+@pytest.mark.parametrize("M,K,V", [(416, 5120, 152064), (264, 4096, 128256), (164, 5120, 32768), (33, 8192, 128256),
+                                   (48, 1024, 65948), (448, 256, 1000), (300, 1024, 3000)])
+def test_vocab_ring_workspace(M, K, V):
+    """Workspace of the ring path: the bf16 hidden copy, a 64-bit key per row
+    and key slot (whole slices one slot, a k-split slice one per vocab group),
+    and the k parts' fp32 products (8 waves x 4 vocab tiles x NT row tiles x
+    64 lanes x 16 bytes per part)."""
+    nt, vg, nwg, full, split = _ring_plan(M, K, V)
+    Mp = (M + 15) // 16 * 16
+    nkeys = full + (nwg - full) * vg if split > 1 else nwg
+    parts = (nwg - full) * split * 8 * 4 * nt * 64 * 16 if split > 1 else 0
+    out = C.c_size_t()
+    assert L.lib.vc_vocab_workspace_bytes(M, K, V, C.byref(out)) == L.VC_OK
+    assert out.value == _align(Mp * K * 2) + _align(nkeys * M * 8) + _align(parts)
+    if (M, K, V) == (416, 5120, 152064):
+        assert (nwg, full, split, nkeys) == (594, 512, 3, 840)  # 82 leftover slices in 3 k parts
+
+
 def test_stage_and_compressor_checks():
     sh = shape()
     rc = L.lib.vc_stage_full_kv(C.byref(sh), 0x10000, 0x10000, 1000, 900, 200, 0x10000, 0x10000, 4096, None, None)

@@ -708,6 +708,164 @@ __global__ __launch_bounds__(64) void vocab_fixup_kernel(const VocabParams P) {
   });
 }
 
+// Band kernel, M <= 32 (the draft step): the stream kernel's equal shares of
+// the vocabulary's 16-row tiles (one workgroup per CU), but W moves through
+// a two-stage LDS ring of 64-wide k slices, 128 bytes of each row: whole
+// cache lines, so the loads can be non-temporal (a plain read of W streams
+// at 6.1 TB/s with the stream kernel's register layout, 64 bytes of a line
+// per instruction and the default policy, against 6.9 TB/s with whole lines
+// and non-temporal direct-to-LDS loads). Every wave issues its share of a
+// stage's 1 KB loads (8 rows x 128 bytes; lane l fills row l / 8, 16-byte
+// unit l % 8 with the row's unit (l % 8) ^ (row % 8), so the 16 rows of an
+// operand read hit distinct banks in pairs), waits for them, meets the
+// others at the stage barrier and issues the next stage into the other slot
+// (which everyone has finished reading). The hidden rows are read from
+// global memory per stage (L2 hits), right after the stage's W loads, so
+// waiting for them is waiting for the stage; with ROUND (one m-tile, M <= 8)
+// they are fp32 rounded in registers, otherwise the bf16 copy.
+constexpr int kBandWaves = 8;
+constexpr int kBandMaxTiles = 38;  // tiles per share: two stages of 76 KB
+constexpr int kBandStage = kBandMaxTiles * 16 * 128;
+
+// One 1 KB non-temporal direct-to-LDS load (see ring_dma).
+__device__ __forceinline__ void band_dma(const int (&rsrc)[4], uint32_t m0, int voff) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 r = {rsrc[0], rsrc[1], rsrc[2], rsrc[3]};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(m0), "s"(r)
+      : "memory");
+}
+
+template <int MS, int NA, bool ROUND>
+__global__ __launch_bounds__(64 * kBandWaves, 1) void vocab_band_kernel(const VocabParams P) {
+  static_assert(NA * kBandWaves >= kBandMaxTiles, "the waves cover a share");
+  static_assert(!ROUND || MS == 1, "rounding in registers with one m-tile");
+  __shared__ __attribute__((aligned(1024))) char ring[2 * kBandStage];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, qg = lane >> 4;
+  const long ntv = (P.V + 15) / 16;
+  const int t_lo = (int)(blockIdx.x * ntv / gridDim.x), t_hi = (int)((blockIdx.x + 1) * ntv / gridDim.x);
+  const int nch = 2 * (t_hi - t_lo);  // 1 KB chunks per stage (at most 2 kBandMaxTiles, by the plan)
+  const int tfirst = t_lo + wave * NA;
+  const int vbase = tfirst * 16;
+  const int vlim = min(P.V, t_hi * 16);
+  const int nk = P.K / 64;
+  // W rows [16 t_lo, min(16 t_hi, V)); rows past the vocabulary read as zero
+  const uint64_t wb = reinterpret_cast<uint64_t>(P.w) + (uint64_t)t_lo * 16u * (uint64_t)P.K * 2u;
+  const int rw[4] = {(int)__builtin_amdgcn_readfirstlane((uint32_t)wb),
+                     (int)(__builtin_amdgcn_readfirstlane((uint32_t)(wb >> 32)) & 0xFFFFu),
+                     (int)__builtin_amdgcn_readfirstlane((uint32_t)(vlim - t_lo * 16) * (uint32_t)P.K * 2u),
+                     0x00020000};
+  const uint32_t ring0 = lds_addr(ring);
+  const int lrow = lane >> 3, lu = lane & 7;
+  // W loads of stage s (k slice s): chunks wave, wave + 8, ... of the
+  // share (the stage wait is a full one, so waves may issue different
+  // numbers); past the last stage the last slice again into the slot no
+  // step reads
+  auto issue_w = [&](int s) {
+    const uint32_t slot = ring0 + (uint32_t)((s & 1) * kBandStage);
+    const int k0 = min(s, nk - 1) * 64;
+    for (int c = wave; c < nch; c += kBandWaves) {
+      const int row = 8 * c + lrow;
+      band_dma(rw, __builtin_amdgcn_readfirstlane(slot + (uint32_t)c * 1024u),
+               row * P.K * 2 + k0 * 2 + 16 * (lu ^ (row & 7)));
+    }
+  };
+  // hidden operands of stage s: m-tile t, k-step kk (32 wide) of the slice
+  using HRaw = std::conditional_t<ROUND, f32x4[MS][2][2], u32x4[MS][2]>;
+  auto load_h = [&](HRaw& H, int s) {
+    const int k0 = min(s, nk - 1) * 64;
+#pragma unroll
+    for (int t = 0; t < MS; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if constexpr (ROUND) {
+          const float* hp = P.h + (size_t)min(16 * t + n, P.M - 1) * P.K + k0 + 32 * kk + 8 * qg;
+          H[t][kk][0] = *reinterpret_cast<const f32x4*>(hp);
+          H[t][kk][1] = *reinterpret_cast<const f32x4*>(hp + 4);
+        } else {
+          H[t][kk] = *reinterpret_cast<const u32x4*>(P.hb + (size_t)(16 * t + n) * P.K + k0 + 32 * kk + 8 * qg);
+        }
+      }
+  };
+  auto to_bf16 = [&](const HRaw& H, u32x4 (&B)[MS][2]) {
+#pragma unroll
+    for (int t = 0; t < MS; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if constexpr (ROUND) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            B[t][kk][2 * j] = f32_to_bf16_bits(H[t][kk][j][0]) | (f32_to_bf16_bits(H[t][kk][j][1]) << 16);
+            B[t][kk][2 * j + 1] = f32_to_bf16_bits(H[t][kk][j][2]) | (f32_to_bf16_bits(H[t][kk][j][3]) << 16);
+          }
+        } else {
+          B[t][kk] = H[t][kk];
+        }
+      }
+  };
+  f32x4 acc[NA][MS];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int t = 0; t < MS; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this wave's tiles in the share (slots past it compute on the last tile
+  // and store nothing): LDS rows of tile a
+  int arow[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) arow[a] = 16 * (min(tfirst + a, t_hi - 1) - t_lo) + n;
+  HRaw H;
+  u32x4 B[MS][2];
+  issue_w(0);
+  load_h(H, 0);
+  for (int s = 0; s < nk; ++s) {
+    // this wave's loads of stage s have landed (W and hidden); after the
+    // barrier everyone's have, and everyone has finished reading stage
+    // s - 1, whose slot stage s + 1 then takes
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    to_bf16(H, B);
+    issue_w(s + 1);
+    load_h(H, s + 1);
+    const char* stage = ring + (s & 1) * kBandStage;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(stage + arow[a] * 128 + 16 * ((4 * kk + qg) ^ (arow[a] & 7)));
+#pragma unroll
+        for (int t = 0; t < MS; ++t) acc[a][t] = mfma_bf16(A, B[t][kk], acc[a][t]);
+      }
+  }
+  wait_vmcnt<0>();  // nothing may land after the workgroup has gone
+  int mrow[MS];
+#pragma unroll
+  for (int t = 0; t < MS; ++t) mrow[t] = 16 * t;
+  uint64_t best[MS];
+  epilogue<NA, MS>(P, acc, vbase, mrow, lane, vlim, [&](int t, uint64_t k) { best[t] = k; });
+  __syncthreads();  // the ring is free: every wave has left the loop
+  uint64_t* red = reinterpret_cast<uint64_t*>(ring);  // [kBandWaves][16 MS]
+#pragma unroll
+  for (int t = 0; t < MS; ++t)
+    if (qg == 0) red[wave * 16 * MS + 16 * t + n] = best[t];
+  __syncthreads();
+  for (int m = threadIdx.x; m < P.M; m += 64 * kBandWaves) {
+    uint64_t k = red[m];
+#pragma unroll
+    for (int w = 1; w < kBandWaves; ++w) k = red[w * 16 * MS + m] > k ? red[w * 16 * MS + m] : k;
+    P.keys[(size_t)blockIdx.x * P.M + m] = k;
+  }
+}
+
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) {
   const int m = blockIdx.x;
   uint64_t k = 0;
@@ -733,6 +891,7 @@ __global__ __launch_bounds__(256) void vocab_reduce_kernel(const VocabParams P) 
 
 struct VocabPlan {
   bool stream;
+  bool band;  // stream: the band kernel (W through LDS in 64-wide k slices) instead
   int ms;     // stream: m-tiles
   int na;     // stream: vocab tiles of 16 rows per wave
   bool round; // stream: hidden rows rounded in registers (one m-tile, M <= 8)
@@ -772,6 +931,13 @@ VocabPlan vocab_plan(int M, int K, int V) {
     p.na = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 5;
     p.nwg = (int)nwg;
     p.round = M <= 8;
+    // the band kernel holds a share of at most kBandMaxTiles tiles per
+    // stage and keeps one stage in flight, enough for the latency only from
+    // about 32 tiles (64 KB) on (measured: a 152064-entry vocabulary, shares
+    // of 38 tiles, 268.7 -> 242.6 us; 128256 entries, 32 tiles, 180.1 ->
+    // 177.0 us; 32768 entries, 8 tiles, 56.6 -> 79.7 us, so the stream
+    // kernel keeps small shares)
+    p.band = share >= 32 && share <= kBandMaxTiles && K % 64 == 0;
   } else if (kTiledEnabled && mt <= 18) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;
@@ -881,7 +1047,13 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     launch_ev(hidden_to_bf16_kernel, dim3(blocks), dim3(256), 0, stream, main_only ? nullptr : tm.start, nullptr, P);
   }
-  if (plan.stream) {
+  if (plan.stream && plan.band) {
+    hipEvent_t start = (main_only || convert) ? mstart : tm.start;
+    const dim3 grid(plan.nwg), block(64 * kBandWaves);
+    if (plan.ms == 1 && plan.round) launch_ev(vocab_band_kernel<1, 5, true>, grid, block, 0, stream, start, mstop, P);
+    else if (plan.ms == 1) launch_ev(vocab_band_kernel<1, 5, false>, grid, block, 0, stream, start, mstop, P);
+    else launch_ev(vocab_band_kernel<2, 5, false>, grid, block, 0, stream, start, mstop, P);
+  } else if (plan.stream) {
     const dim3 block(64 * kStreamWaves);
     hipEvent_t start = (main_only || convert) ? mstart : tm.start;
     const dim3 grid(plan.nwg);

@@ -938,6 +938,8 @@ VocabPlan vocab_plan(int M, int K, int V) {
     // 177.0 us; 32768 entries, 8 tiles, 56.6 -> 79.7 us, so the stream
     // kernel keeps small shares)
     p.band = share >= 32 && share <= kBandMaxTiles && K % 64 == 0;
+    // (rounding 16 fp32 hidden rows in the band kernel instead of reading
+    // the bf16 copy measured 242 -> 259 us, so it keeps M <= 8 too)
   } else if (kTiledEnabled && mt <= 18) {
     p.stream = false;
     p.tiled = mt <= 6 ? 3 : mt <= 12 ? 6 : 9;

@@ -39,7 +39,7 @@ MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOP
 # hot-path kernels and the source file each is built from
 SOURCES = {"draft_kivi_kernel": "draft_attn.hip", "draft_rows_kernel": "draft_attn.hip",
            "verify_kernel": "verify_attn.hip", "verify_merge_kernel": "verify_attn.hip",
-           "vocab_stream_kernel": "vocab.hip", "vocab_ring_kernel": "vocab.hip",
+           "vocab_stream_kernel": "vocab.hip", "vocab_band_kernel": "vocab.hip", "vocab_ring_kernel": "vocab.hip",
            "vocab_fixup_kernel": "vocab.hip", "vocab_reduce_kernel": "vocab.hip",
            "kivi_quantize_kernel": "round_ops.hip"}
 HEADER = ("Run from the repository root on one MI355X (after `cd /tmp && export TMPDIR=/tmp`, with absolute paths to "

@@ -482,7 +482,9 @@ VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097
                (160, 1024, 1025), (1, 256, 152064), (8, 512, 128256), (20, 256, 65536), (24, 256, 128256),
                (4, 256, 65536), (16, 256, 152064), (12, 256, 128256), (16, 256, 65536), (448, 256, 1000),
                # 258 ring slices: 256 whole, the last two (one partial) in four k parts
-               (48, 1024, 65948)]
+               (48, 1024, 65948),
+               # band kernel, shares of 37 tiles, the vocabulary's last tile partial
+               (5, 256, 150001)]
 
 
 @pytest.mark.parametrize("case", VOCAB_CASES, ids=[f"vocab{i}" for i in range(len(VOCAB_CASES))])

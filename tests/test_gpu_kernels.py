@@ -534,6 +534,29 @@ def test_vocab_parity(L, case):
     log(f"  near-tie excused rows: {excused}/{M}")
 
 
+def _random_vocab_cases(n=10, seed=2024):
+    """Seeded shapes spread over the plan's paths: band (M <= 32, shares of
+    32..38 tiles), stream (smaller shares), ring with and without k parts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        K = int(rng.choice([256, 512, 1024]))
+        kind = i % 3
+        if kind == 0:    # band
+            M, V = int(rng.integers(1, 33)), int(rng.integers(126000, 155000))
+        elif kind == 1:  # stream
+            M, V = int(rng.integers(1, 33)), int(rng.integers(3000, 60000))
+        else:            # ring
+            M, V = int(rng.integers(33, 449)), int(rng.integers(1000, 40000))
+        cases.append((M, K, V))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_vocab_cases(), ids=[f"rvocab{i}" for i in range(10)])
+def test_vocab_random_shapes(L, case):
+    test_vocab_parity(L, case)
+
+
 @pytest.mark.skip(reason=TILED_FAULT)
 def test_vocab_tiled_parity(L):
     """Meant for the tiled vocab kernel (M up to 288: W and hidden slices

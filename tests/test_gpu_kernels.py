@@ -159,6 +159,28 @@ def test_draft_kivi_parity(L, case):
     assert np.array_equal(out, out2), "draft attention is not deterministic"
 
 
+def _random_kivi_cases(n=8, seed=2025):
+    """Seeded draft shapes: batch 1..3, 1..8 KV heads, g in 1..16, D 64/128,
+    2 or 4 bits, bodies of 0..3000 tokens (whole blocks), tails of 1..200."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 16]))
+        D = int(rng.choice([64, 128]))
+        bits = int(rng.choice([2, 4]))
+        body = [32 * int(rng.integers(0, 95)) for _ in range(B)]
+        tail = [int(rng.integers(1, 201)) for _ in range(B)]
+        cases.append((B, g * Hkv, Hkv, D, bits, body, tail, bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_kivi_cases(), ids=[f"rkivi{i}" for i in range(8)])
+def test_draft_kivi_random_shapes(L, case):
+    test_draft_kivi_parity(L, case)
+
+
 def test_draft_kivi_unrestricted_key_scales(L):
     """Records whose key scales are plain fp16 values (not three significant
     bits): the query x key scale fold rounds, and the output must stay within
@@ -395,6 +417,29 @@ def test_verify_parity(L, case):
                          L.VC_VERIFY_BEGIN | L.VC_VERIFY_END, out2.data_ptr(), ws.data_ptr(), ws.numel(), stream())
         torch.cuda.synchronize()
         assert np.array_equal(got, out2.cpu().numpy()), "verify attention is not deterministic"
+
+
+def _random_verify_cases(n=8, seed=2026):
+    """Seeded verification shapes: batch 1..2, 2..8 KV heads, g in 1..8,
+    D 64/128, NR up to 64 and R = NR * g up to 288 rows, contexts of 1..3000 tokens, resident
+    or in chunks of 256 / 512."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 5, 8]))
+        D = int(rng.choice([64, 128]))
+        NR = int(rng.integers(1, min(64, 288 // g) + 1))
+        ctx = [int(rng.integers(1, 3001)) for _ in range(B)]
+        chunk = [None, 256, 512][int(rng.integers(0, 3))]
+        cases.append((B, g * Hkv, Hkv, D, NR, ctx, chunk))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_verify_cases(), ids=[f"rverify{i}" for i in range(8)])
+def test_verify_random_shapes(L, case):
+    test_verify_parity(L, case)
 
 
 @pytest.mark.parametrize("NR", [9, 41], ids=["producers", "self-issuing"])

@@ -794,6 +794,24 @@ __device__ __forceinline__ void dump_slots(int lane, DState<D, W, NHS>& st, bool
   }
 }
 
+// The split partials of one (sequence, KV head): rows h * S + s (query head
+// h of the unit, split s), D floats of unnormalised output and a (max, sum)
+// pair each. They are written and read with device-coherent accesses (the
+// `sc1` policy that agent-scope atomics compile to), which bypass the
+// per-XCD L2s, so a workgroup on another XCD reads what was stored.
+constexpr int kCoherent = 16;  // sc1
+struct UnitParts {
+  __amdgpu_buffer_rsrc_t o, ml;
+};
+template <int D>
+__device__ __forceinline__ UnitParts unit_parts(const DraftParams& P, int b, int hk) {
+  const size_t row0 = ((size_t)b * P.Hq + (size_t)hk * P.g) * P.S;
+  const int rows = P.g * P.S;
+  return UnitParts{
+      __builtin_amdgcn_make_buffer_rsrc(P.part_o + row0 * D, (short)0, rows * D * 4, 0x00020000),
+      __builtin_amdgcn_make_buffer_rsrc(P.part_ml + row0 * 2, (short)0, rows * 8, 0x00020000)};
+}
+
 // Merge NWV wave states in the slot layout (wave w's at o_of(w), ml_of(w))
 // and store the split's partial (running max, sum and unnormalised output
 // per query head of the unit). One thread per slot, every LDS load issued
@@ -831,93 +849,131 @@ __device__ __forceinline__ void merge_slots(const DraftParams& P, int b, int hk,
       }
     }
     const int c0 = 16 * (2 * W * jr + mm) + 4 * qg;
-    const size_t row = ((size_t)b * P.Hq + (size_t)hk * P.g + head) * P.S + split;
+    const int row = head * P.S + split;  // among the unit's partial rows
+    const UnitParts up = unit_parts<D>(P, b, hk);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(O[0]), __float_as_uint(O[1]), __float_as_uint(O[2]), __float_as_uint(O[3])}, up.o,
+        (row * D + c0) * 4, 0, kCoherent);
+    if (c0 == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(M), __float_as_uint(L)}, up.ml, row * 8, 0,
+                                            kCoherent);
+  }
+}
+
+// The split merge of finish_unit, every partial load of a thread in flight
+// at once. Task t < Q * SG takes the 4-channel run q = t mod Q of the unit's
+// outputs (Q = g D / 4: query head q / (D / 4), channels 4 (q mod D / 4) +
+// 0..3) and split group sg = t / Q, splits [sg SPG, (sg + 1) SPG), with
+// SG = min(ceil(S / 16), nthreads / Q) groups of SPG splits (one group, and
+// several tasks per thread, when Q > nthreads), loaded BATCH (<= SPG, or 16)
+// at a time: up to 16 splits in one trip to memory, without the group merge
+// through LDS. A task merges its splits in split order; with one group it stores
+// the run, else it leaves (max, sum, run) in LDS and thread q < Q merges the
+// SG groups in group order. The order of the additions depends on S and the
+// workgroup size only, never on which workgroup merges. lds: nthreads * 6
+// floats, free.
+struct MergeGroups {
+  int Q, SG, SPG;
+};
+template <int D>
+__device__ __forceinline__ MergeGroups merge_groups(const DraftParams& P, int nthreads) {
+  const int Q = P.g * (D / 4);
+  const int SG = max(1, min((P.S + 15) / 16, nthreads / Q));
+  return MergeGroups{Q, SG, (P.S + SG - 1) / SG};
+}
+template <int D, int BATCH>
+__device__ __forceinline__ void merge_unit(const DraftParams& P, int b, int hk, int nthreads, float* lds) {
+  constexpr int QPH = D / 4;
+  const MergeGroups mg = merge_groups<D>(P, nthreads);
+  const int Q = mg.Q, SG = mg.SG, SPG = mg.SPG;
+  const UnitParts up = unit_parts<D>(P, b, hk);
+  float* const out = P.out + ((size_t)b * P.Hq + (size_t)hk * P.g) * D;
+  auto finish = [&](int q, const f32x4& O, float L) {
+    *reinterpret_cast<f32x4*>(out + 4 * q) = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  for (int t = threadIdx.x; t < Q * SG; t += nthreads) {
+    const int q = t % Q, sg = t / Q, h = q / QPH, c4 = q % QPH;
+    const int s0 = sg * SPG, s1 = min(P.S, s0 + SPG);
+    float M = kNegInf, L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sb = s0; sb < s1; sb += BATCH) {
+      u32x4 o[BATCH];
+      u32x2 ml[BATCH];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      __hip_atomic_store(&P.part_o[row * D + c0 + r], O[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c0 == 0) {
-      __hip_atomic_store(&P.part_ml[row * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&P.part_ml[row * 2 + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < BATCH; ++i) {
+        const int row = h * P.S + min(sb + i, s1 - 1);  // past the group: its last split again, unused
+        o[i] = __builtin_amdgcn_raw_buffer_load_b128(up.o, (row * D + 4 * c4) * 4, 0, kCoherent);
+        ml[i] = __builtin_amdgcn_raw_buffer_load_b64(up.ml, row * 8, 0, kCoherent);
+      }
+      float m[BATCH];
+      float mx = M;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        m[i] = sb + i < s1 ? __uint_as_float(ml[i][0]) : kNegInf;
+        mx = fmaxf(mx, m[i]);
+      }
+      if (mx == kNegInf) continue;  // nothing visible so far
+      const float a = M == kNegInf ? 0.f : fast_exp2(M - mx);
+      O *= a;
+      L *= a;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const bool ok = m[i] != kNegInf;
+        const float w = ok ? fast_exp2(m[i] - mx) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[r] = ok ? fmaf(__uint_as_float(o[i][r]), w, O[r]) : O[r];
+        L = ok ? fmaf(__uint_as_float(ml[i][1]), w, L) : L;
+      }
+      M = mx;
+    }
+    if (SG == 1) {
+      finish(q, O, L);
+    } else {
+      float* g = lds + (size_t)t * 6;  // t < nthreads here
+      *reinterpret_cast<f32x4*>(g) = O;
+      g[4] = M;
+      g[5] = L;
     }
   }
+  if (SG == 1) return;
+  __syncthreads();
+  const int q = threadIdx.x;
+  if (q >= Q) return;
+  float M = kNegInf;
+  for (int sg = 0; sg < SG; ++sg) M = fmaxf(M, lds[(sg * Q + q) * 6 + 4]);
+  f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int sg = 0; sg < SG; ++sg) {
+      const float* g = lds + (size_t)(sg * Q + q) * 6;
+      if (g[4] == kNegInf) continue;
+      const float w = fast_exp2(g[4] - M);
+      const f32x4 og = *reinterpret_cast<const f32x4*>(g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[r] = fmaf(og[r], w, O[r]);
+      L = fmaf(g[5], w, L);
+    }
+  }
+  finish(q, O, L);
 }
 
 // Called by every thread after merge_slots. The workgroup's partial stores
 // complete, then one thread counts the split in; the workgroup that brings
-// the count to S merges the S partials of its (sequence, KV head) in split
+// the count to S merges the S partials of its (sequence, KV head) in a fixed
 // order (so the result does not depend on the order in which workgroups
 // ran), writes the output and sets the count back to zero for the next
-// call. The partials are written and read with agent-scope atomic accesses
-// (device-coherent: they bypass the per-XCD L2s), and every thread waits for
-// its stores to complete (vmcnt(0)) before the workgroup barrier that
-// precedes the counter atomic, so the partials are in coherent memory before
-// the count can reach S. A release on the counter atomic and an acquire
-// fence in the merging workgroup would state that ordering in the memory
-// model, but at agent scope on MI355X they write back and invalidate the
-// L2: measured, the draft kernel went from 41.2 to 54.2 us per launch on the
-// Llama-3-8B layer and from 135.2 to 146.8 us on the Qwen-32B layer.
-// The split merge of finish_unit over outputs idx, idx + nthreads, ...,
-// NI of them per pass so that their loads are in flight together, the
-// partials of BATCH splits at a time per output. An output past the end
-// takes the first one's addresses and is not stored.
-template <int D, int NI, int BATCH>
-__device__ __forceinline__ void merge_splits(const DraftParams& P, int b, int hk, int nthreads) {
-  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  for (int idx = threadIdx.x; idx < P.g * D; idx += NI * nthreads) {
-    int hq[NI], c[NI];
-    bool on[NI];
-    size_t row0[NI];
-    float M[NI], L[NI], O[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      on[j] = idx + j * nthreads < P.g * D;
-      const int ij = on[j] ? idx + j * nthreads : idx;
-      hq[j] = hk * P.g + ij / D;
-      c[j] = ij % D;
-      row0[j] = ((size_t)b * P.Hq + hq[j]) * P.S;
-      M[j] = kNegInf;
-      L[j] = 0.f;
-      O[j] = 0.f;
-    }
-    for (int s0 = 0; s0 < P.S; s0 += BATCH) {
-      float ms[NI][BATCH], ls[NI][BATCH], os[NI][BATCH];
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-          const size_t r = row0[j] + min(s0 + i, P.S - 1);
-          const bool in = s0 + i < P.S;
-          ms[j][i] = in ? ld(&P.part_ml[r * 2]) : kNegInf;
-          ls[j][i] = in ? ld(&P.part_ml[r * 2 + 1]) : 0.f;
-          os[j][i] = in ? ld(&P.part_o[r * D + c[j]]) : 0.f;
-        }
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        float mx = M[j];
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) mx = fmaxf(mx, ms[j][i]);
-        if (mx == kNegInf) continue;  // nothing visible so far
-        const float a = M[j] == kNegInf ? 0.f : fast_exp2(M[j] - mx);
-        O[j] *= a;
-        L[j] *= a;
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-          const bool ok = ms[j][i] != kNegInf;
-          const float w = ok ? fast_exp2(ms[j][i] - mx) : 0.f;
-          O[j] = ok ? fmaf(os[j][i], w, O[j]) : O[j];
-          L[j] = ok ? fmaf(ls[j][i], w, L[j]) : L[j];
-        }
-        M[j] = mx;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if (on[j]) P.out[((size_t)b * P.Hq + hq[j]) * D + c[j]] = (L[j] > 0.f) ? O[j] / L[j] : 0.f;
-  }
-}
-
+// call. The partials are written and read with device-coherent accesses
+// (they bypass the per-XCD L2s), and every thread waits for its stores to
+// complete (vmcnt(0)) before the workgroup barrier that precedes the counter
+// atomic, so the partials are in coherent memory before the count can reach
+// S. A release on the counter atomic and an acquire fence in the merging
+// workgroup would state that ordering in the memory model, but at agent
+// scope on MI355X they write back and invalidate the L2: measured, the draft
+// kernel went from 41.2 to 54.2 us per launch on the Llama-3-8B layer and
+// from 135.2 to 146.8 us on the Qwen-32B layer.
 template <int D>
-__device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk, int nthreads, int* lds_flag) {
+__device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk, int nthreads, int* lds_flag,
+                                            float* lds) {
   const size_t unit = (size_t)b * P.Hkv + hk;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
   __syncthreads();
@@ -929,12 +985,19 @@ __device__ __forceinline__ void finish_unit(const DraftParams& P, int b, int hk,
   __syncthreads();
   if (!*lds_flag) return;
   asm volatile("" ::: "memory");
-  // one output per thread when one pass covers the unit's outputs, else two
-  // per pass (fewer splits per load batch, to bound the registers)
-  if (P.g * D <= nthreads)
-    merge_splits<D, 1, 8>(P, b, hk, nthreads);
+  // a load batch no larger than a task's splits (loads past them would be
+  // issued for nothing)
+  const int spg = merge_groups<D>(P, nthreads).SPG;
+  if (spg <= 1)
+    merge_unit<D, 1>(P, b, hk, nthreads, lds);
+  else if (spg <= 2)
+    merge_unit<D, 2>(P, b, hk, nthreads, lds);
+  else if (spg <= 4)
+    merge_unit<D, 4>(P, b, hk, nthreads, lds);
+  else if (spg <= 8)
+    merge_unit<D, 8>(P, b, hk, nthreads, lds);
   else
-    merge_splits<D, 2, 4>(P, b, hk, nthreads);
+    merge_unit<D, 16>(P, b, hk, nthreads, lds);
   if (threadIdx.x == 0) __hip_atomic_store(&P.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -955,7 +1018,7 @@ __device__ __forceinline__ void store_partial(const DraftParams& P, int b, int h
       P, b, hk, split, 64 * NW, [&](int w) { return lds_o + (size_t)w * NH * D; },
       [&](int w) { return lds_ml + w * NH * 2; });
   __shared__ int last;
-  finish_unit<D>(P, b, hk, 64 * NW, &last);
+  finish_unit<D>(P, b, hk, 64 * NW, &last, lds);
 }
 
 template <int D>
@@ -1255,8 +1318,9 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
       P, b, hk, split, LL::NW * 64 + 64,
       [&](int w) { return w < NW ? body_o + (size_t)w * NH * D : tail_merge; },
       [&](int w) { return w < NW ? body_ml + w * NH * 2 : tail_merge + NH * D; });
+  static_assert(LL::STAGE0 >= (LL::NW * 64 + 64) * 6 * 4, "split merge area");
   __shared__ int last;
-  finish_unit<D>(P, b, hk, LL::NW * 64 + 64, &last);
+  finish_unit<D>(P, b, hk, LL::NW * 64 + 64, &last, body_o);
 }
 
 // Token-drop (GATHER) and dense draft caches: bf16 rows everywhere. The
@@ -1311,6 +1375,7 @@ __global__ __launch_bounds__((64 * RowShape<D, NHS>::NW), (RowShape<D, NHS>::PER
     }
   }
   tail_share<D, NHS, NW>(P, b, hk, split, wave, lane, st, my_lds, lds_p);
+  static_assert(draft_stage_bytes<D, NHS, NW>() >= 64 * NW * 6 * sizeof(float), "split merge area");
   store_partial<D, NHS, NW>(P, b, hk, split, lane, wave, st, reinterpret_cast<float*>(smem));
 }
 

@@ -132,6 +132,8 @@ KIVI_CASES = [
     (2, 48, 4, 128, 4, [512, 224], [40, 7], True),       # g = 12, 4-bit, padding heads in the set
     (2, 40, 8, 128, 2, [0, 96], [17, 3], False),         # five-stage ring: empty body, fewer blocks than stages
     (1, 40, 8, 128, 4, [992], [20], False),              # g = 5, 4-bit (two channel groups per row)
+    (1, 8, 1, 128, 2, [8192], [70], False),              # one unit: 32 splits, merged in two split groups
+    (1, 16, 1, 128, 2, [8192], [9], False),              # 86 splits, one group in six batches, two runs per thread
 ]
 
 
@@ -266,6 +268,9 @@ ROW_CASES = [
     ("dense", 2, 32, 8, 128, 3001, [1000, 3001], [3, 0]),
     ("dense", 1, 40, 8, 128, 700, [700], [26]),
     ("tokdrop", 1, 32, 8, 128, 2048, 0.25, [19], True),
+    ("tokdrop", 1, 64, 4, 128, 2048, 0.25, [23]),        # g = 16: more output runs than threads in the split merge
+    ("dense", 1, 48, 4, 128, 900, [900], [5]),            # g = 12, three head sets
+    ("dense", 1, 8, 1, 128, 8192, [8192], [10]),          # one unit: 32 splits, merged in two split groups
 ]
 
 

@@ -946,14 +946,14 @@ VocabPlan vocab_plan(int M, int K, int V) {
     p.nwg = (V + kTRows - 1) / kTRows;
   } else {
     // the row groups of NT tiles cover every row tile (the padding tiles'
-    // products are wasted): four vocab groups of 64 rows up to 18 and for 21
-    // to 26 row tiles, two vocab groups (a workgroup of 128 vocab rows and
+    // products are wasted, so NT is the smallest that covers them): four
+    // vocab groups of 64 rows up to 18 and for 21 to 26 row tiles, two vocab groups (a workgroup of 128 vocab rows and
     // four row groups) for 19, 20, 27 and 28 (measured: M = 300 654 us
     // against 765 us with four groups of 13; M = 416 753 us with four groups
     // of 13 against 793 us with two of 7)
     p.stream = false;
     if (mt <= 18) {
-      p.ring = mt <= 4 ? 2 : mt <= 10 ? 5 : 9;
+      p.ring = mt <= 4 ? 2 : (mt + 1) / 2;
       p.rvg = 4;
     } else if (mt <= 20) {
       p.ring = 5;
@@ -1083,7 +1083,12 @@ vc_status vocab_launch(int M, int K, int V, const float* h, const void* w, int32
   } else if (plan.ring) {
     switch (plan.ring * 16 + plan.rvg) {
       case 2 * 16 + 4: st = launch_ring<2, 4>(plan, P, stream, mstart, mstop); break;
+      case 3 * 16 + 4: st = launch_ring<3, 4>(plan, P, stream, mstart, mstop); break;
+      case 4 * 16 + 4: st = launch_ring<4, 4>(plan, P, stream, mstart, mstop); break;
       case 5 * 16 + 4: st = launch_ring<5, 4>(plan, P, stream, mstart, mstop); break;
+      case 6 * 16 + 4: st = launch_ring<6, 4>(plan, P, stream, mstart, mstop); break;
+      case 7 * 16 + 4: st = launch_ring<7, 4>(plan, P, stream, mstart, mstop); break;
+      case 8 * 16 + 4: st = launch_ring<8, 4>(plan, P, stream, mstart, mstop); break;
       case 9 * 16 + 4: st = launch_ring<9, 4>(plan, P, stream, mstart, mstop); break;
       case 13 * 16 + 4: st = launch_ring<13, 4>(plan, P, stream, mstart, mstop); break;
       case 5 * 16 + 2: st = launch_ring<5, 2>(plan, P, stream, mstart, mstop); break;

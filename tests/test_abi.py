@@ -116,7 +116,7 @@ def _ring_plan(M, K, V):
     CUs (at least 8 k slices per part, only when that round would leave half
     of the CUs or more idle)."""
     mt = (M + 15) // 16
-    nt, vg = ((2, 4) if mt <= 4 else (5, 4) if mt <= 10 else (9, 4)) if mt <= 18 else \
+    nt, vg = (max(2, (mt + 1) // 2), 4) if mt <= 18 else \
         (5, 2) if mt <= 20 else (13, 4) if mt <= 26 else (7, 2)
     nwg = -(-V // (64 * vg))
     left, full, split = nwg % 256, nwg, 1
@@ -130,7 +130,8 @@ def _align(x):
 
 
 @pytest.mark.parametrize("M,K,V", [(416, 5120, 152064), (264, 4096, 128256), (164, 5120, 32768), (33, 8192, 128256),
-                                   (48, 1024, 65948), (448, 256, 1000), (300, 1024, 3000)])
+                                   (48, 1024, 65948), (448, 256, 1000), (300, 1024, 3000), (90, 512, 3001),
+                                   (200, 512, 2500), (250, 1024, 4001)])
 def test_vocab_ring_workspace(M, K, V):
     """Workspace of the ring path: the bf16 hidden copy, a 64-bit key per row
     and key slot (whole slices one slot, a k-split slice one per vocab group),

@@ -534,7 +534,9 @@ VOCAB_CASES = [(1, 512, 4096), (8, 4096, 20007), (9, 512, 4096), (16, 1024, 4097
                # 258 ring slices: 256 whole, the last two (one partial) in four k parts
                (48, 1024, 65948),
                # band kernel, shares of 37 tiles, the vocabulary's last tile partial
-               (5, 256, 150001)]
+               (5, 256, 150001),
+               # ring row groups of 3, 7 and 8 row tiles
+               (90, 512, 3001), (200, 512, 2500), (250, 1024, 4001)]
 
 
 @pytest.mark.parametrize("case", VOCAB_CASES, ids=[f"vocab{i}" for i in range(len(VOCAB_CASES))])

@@ -12,8 +12,9 @@
 // pace_waves). Every wave keeps an online-softmax state for all g query heads
 // of the KV head; the wave states are merged through LDS into a per-split
 // partial (max, sum, unnormalised output), and the last workgroup of a
-// (KV head, sequence) to store its partial merges the partials in split
-// order.
+// (KV head, sequence) to store its partial merges the partials in a fixed
+// order (split groups of up to 16 splits, each in split order, then the
+// groups in order).
 //
 // MFMA mapping (v_mfma_f32_16x16x32; fp16 for KIVI and the fp16 tail, bf16
 // for the scores of bf16 rows, fp16 for every P x V: probabilities in fp16,

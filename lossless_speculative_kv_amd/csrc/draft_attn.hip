@@ -152,13 +152,13 @@ struct Geo {
 
 // ------------------------------------------------------ softmax state ----
 // m, l: score layout (lane (q, t) owns heads HPL*q + u of each set);
-// zt, acc: PV layout (lane n = (hl, jr) owns output column (hl, jr)).
+// zc, acc: PV layout (lane n = (hl, jr) owns output column (hl, jr)).
 template <int D, int W, int NHS>
 struct DState {
   static constexpr int HPL = Geo<D, W>::HPL, MT = Geo<D, W>::MT;
   float m[NHS][HPL];  // running max, uniform over the lane row
   float l[NHS][HPL];  // this lane's share of sum p
-  float zt[NHS][W];   // this lane's share of sum p * value zero point, per group (KIVI)
+  f32x4 zc[NHS];      // KIVI: sum p * value zero point, MFMA layout: row g = channel group, column (hl, jr)
   f32x4 acc[NHS][MT];
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -168,8 +168,7 @@ struct DState {
         m[h][u] = kNegInf;
         l[h][u] = 0.f;
       }
-#pragma unroll
-      for (int w = 0; w < W; ++w) zt[h][w] = 0.f;
+      zc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -223,8 +222,7 @@ __device__ __forceinline__ void soft_block(DState<D, W, NHS>& st, int h, const f
       const float au = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(alpha[u])));
       a = (hl % HPL == u) ? au : a;
     }
-#pragma unroll
-    for (int w = 0; w < W; ++w) st.zt[h][w] *= a;
+    st.zc[h] *= a;
 #pragma unroll
     for (int m = 0; m < MT; ++m) st.acc[h][m] *= a;
   }
@@ -354,7 +352,8 @@ struct KiviRaw {
   uint32_t kw[2][NWL];  // key codes of tokens t and t + 16
   uint32_t vw[VWL];     // value codes of the lane's slots
   uint32_t ks[4 * W];   // key scales of the lane's W 8-channel runs
-  u32x4 vs[W], vz[W];   // value scales / zeros of the lane's 8 slots, per group
+  u32x4 vs[W];          // value scales of the lane's 8 slots, per group
+  u32x4 vz;             // value zeros of group n (lane n < NG) for the lane's 8 slots
 };
 
 // The lane's operands of one staged block.
@@ -372,8 +371,13 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
     uint32_t t[4];
     lds_words<4>(blk + BL::VS + ((W * jr + w) * 32 + qg * 8) * 2, t);
     r.vs[w] = u32x4{t[0], t[1], t[2], t[3]};
-    lds_words<4>(blk + BL::VZ + ((W * jr + w) * 32 + qg * 8) * 2, t);
-    r.vz[w] = u32x4{t[0], t[1], t[2], t[3]};
+  }
+  {
+    // rows of the zero-point product past the groups read group NG - 1
+    // again; their results are never used
+    uint32_t t[4];
+    lds_words<4>(blk + BL::VZ + (min(n, NG - 1) * 32 + qg * 8) * 2, t);
+    r.vz = u32x4{t[0], t[1], t[2], t[3]};
   }
 }
 
@@ -532,17 +536,15 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
   row_scores<D, W>(c, Q.qscale, s);
   uint32_t Pp[4];
   soft_block<D, W, 1>(st, 0, s, bias, lane, lds_p, Pp);
-  // value scales into P~ (one per channel group of the column), value zero
-  // points into zt
+  // value scales into P~ (one per channel group of the column); the value
+  // zero points on the MFMA: row g of zc gains sum_t zero[t][g] p[t] for
+  // every column, with the same fp16 probabilities as the products
   uint32_t Pv[W][4];
 #pragma unroll
   for (int w = 0; w < W; ++w)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t pr = Pp[r], zw = raw.vz[w][r], sw = raw.vs[w][r];
-      st.zt[0][w] = fmaf(f16_hi(pr), f16_hi(zw), fmaf(f16_lo(pr), f16_lo(zw), st.zt[0][w]));
-      Pv[w][r] = as_u32(as_f16x2(pr) * as_f16x2(sw));
-    }
+    for (int r = 0; r < 4; ++r) Pv[w][r] = as_u32(as_f16x2(Pp[r]) * as_f16x2(raw.vs[w][r]));
+  st.zc[0] = mfma_f16(raw.vz, u32x4{Pp[0], Pp[1], Pp[2], Pp[3]}, st.zc[0]);
 
   // ---- PV: channel tile m belongs to group m/2, i.e. run (m/2) % W of the column ----
 #pragma unroll
@@ -692,6 +694,26 @@ __device__ __forceinline__ void row_query(const DraftParams& P, int b, int hk, i
   }
 }
 
+// The value zero-point terms of this lane's PV column (hl, jr) for the
+// channel tiles 2W jr + mm: row g = W jr + mm / 2 of zc, which lane n of
+// lane group 0 holds (MFMA output rows 0..3).
+template <int D, int W, int NHS>
+__device__ __forceinline__ void zero_terms(const DState<D, W, NHS>& st, int h, int lane, float (&zt)[2 * W]) {
+  using G = Geo<D, W>;
+  const int n = lane & 15, jr = n % G::NR;
+  float z[G::NG];
+#pragma unroll
+  for (int g = 0; g < G::NG; ++g)
+    z[g] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * n, __float_as_int(st.zc[h][g])));
+#pragma unroll
+  for (int mm = 0; mm < 2 * W; ++mm) {
+    float v = z[mm >> 1];
+#pragma unroll
+    for (int jj = 1; jj < G::NR; ++jj) v = (jr == jj) ? z[W * jj + (mm >> 1)] : v;
+    zt[mm] = v;
+  }
+}
+
 // The wave merge at the end of a workgroup. Each wave first writes its state
 // in one layout for every state type: per query head of the unit, the
 // unnormalised output row (D floats, the value zero-point term added) and
@@ -708,13 +730,15 @@ __device__ __forceinline__ void dump_state(int lane, DState<D, W, NHS>& st, bool
 #pragma unroll
   for (int h = 0; h < NHS; ++h) {
     float* oh = o + (size_t)(h * HS + hl) * D;
+    float ztm[2 * W] = {};
+    if (has_zero) zero_terms<D, W, NHS>(st, h, lane, ztm);
     // column (hl, jr) is valid for the 2W channel tiles of row group jr. The
     // tile index is lane-dependent, so the values are picked with selects:
     // an indexed access (or branches the compiler folds into one) would move
     // the accumulators to scratch memory.
 #pragma unroll
     for (int mm = 0; mm < 2 * W; ++mm) {
-      const float zt = has_zero ? sum_q(st.zt[h][mm >> 1]) : 0.f;
+      const float zt = ztm[mm];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = st.acc[h][mm][r];
@@ -769,9 +793,11 @@ __device__ __forceinline__ void dump_slots(int lane, DState<D, W, NHS>& st, bool
   const int n = lane & 15, qg = lane >> 4, jr = n % NR;
 #pragma unroll
   for (int h = 0; h < NHS; ++h) {
+    float ztm[2 * W] = {};
+    if (has_zero) zero_terms<D, W, NHS>(st, h, lane, ztm);
 #pragma unroll
     for (int mm = 0; mm < 2 * W; ++mm) {
-      const float zt = has_zero ? sum_q(st.zt[h][mm >> 1]) : 0.f;
+      const float zt = ztm[mm];
       f32x4 v = st.acc[h][mm];
 #pragma unroll
       for (int jj = 1; jj < NR; ++jj) {

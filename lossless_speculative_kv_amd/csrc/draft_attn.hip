@@ -1254,10 +1254,10 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         // block i is computed, so the LDS reads have a whole step to land
         KiviRaw<D, BITS, W> rc;
         auto step3 = [&](const KiviRaw<D, BITS, W>& cur, const char* cur_stage, KiviRaw<D, BITS, W>& nxt2,
-                         char* refill, int refill_blk, const char* stage2) {
+                         char* refill, int refill_blk, const char* stage2, bool paced) {
           const f32x4 cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
-          pace(refill_blk - 5);
+          if (paced) pace(refill_blk - 5);
           kivi_compute<D, BITS, W>(cur, cb, lane, Q, st, lds_p);
           wait_vm<3 * BL::NI>();  // block i + 2 has landed
           kivi_read<D, BITS, W>(nxt2, stage2, lane);
@@ -1268,27 +1268,27 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         kivi_read<D, BITS, W>(rb, w1, lane);
         for (int blk = b0;; blk += 6) {
           // block i sits in stage i mod 6
-          step3(ra, w0, rc, w5, blk + 5, w2);
+          step3(ra, w0, rc, w5, blk + 5, w2, true);
           if (blk + 1 > last) break;
-          step3(rb, w1, ra, w0, blk + 6, w3);
+          step3(rb, w1, ra, w0, blk + 6, w3, false);
           if (blk + 2 > last) break;
-          step3(rc, w2, rb, w1, blk + 7, w4);
+          step3(rc, w2, rb, w1, blk + 7, w4, true);
           if (blk + 3 > last) break;
-          step3(ra, w3, rc, w2, blk + 8, w5);
+          step3(ra, w3, rc, w2, blk + 8, w5, false);
           if (blk + 4 > last) break;
-          step3(rb, w4, ra, w3, blk + 9, w0);
+          step3(rb, w4, ra, w3, blk + 9, w0, true);
           if (blk + 5 > last) break;
-          step3(rc, w5, rb, w4, blk + 10, w1);
+          step3(rc, w5, rb, w4, blk + 10, w1, false);
           if (blk + 6 > last) break;
         }
       } else {
         auto step = [&](const KiviRaw<D, BITS, W>& cur, const char* cur_stage, KiviRaw<D, BITS, W>& nxt,
-                        char* refill, int refill_blk, const char* next_stage) {
+                        char* refill, int refill_blk, const char* next_stage, bool paced) {
           // the zero-point term reads the block's stage before the refill
           // is issued (only the next block's load is then in flight)
           const f32x4 cb = kivi_zero_term<D, BITS, W>(cur_stage, lane, Q);
           issue_block<D, BITS>(refill, res, gblk(min(refill_blk, last)), lane);
-          pace(refill_blk - 2);
+          if (paced) pace(refill_blk - 2);
           kivi_compute<D, BITS, W>(cur, cb, lane, Q, st, lds_p);
           wait_vm<(NS - 2) * BL::NI>();  // the next block has landed
           kivi_read<D, BITS, W>(nxt, next_stage, lane);
@@ -1298,17 +1298,17 @@ __global__ __launch_bounds__((KiviShape<D, BITS, W>::THREADS), (KiviShape<D, BIT
         kivi_read<D, BITS, W>(ra, w0, lane);
         for (int blk = b0;; blk += 6) {
           // block i sits in stage i mod 3
-          step(ra, w0, rb, w2, blk + 2, w1);
+          step(ra, w0, rb, w2, blk + 2, w1, true);
           if (blk + 1 > last) break;
-          step(rb, w1, ra, w0, blk + 3, w2);
+          step(rb, w1, ra, w0, blk + 3, w2, false);
           if (blk + 2 > last) break;
-          step(ra, w2, rb, w1, blk + 4, w0);
+          step(ra, w2, rb, w1, blk + 4, w0, true);
           if (blk + 3 > last) break;
-          step(rb, w0, ra, w2, blk + 5, w1);
+          step(rb, w0, ra, w2, blk + 5, w1, false);
           if (blk + 4 > last) break;
-          step(ra, w1, rb, w0, blk + 6, w2);
+          step(ra, w1, rb, w0, blk + 6, w2, true);
           if (blk + 5 > last) break;
-          step(rb, w2, ra, w1, blk + 7, w0);
+          step(rb, w2, ra, w1, blk + 7, w0, false);
           if (blk + 6 > last) break;
         }
       }

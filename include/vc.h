@@ -115,7 +115,9 @@ typedef struct {
  *                8*(s/2) + 4*(s%2) + 2*(m%2)             for bits = 2,
  *                16*(s/4) + 8*(s%2) + 4*((s/2)%2)        for bits = 4.
  *     8*D*bits   key scale fp16 [D] (per channel, over the block's tokens),
- *                then key zero fp16 [D].
+ *                then key zero fp16 [D]; both in runs of 8 channels whose
+ *                positions 0..7 hold channels 0, 2, 1, 3, 4, 6, 5, 7 of
+ *                the run.
  *     8*D*bits + 4*D
  *                value scale fp16 [D/32][32], then value zero fp16
  *                [D/32][32]: entry 8*q + s of channel group j is the

@@ -382,17 +382,17 @@ __device__ __forceinline__ void kivi_read(KiviRaw<D, BITS, W>& r, const char* bl
 }
 
 // Query data of one wave, fixed over the body (one head set, g <= HS).
-//   qp: A layout, lane (q, (hl, jr)), run w = K-step W*jr + w: fp16 pairs
-//       (slots 2r, 2r + 1) of q[hl][8(q*NG + W*jr + w) + kperm(s)], zero for
-//       padding heads (the scores are scaled after the MFMA);
-//   qn: A operand of the key zero-point product, lane (q, (hl, jr)), K-step
-//       kk: fp16 pairs of q[hl][32 kk + 8q + 0..7] on the head's first row
-//       (jr = 0), zero elsewhere.
+//   qm: A layout, lane (q, (hl, jr)), K-step kk (channel run q*NG + kk):
+//       fp16 pairs (slots 2r, 2r + 1) of q[hl][8(q*NG + kk) + kperm(s)] when
+//       kk / W == jr, zero otherwise and for padding heads (the scores are
+//       scaled after the MFMA). Times the key scales it is the operand of
+//       the codes; as it is, that of the key zero points, so row (hl, jr)
+//       of the zero-point product holds the term of the channels of row
+//       group jr, and the NR partial rows of a head add up as the scores do.
 template <int D, int W>
 struct KiviQuery {
   static constexpr int NG = Geo<D, W>::NG;
-  uint32_t qp[W][4];
-  uint32_t qn[NG][4];
+  uint32_t qm[NG][4];
   float qscale;  // log2(e)/sqrt(D), applied to the fp32 scores
 };
 
@@ -404,9 +404,7 @@ struct KiviQuery {
 // one.
 template <int D, int W>
 struct KiviQueryRaw {
-  static constexpr int NG = Geo<D, W>::NG;
-  uint32_t qp[W][4];   // channels 8(q*NG + W*jr + w) + 0..7 of head hl
-  uint32_t qn[NG][4];  // channels 32 kk + 8q + 0..7 of head hl
+  uint32_t qp[W][4];  // channels 8(q*NG + W*jr + w) + 0..7 of head hl
 };
 
 template <int N>
@@ -436,8 +434,6 @@ __device__ __forceinline__ void kivi_query_load(const DraftParams& P, int b, int
   const int hlc = hl < P.g ? hl : 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) global_words<4>(qb + (size_t)hlc * D + 8 * (qg * NG + W * jr + w), R.qp[w]);
-#pragma unroll
-  for (int kk = 0; kk < NG; ++kk) global_words<4>(qb + (size_t)hlc * D + 32 * kk + 8 * qg, R.qn[kk]);
 }
 
 template <int D, int W>
@@ -445,43 +441,40 @@ __device__ __forceinline__ void kivi_query_finish(const DraftParams& P, int lane
                                                   KiviQuery<D, W>& Q) {
   using G = Geo<D, W>;
   constexpr int NR = G::NR;
-  const int n = lane & 15, hl = n / NR;
+  const int n = lane & 15, hl = n / NR, jr = n % NR;
   const bool ok = hl < P.g;
 #pragma unroll
-  for (int w = 0; w < W; ++w)
+  for (int kk = 0; kk < G::NG; ++kk) {
+    const bool on = ok && jr == kk / W;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) x[e] = ok ? bf16_bits_to_f32(half_of(R.qp[w], kperm(2 * r + e))) : 0.f;
+      for (int e = 0; e < 2; ++e) x[e] = on ? bf16_bits_to_f32(half_of(R.qp[kk % W], kperm(2 * r + e))) : 0.f;
       // unscaled: a bf16 query value is an fp16 value (above 2^-14), so the
       // only rounding left before the MFMA is that of q * key scale
-      Q.qp[w][r] = pack_f16(x[0], x[1]);
+      Q.qm[kk][r] = pack_f16(x[0], x[1]);
     }
+  }
   Q.qscale = P.qscale;
-  const bool ok0 = ok && (n % NR) == 0;
-#pragma unroll
-  for (int kk = 0; kk < G::NG; ++kk)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Q.qn[kk][r] = pack_f16(ok0 ? bf16_bits_to_f32(R.qn[kk][r] & 0xFFFFu) : 0.f,
-                             ok0 ? bf16_bits_to_f32(R.qn[kk][r] >> 16) : 0.f);
 }
 
 // One 32-token block of the quantised body.
 // The key zero-point term sum_c q_c zero_c of each head on the MFMA: the
-// natural-order query of the head's first row times the zero points read
-// from the block's ring stage. The product is exact in fp32 and seeds both
-// score tiles of kivi_compute.
+// unscaled query operand of each K-step times the zero points of its
+// channel runs (stored in the runs' slot order), read from the block's ring
+// stage; every token column gets the same term. The product is exact in
+// fp32 and seeds both score tiles of kivi_compute.
 template <int D, int BITS, int W>
 __device__ __forceinline__ f32x4 kivi_zero_term(const char* stage, int lane, const KiviQuery<D, W>& Q) {
   using BL = BlockLayout<D, BITS>;
+  constexpr int NG = D / 32;
   const int qg = lane >> 4;
   f32x4 cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const u32x4 z = *reinterpret_cast<const u32x4*>(stage + BL::KZ + (32 * kk + 8 * qg) * 2);
-    cb = mfma_f16(u32x4{Q.qn[kk][0], Q.qn[kk][1], Q.qn[kk][2], Q.qn[kk][3]}, z, cb);
+  for (int kk = 0; kk < NG; ++kk) {
+    const u32x4 z = *reinterpret_cast<const u32x4*>(stage + BL::KZ + (qg * NG + kk) * 16);
+    cb = mfma_f16(u32x4{Q.qm[kk][0], Q.qm[kk][1], Q.qm[kk][2], Q.qm[kk][3]}, z, cb);
   }
   return cb;
 }
@@ -491,9 +484,8 @@ template <int D, int BITS, int W>
 __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, const f32x4& cb, int lane,
                                              const KiviQuery<D, W>& Q, DState<D, W, 1>& st, uint32_t* lds_p) {
   using G = Geo<D, W>;
-  constexpr int NG = G::NG, NR = G::NR, HPL = G::HPL, MT = G::MT, CPL = G::CPL;
+  constexpr int NG = G::NG, HPL = G::HPL, MT = G::MT;
   constexpr int NWL = KiviRaw<D, BITS, W>::NWL, VWL = KiviRaw<D, BITS, W>::VWL;
-  const int n = lane & 15, jr = n % NR;
 
   // key operands of both token tiles, all K-steps
   uint32_t Bk[2][NG][4];
@@ -503,19 +495,16 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
     for (int kk = 0; kk < NG; ++kk) key_operand<BITS, NWL>(raw.kw[i], kk, Bk[i][kk]);
 
   // query with the key scales of this lane's runs folded in: register r of
-  // run w pairs run channels kperm(2r), kperm(2r + 1), i.e. the low (r even)
-  // or high (r odd) halves of scale words 4w + 2(r >> 1) and the next one.
-  // The products are exact: a key scale has at most three significant bits
-  // and a bf16 query value eight, within fp16's eleven.
-  uint32_t Aq[W][4];
+  // K-step kk pairs run channels kperm(2r), kperm(2r + 1), which is scale
+  // word r of the run as stored; the lane's run of K-step kk is its run
+  // kk mod W (K-steps of other row groups multiply a zero query). The
+  // products are exact: a key scale has at most three significant bits and
+  // a bf16 query value eight, within fp16's eleven.
+  uint32_t Aq[NG][4];
 #pragma unroll
-  for (int w = 0; w < W; ++w)
+  for (int kk = 0; kk < NG; ++kk)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t w0 = raw.ks[4 * w + 2 * (r >> 1)], w1 = raw.ks[4 * w + 2 * (r >> 1) + 1];
-      const uint32_t sp = __builtin_amdgcn_perm(w1, w0, (r & 1) ? 0x07060302u : 0x05040100u);
-      Aq[w][r] = as_u32(as_f16x2(Q.qp[w][r]) * as_f16x2(sp));
-    }
+    for (int r = 0; r < 4; ++r) Aq[kk][r] = as_u32(as_f16x2(Q.qm[kk][r]) * as_f16x2(raw.ks[4 * (kk % W) + r]));
   // the key zero-point term (cb) is already inside the scores
   float bias[HPL];
 #pragma unroll
@@ -525,12 +514,9 @@ __device__ __forceinline__ void kivi_compute(const KiviRaw<D, BITS, W>& raw, con
   for (int i = 0; i < 2; ++i) {
     c[i] = cb;
 #pragma unroll
-    for (int kk = 0; kk < NG; ++kk) {
-      const bool on = (jr == kk / W);
-      const uint32_t* a = Aq[kk % W];
-      const u32x4 av = {on ? a[0] : 0u, on ? a[1] : 0u, on ? a[2] : 0u, on ? a[3] : 0u};
-      c[i] = mfma_f16(av, u32x4{Bk[i][kk][0], Bk[i][kk][1], Bk[i][kk][2], Bk[i][kk][3]}, c[i]);
-    }
+    for (int kk = 0; kk < NG; ++kk)
+      c[i] = mfma_f16(u32x4{Aq[kk][0], Aq[kk][1], Aq[kk][2], Aq[kk][3]},
+                      u32x4{Bk[i][kk][0], Bk[i][kk][1], Bk[i][kk][2], Bk[i][kk][3]}, c[i]);
   }
   float s[HPL][2];
   row_scores<D, W>(c, Q.qscale, s);

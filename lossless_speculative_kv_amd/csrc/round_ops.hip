@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
   char* const rec = P.blocks + (unit * nbc + dblk) * REC;
   uint32_t* const rk = reinterpret_cast<uint32_t*>(rec + KC);
   uint32_t* const rv = reinterpret_cast<uint32_t*>(rec + VC);
-  uint16_t* const rks = reinterpret_cast<uint16_t*>(rec + KS);  // scale [D], then zero [D]
+  uint16_t* const rks = reinterpret_cast<uint16_t*>(rec + KS);  // scale [D], then zero [D] (run order)
   uint16_t* const rvs = reinterpret_cast<uint16_t*>(rec + VS);  // scale [D/32][32], then zero
   if (tid < D) {
     // keys: channel tid over 32 tokens
@@ -129,8 +129,11 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(const QuantParams P)
       if (sc != 0.0) c = fmin(fmax(rint((vals_k[t][d] - ze) / sc), 0.0), (double)QMAX);
       ck[t][d] = (uint8_t)c;
     }
-    rks[d] = sb;
-    rks[D + d] = zb;
+    // key scale / zero in runs of 8 channels stored in the order 0, 2, 1, 3,
+    // 4, 6, 5, 7 (the order of the draft kernel's code pairs)
+    const int o = d & 7, pos = (d & ~7) | (4 * (o >> 2) + 2 * (o & 1) + ((o >> 1) & 1));
+    rks[pos] = sb;
+    rks[D + pos] = zb;
   } else if (tid < D + 32 * NG) {
     // values: token t, channel group j
     const int i = tid - D, t = i / NG, j = i % NG;

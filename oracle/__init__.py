@@ -21,7 +21,7 @@ from .attention import attend, attend_masked, attend_prefix
 from .kivi import (quantize_keys, quantize_values, dequantize_keys, dequantize_values,
                    pack_key_codes, pack_value_codes, pack_value_side, unpack_key_codes,
                    unpack_value_codes, unpack_value_side, fp16_round, value_slot_token, pack_blocks,
-                   unpack_blocks, record_bytes, record_offsets)
+                   unpack_blocks, record_bytes, record_offsets, key_side_channel, pack_key_side, unpack_key_side)
 from .tokdrop import select_kept
 from .vocab import to_bf16, logits, argmax_first, tie_bound
 from .accept import greedy_accept
@@ -30,7 +30,7 @@ __all__ = [
     "attend", "attend_masked", "attend_prefix", "quantize_keys", "quantize_values", "dequantize_keys",
     "dequantize_values", "pack_key_codes", "pack_value_codes", "pack_value_side",
     "unpack_key_codes", "unpack_value_codes", "unpack_value_side", "fp16_round", "pack_blocks", "unpack_blocks",
-    "record_bytes", "record_offsets",
+    "record_bytes", "record_offsets", "key_side_channel", "pack_key_side", "unpack_key_side",
     "value_slot_token", "select_kept", "to_bf16", "logits", "argmax_first", "tie_bound",
     "greedy_accept",
 ]

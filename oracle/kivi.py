@@ -223,9 +223,31 @@ def unpack_value_side(packed) -> np.ndarray:
 # one record of 8*D*(b + 1) bytes per 32-token block, holding at byte offsets
 #   0          the block's key codes (uint32 [32][D*b/32], as above)
 #   4*D*b      its value codes (uint32 [64][D*b/64], as above)
-#   8*D*b      key scale fp16 [D], then key zero fp16 [D]
+#   8*D*b      key scale fp16 [D], then key zero fp16 [D], each in runs of 8
+#              channels whose positions 0..7 hold the run's channels
+#              0, 2, 1, 3, 4, 6, 5, 7 (key_side_channel)
 #   8*D*b+4*D  value scale fp16 [D/32][32], then value zero fp16 [D/32][32]
 # (little-endian words), so that one block is one contiguous read.
+
+
+def key_side_channel(e: int) -> int:
+    """Channel (within its run of 8) stored at position e of a run of the
+    key scale / zero pieces: 0, 2, 1, 3, 4, 6, 5, 7 (the order is its own
+    inverse)."""
+    return 4 * (e // 4) + 2 * (e % 2) + (e // 2) % 2
+
+
+def pack_key_side(param) -> np.ndarray:
+    """Key scale or zero [nb][D] -> [nb][D] in the record's run order."""
+    p = np.asarray(param)
+    nb, D = p.shape
+    order = [8 * (c // 8) + key_side_channel(c % 8) for c in range(D)]
+    return np.ascontiguousarray(p[:, order])
+
+
+def unpack_key_side(packed) -> np.ndarray:
+    """Inverse of pack_key_side (the same reordering)."""
+    return pack_key_side(packed)
 
 
 def record_bytes(D: int, bits: int) -> int:
@@ -247,8 +269,8 @@ def pack_blocks(kcodes, kscale, kzero, vcodes, vscale, vzero, bits: int) -> np.n
     nb = T // GROUP
     kw = pack_key_codes(kcodes, bits).reshape(nb, -1).astype("<u4")
     vw = pack_value_codes(vcodes, bits).reshape(nb, -1).astype("<u4")
-    ks = np.asarray(kscale).astype("<f2").reshape(nb, D)
-    kz = np.asarray(kzero).astype("<f2").reshape(nb, D)
+    ks = pack_key_side(np.asarray(kscale).astype("<f2").reshape(nb, D))
+    kz = pack_key_side(np.asarray(kzero).astype("<f2").reshape(nb, D))
     vs = pack_value_side(np.asarray(vscale).astype("<f2")).reshape(nb, D)
     vz = pack_value_side(np.asarray(vzero).astype("<f2")).reshape(nb, D)
     out = np.zeros((nb, record_bytes(D, bits)), dtype=np.uint8)
@@ -272,8 +294,8 @@ def unpack_blocks(records, bits: int, D: int):
 
     kc = unpack_key_codes(piece("key_codes", nkw, "<u4").reshape(nb * GROUP, D * bits // 32), bits, D)
     vc = unpack_value_codes(piece("value_codes", 64 * (D * bits // 64), "<u4").reshape(nb, 64, -1), bits, D)
-    ks = piece("key_scale", D, "<f2").astype(np.float16)
-    kz = piece("key_zero", D, "<f2").astype(np.float16)
+    ks = unpack_key_side(piece("key_scale", D, "<f2")).astype(np.float16)
+    kz = unpack_key_side(piece("key_zero", D, "<f2")).astype(np.float16)
     vs = unpack_value_side(piece("value_scale", D, "<f2").reshape(nb, D // GROUP, GROUP)).astype(np.float16)
     vz = unpack_value_side(piece("value_zero", D, "<f2").reshape(nb, D // GROUP, GROUP)).astype(np.float16)
     return kc, ks, kz, vc, vs, vz

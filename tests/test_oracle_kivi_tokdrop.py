@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import (dequantize_keys, dequantize_values, fp16_round, pack_blocks, pack_key_codes,
-                    pack_value_codes, pack_value_side, quantize_keys, quantize_values, record_bytes,
+                    pack_value_codes, pack_value_side, quantize_keys, quantize_values, record_bytes, record_offsets,
                     select_kept, unpack_blocks, unpack_key_codes, unpack_value_codes, unpack_value_side)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -178,6 +178,25 @@ def test_block_record_golden_offsets():
                     p if name == "value_scale" else 0 * p, p if name == "value_zero" else 0 * p]
             rec = pack_blocks(*args, bits)[0]
             assert np.flatnonzero(rec).tolist() == [case[name] + 1] and rec[case[name] + 1] == 0x3C
+
+
+def test_key_side_golden_order():
+    """Hand-worked positions of the key scale / zero pieces
+    (tests/golden/kivi_layout.json): a scale of 1.0 on one channel lands at
+    byte key_scale + 2 * position + 1, a zero at key_zero + 2 * position + 1."""
+    with open(os.path.join(GOLDEN, "kivi_layout.json")) as f:
+        cases = json.load(f)["key_side"]["cases"]
+    one = np.float16(1.0)  # 0x3C00: bytes 00 3C
+    for case in cases:
+        D, c, pos = case["D"], case["channel"], case["position"]
+        z = np.zeros((32, D), np.int64)
+        for name in ("key_scale", "key_zero"):
+            p = np.zeros((1, D), np.float16)
+            p[0, c] = one
+            rec = pack_blocks(z, p if name == "key_scale" else 0 * p, p if name == "key_zero" else 0 * p, z,
+                              np.zeros((32, D // 32), np.float16), np.zeros((32, D // 32), np.float16), 2)[0]
+            at = record_offsets(D, 2)[name] + 2 * pos + 1
+            assert np.flatnonzero(rec).tolist() == [at] and rec[at] == 0x3C, (case, name)
 
 
 def _kept_by_rank(scores, n_keep):

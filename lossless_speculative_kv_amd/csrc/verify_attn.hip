@@ -176,26 +176,6 @@ __device__ __forceinline__ void chunk_to_f16(char* chunk, int lane) {
 // lgkmcnt(0): this wave's LDS accesses have completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Online-softmax state of RT row tiles. The row sums live in an MFMA
-// accumulator (lsum): P^T contracted with a ones operand, so each sum is
-// complete after the MFMA (no cross-lane reduction) and uses the same fp16
-// probabilities as the numerator.
-template <int RT, int MT>
-struct VState {
-  float m[RT];  // running max (log2 domain, scaled), identical on all lanes of a column
-  f32x4 acc[RT][MT];
-  f32x4 lsum[RT];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      m[rt] = kNegInf;
-      lsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-};
-
 // Raw scores s (unscaled q.k, -inf where masked) of one tile become
 // p = 2^(s * qscale - m + kProbShift). The running max moves only when the
 // tile's max exceeds it by more than kRescaleThreshold, which keeps the
@@ -206,6 +186,31 @@ struct VState {
 // row sums carry the same factor 2^kProbShift, on every split alike.
 constexpr float kProbShift = 7.0f;
 static_assert(kRescaleThreshold + kProbShift <= 15.0f, "largest probability inside fp16's range");
+
+// Online-softmax state of RT row tiles. The row sums live in an MFMA
+// accumulator (lsum): P^T contracted with a ones operand, so each sum is
+// complete after the MFMA (no cross-lane reduction) and uses the same fp16
+// probabilities as the numerator.
+template <int RT, int MT>
+struct VState {
+  float m[RT];   // running max (log2 domain, scaled), identical on all lanes of a column
+  float nm[RT];  // exponent offset kProbShift - m (kProbShift while m is -inf)
+  float th[RT];  // rescale threshold in raw score units: (m + kRescaleThreshold) / qscale
+  f32x4 acc[RT][MT];
+  f32x4 lsum[RT];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      m[rt] = kNegInf;
+      nm[rt] = kProbShift;
+      th[rt] = kNegInf;
+      lsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
 // Maximum that propagates NaN (v_maximum3_f32): unlike fmaxf it needs no
 // canonicalising of operands that come from the MFMA or a lane permute.
 // Scores are finite or -inf on every row whose result is kept.
@@ -217,23 +222,29 @@ __device__ __forceinline__ float vmax_q(float x) {
   return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The tile's raw maxima are compared with the threshold kept in raw score
+// units, and the exponent offset is kept beside the max, so a tile that
+// moves no max costs no scaling of the maxima and no test of an unset max.
 template <int RT, int MT>
-__device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT][2][4], float qscale) {
-  float bm[RT];
+__device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT][2][4], float qscale,
+                                               float rqscale) {
+  float x[RT];
   bool need = false;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float x = vmax(vmax(vmax(s[rt][0][0], s[rt][0][1]), vmax(s[rt][0][2], s[rt][0][3])),
-                         vmax(vmax(s[rt][1][0], s[rt][1][1]), vmax(s[rt][1][2], s[rt][1][3])));
-    bm[rt] = vmax_q(x) * qscale;
-    need = need || (bm[rt] > st.m[rt] + kRescaleThreshold);
+    x[rt] = vmax_q(vmax(vmax(vmax(s[rt][0][0], s[rt][0][1]), vmax(s[rt][0][2], s[rt][0][3])),
+                        vmax(vmax(s[rt][1][0], s[rt][1][1]), vmax(s[rt][1][2], s[rt][1][3]))));
+    need = need || (x[rt] > st.th[rt]);
   }
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const bool up = bm[rt] > st.m[rt] + kRescaleThreshold;
-      const float alpha = up ? fast_exp2(st.m[rt] - bm[rt]) : 1.f;
-      st.m[rt] = up ? bm[rt] : st.m[rt];
+      const bool up = x[rt] > st.th[rt];
+      const float bm = x[rt] * qscale;
+      const float alpha = up ? fast_exp2(st.m[rt] - bm) : 1.f;
+      st.m[rt] = up ? bm : st.m[rt];
+      st.nm[rt] = up ? kProbShift - bm : st.nm[rt];
+      st.th[rt] = up ? (bm + kRescaleThreshold) * rqscale : st.th[rt];
       st.lsum[rt] *= alpha;
 #pragma unroll
       for (int t = 0; t < MT; ++t) st.acc[rt][t] *= alpha;
@@ -241,9 +252,9 @@ __device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    // a row that has seen no visible token yet (max still -inf) gets p = 0
-    // from its -inf scores instead of 2^(-inf + inf)
-    const float nm = (st.m[rt] == kNegInf ? 0.f : -st.m[rt]) + kProbShift;
+    // a row that has seen no visible token yet (max still -inf, offset
+    // kProbShift) gets p = 0 from its -inf scores
+    const float nm = st.nm[rt];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -259,7 +270,8 @@ __device__ __forceinline__ void verify_softmax(VState<RT, MT>& st, float (&s)[RT
 template <int D, int RT, bool MASK, typename Between>
 __device__ __forceinline__ void tile_compute(const char* kstage, const char* vstage, int nvalid, int lane,
                                              const uint32_t (&Bq)[RT][D / 32][4], const int (&lim)[RT],
-                                             float qscale, VState<RT, D / 16>& st, Between&& between) {
+                                             float qscale, float rqscale, VState<RT, D / 16>& st,
+                                             Between&& between) {
   constexpr int NG = D / 32, MT = D / 16;
   const int n = lane & 15, qg = lane >> 4;
   float s[RT][2][4];
@@ -285,7 +297,7 @@ __device__ __forceinline__ void tile_compute(const char* kstage, const char* vst
       }
     }
   }
-  verify_softmax<RT, MT>(st, s, qscale);
+  verify_softmax<RT, MT>(st, s, qscale, rqscale);
   uint32_t Bp[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -510,6 +522,7 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   if constexpr (!SELF) __builtin_amdgcn_s_setprio(1);
   VState<RT, MT> st;
   st.init();
+  const float rqscale = 1.f / P.qscale;
   if constexpr (SELF) {
     // the query has landed before the ring starts, so the compiler (which
     // does not see the ring's asm loads) has nothing left to wait for in the
@@ -558,7 +571,8 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
   for (int sp = 0; sp < nfull_steps; ++sp) {
     step_sync(sp);
     const int t = sp * TPS + parity;
-    tile_compute<D, RT, false>(kslot(t), vslot(t), kTT, lane, Bq, lim_all, P.qscale, st, [&] { convert_next(sp); });
+    tile_compute<D, RT, false>(kslot(t), vslot(t), kTT, lane, Bq, lim_all, P.qscale, rqscale, st,
+                               [&] { convert_next(sp); });
   }
   for (int sp = nfull_steps; sp < nsteps; ++sp) {
     step_sync(sp);
@@ -570,7 +584,8 @@ __global__ __launch_bounds__(512, 2) void verify_kernel(const VerifyParams P) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) lim[rt] = blk ? rowj[rt] - tb * kTT : kTT;
       const int nv = blk ? min(kTT, P.NR - tb * kTT) : min(kTT, nval - t * kTT);
-      tile_compute<D, RT, true>(kslot(t), vslot(t), nv, lane, Bq, lim, P.qscale, st, [&] { convert_next(sp); });
+      tile_compute<D, RT, true>(kslot(t), vslot(t), nv, lane, Bq, lim, P.qscale, rqscale, st,
+                                [&] { convert_next(sp); });
     } else {
       convert_next(sp);
     }

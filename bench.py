@@ -57,8 +57,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen-32b-layer")
     ap.add_argument("--extra", default="llama-70b-layer-1m",
                     help="comma-separated workloads measured after the main one (3 rounds each) and reported "
